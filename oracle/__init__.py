@@ -1,0 +1,210 @@
+"""Python access to the CPU oracle (``qamw_oracle.c``) -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s cpu_baseline leg
+may import this module.  The GPU library and its binding never do.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "qamw_oracle.c")
+_HDR = os.path.join(_HERE, "qamw_oracle.h")
+_LIB = os.path.join(_HERE, "libqamw_oracle.so")
+
+FLAG_NONFINITE, FLAG_BAD_SCALE, FLAG_NORM_RANGE, FLAG_POINT_RANGE = 1, 2, 4, 8
+
+GCC_FLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC", "-shared"]
+
+
+def compile_to(src: str, out: str, extra=()) -> None:
+    """Compile an oracle source file (the given one or a variant) into a shared library."""
+    cmd = ["gcc"] + GCC_FLAGS + ["-I", _HERE] + list(extra) + [src, "-o", out, "-lm"]
+    subprocess.check_call(cmd)
+
+
+def build(force: bool = False) -> str:
+    newest = max(os.path.getmtime(_SRC), os.path.getmtime(_HDR))
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < newest:
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        compile_to(_SRC, tmp)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _bind(lib):
+    vp, i32, i64, dbl, f32, u16 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double,
+                                   ctypes.c_float, ctypes.c_uint16)
+    sig = {
+        "oracle_f16_from_f32": ([f32], u16),
+        "oracle_f32_from_f16": ([u16], f32),
+        "oracle_bf16_from_f32": ([f32], u16),
+        "oracle_hadamard": ([i32, vp], None),
+        "oracle_default_block": ([i32], i32),
+        "oracle_bpw": ([i32, i32], dbl),
+        "oracle_row_stride": ([i32, i32], ctypes.c_size_t),
+        "oracle_front_end": ([vp, i32, i64, i32, i64, vp, vp, i32, vp, vp, vp], ctypes.c_int),
+        "oracle_calibrate": ([vp, i32, i64, i32, i64, vp, vp, i32, vp, vp], ctypes.c_int),
+        "oracle_nearest": ([f32, f32, vp, i32, vp], i32),
+        "oracle_nearest_many": ([vp, i64, vp, i32, vp, vp], None),
+        "oracle_pack_row": ([vp, i32, i32, vp, ctypes.c_size_t], None),
+        "oracle_unpack_row": ([vp, i32, i32, vp], None),
+        "oracle_encode": ([vp, i32, i64, i32, i64, vp, vp, i32, vp, i32, vp, vp, vp, vp, vp, vp],
+                          ctypes.c_int),
+        "oracle_decode": ([vp, vp, i64, i32, vp, vp, i32, vp, vp, i32, vp, vp, vp], ctypes.c_int),
+        "oracle_lloyd": ([vp, i64, i32, i32, vp, vp, vp, vp], ctypes.c_int),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+class Oracle:
+    """numpy front-end to one compiled oracle library (the default build or a variant)."""
+
+    def __init__(self, path: Optional[str] = None):
+        if path is None:
+            path = _LIB if os.path.exists(_LIB) else build()
+        self.path = path
+        self.lib = _bind(ctypes.CDLL(path))
+
+    # -- helpers -------------------------------------------------------------
+    @staticmethod
+    def _p(a: Optional[np.ndarray]):
+        return None if a is None else a.ctypes.data
+
+    @staticmethod
+    def _w(w: np.ndarray) -> Tuple[np.ndarray, int]:
+        w = np.ascontiguousarray(w)
+        if w.dtype == np.uint16:
+            return w, 1
+        if w.dtype == np.float32:
+            return w, 0
+        raise TypeError("weights must be float32 or uint16 (bf16 bits)")
+
+    # -- scalars -------------------------------------------------------------
+    def f16_from_f32(self, x: float) -> int:
+        return self.lib.oracle_f16_from_f32(x)
+
+    def f32_from_f16(self, h: int) -> float:
+        return self.lib.oracle_f32_from_f16(h)
+
+    def bf16_from_f32(self, x: float) -> int:
+        return self.lib.oracle_bf16_from_f32(x)
+
+    def default_block(self, d_in: int) -> int:
+        return self.lib.oracle_default_block(d_in)
+
+    def bpw(self, d_in: int, bits: int) -> float:
+        return self.lib.oracle_bpw(d_in, bits)
+
+    def row_stride(self, d_in: int, bits: int) -> int:
+        return self.lib.oracle_row_stride(d_in, bits)
+
+    # -- arrays --------------------------------------------------------------
+    def hadamard(self, b: int) -> np.ndarray:
+        H = np.empty((b, b), dtype=np.float64)
+        self.lib.oracle_hadamard(b, self._p(H))
+        return H
+
+    def front_end(self, w, s, sign_bits, block):
+        w, bf = self._w(w)
+        n, d_in = w.shape
+        y = np.empty((n, d_in), dtype=np.float64)
+        r = np.empty((n,), dtype=np.float64)
+        st = np.zeros((1,), dtype=np.int32)
+        rc = self.lib.oracle_front_end(self._p(w), bf, n, d_in, d_in, self._p(s), self._p(sign_bits),
+                                       block, self._p(y), self._p(r), self._p(st))
+        assert rc == 0
+        return y, r, int(st[0])
+
+    def calibrate(self, w, s, sign_bits, block):
+        w, bf = self._w(w)
+        n, d_in = w.shape
+        sigma = np.empty((d_in // 2,), dtype=np.float32)
+        st = np.zeros((1,), dtype=np.int32)
+        rc = self.lib.oracle_calibrate(self._p(w), bf, n, d_in, d_in, self._p(s), self._p(sign_bits),
+                                       block, self._p(sigma), self._p(st))
+        assert rc == 0
+        return sigma, int(st[0])
+
+    def nearest(self, p: np.ndarray, cb: np.ndarray):
+        p = np.ascontiguousarray(p, dtype=np.float32).reshape(-1, 2)
+        cb = np.ascontiguousarray(cb, dtype=np.float32).reshape(-1, 2)
+        idx = np.empty((p.shape[0],), dtype=np.int32)
+        d = np.empty((p.shape[0],), dtype=np.float32)
+        self.lib.oracle_nearest_many(self._p(p), p.shape[0], self._p(cb), cb.shape[0], self._p(idx), self._p(d))
+        return idx, d
+
+    def pack_row(self, idx: np.ndarray, bits: int, d_in: int) -> np.ndarray:
+        idx = np.ascontiguousarray(idx, dtype=np.int32)
+        stride = self.row_stride(d_in, bits)
+        out = np.empty((stride,), dtype=np.uint8)
+        self.lib.oracle_pack_row(self._p(idx), d_in // 2, bits, self._p(out), stride)
+        return out
+
+    def unpack_row(self, row: np.ndarray, bits: int, d_in: int) -> np.ndarray:
+        row = np.ascontiguousarray(row, dtype=np.uint8)
+        idx = np.empty((d_in // 2,), dtype=np.int32)
+        self.lib.oracle_unpack_row(self._p(row), d_in // 2, bits, self._p(idx))
+        return idx
+
+    def encode(self, w, s, sign_bits, block, cb, bits, sigma, want_idx=True, want_p=False):
+        w, bf = self._w(w)
+        n, d_in = w.shape
+        stride = self.row_stride(d_in, bits)
+        norm = np.empty((n,), dtype=np.uint16)
+        codes = np.empty((n, stride), dtype=np.uint8)
+        idx = np.empty((n, d_in // 2), dtype=np.int32) if want_idx else None
+        p = np.empty((n, d_in), dtype=np.float32) if want_p else None
+        st = np.zeros((1,), dtype=np.int32)
+        cb = np.ascontiguousarray(cb, dtype=np.float32)
+        sigma = np.ascontiguousarray(sigma, dtype=np.float32)
+        rc = self.lib.oracle_encode(self._p(w), bf, n, d_in, d_in, self._p(s), self._p(sign_bits), block,
+                                    self._p(cb), bits, self._p(sigma), self._p(norm), self._p(codes),
+                                    self._p(idx), self._p(p), self._p(st))
+        assert rc == 0
+        return {"norm": norm, "codes": codes, "idx": idx, "p": p, "status": int(st[0])}
+
+    def decode(self, codes, norm, d_in, sigma, cb, bits, s, sign_bits, block, want_f64=False):
+        codes = np.ascontiguousarray(codes, dtype=np.uint8)
+        norm = np.ascontiguousarray(norm, dtype=np.uint16)
+        n = norm.shape[0]
+        f32 = np.empty((n, d_in), dtype=np.float32)
+        b16 = np.empty((n, d_in), dtype=np.uint16)
+        f64 = np.empty((n, d_in), dtype=np.float64) if want_f64 else None
+        cb = np.ascontiguousarray(cb, dtype=np.float32)
+        rc = self.lib.oracle_decode(self._p(codes), self._p(norm), n, d_in, self._p(sigma), self._p(cb), bits,
+                                    self._p(s), self._p(sign_bits), block, self._p(f32), self._p(b16),
+                                    self._p(f64))
+        assert rc == 0
+        return {"f32": f32, "bf16": b16, "f64": f64}
+
+    def lloyd(self, pts, bits, iters, init=None):
+        pts = np.ascontiguousarray(pts, dtype=np.float32).reshape(-1, 2)
+        K = 1 << bits
+        cb = np.empty((K, 2), dtype=np.float32)
+        e = np.empty((max(iters, 1),), dtype=np.int64)
+        st = np.zeros((1,), dtype=np.int32)
+        init_a = None if init is None else np.ascontiguousarray(init, dtype=np.float32)
+        rc = self.lib.oracle_lloyd(self._p(pts), pts.shape[0], bits, iters, self._p(init_a), self._p(cb),
+                                   self._p(e), self._p(st))
+        assert rc == 0
+        return cb, e[:iters], int(st[0])
+
+
+_default: Optional[Oracle] = None
+
+
+def get() -> Oracle:
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default

@@ -1,0 +1,57 @@
+"""Planted mistakes: each variant of the oracle below carries one plausible bug, and the pins in
+test_oracle_pins.py must catch every one of them.  Variants are compiled from a patched copy of the
+oracle source in a temporary directory; the oracle itself is never modified."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "qamw_oracle.c")
+
+MUTANTS = [
+    ("sign mask dropped", "a[j] = eps_of(sign_bits, j) * (a[j] / r);", "a[j] = (a[j] / r);"),
+    ("Hadamard sign from i|k", "(__builtin_popcount(i & k) & 1) ? -scale : scale",
+     "(__builtin_popcount(i | k) & 1) ? -scale : scale"),
+    ("pair second coordinate", "float py = (float)(y[2 * k + 1] / (double)sigma[k]);",
+     "float py = (float)(y[2 * k] / (double)sigma[k]);"),
+    ("sigma multiplied", "float px = (float)(y[2 * k] / (double)sigma[k]);",
+     "float px = (float)(y[2 * k] * (double)sigma[k]);"),
+    ("distance sign", "float dx = px - cb[2 * j];", "float dx = px + cb[2 * j];"),
+    ("ties to highest index", "if (d < best_d) {", "if (d <= best_d) {"),
+    ("norm without sqrt", "double r = sqrt(r2);", "double r = r2;"),
+    ("MSB-first packing", "out[q / 8] |= (uint8_t)(1u << (q % 8));", "out[q / 8] |= (uint8_t)(0x80u >> (q % 8));"),
+    ("decode keeps channel scale", "* v[j]) / (double)s[j];", "* v[j]);"),
+    ("decode wrong column", "acc += H[(size_t)k * block + jj] * x[(size_t)t * block + k];",
+     "acc += H[(size_t)k * block + (jj ^ 1)] * x[(size_t)t * block + k];"),
+    ("decode drops sign mask", "((rn * eps_of(sign_bits, j)) * v[j])", "((rn * 1.0) * v[j])"),
+    ("decode drops sigma", "x[2 * k] = (double)sigma[k] * (double)cb[2 * idx[k]];",
+     "x[2 * k] = (double)cb[2 * idx[k]];"),
+    ("Lloyd divides by n+1", "cb[2 * j] = (float)(((double)sx[j] * 0x1p-32) / (double)cnt[j]);",
+     "cb[2 * j] = (float)(((double)sx[j] * 0x1p-32) / (double)(cnt[j] + 1));"),
+    ("Lloyd resets empty cells", "if (cnt[j] > 0) { /* centroid", "if (1) { if (!cnt[j]) cnt[j] = 1; /* centroid"),
+    ("calibration counts zero rows", "sum[k] / (double)n_nz", "sum[k] / (double)n_rows"),
+    ("calibration constant", "sqrt(ORACLE_PI / 2.0)", "sqrt(2.0 / ORACLE_PI)"),
+    ("f16 truncates", "return rint(x / quantum) * quantum;", "return trunc(x / quantum) * quantum;"),
+    ("no row alignment", "return (used + 15) / 16 * 16;", "return used;"),
+    ("block cap 512", "while (b < 1024 && d_in % (2 * b) == 0)", "while (b < 512 && d_in % (2 * b) == 0)"),
+    ("bpw norm bits", "return bits / 2.0 + 16.0 / d_in;", "return bits / 2.0 + 32.0 / d_in;"),
+    ("stored norm not rounded via float", "nh = oracle_f16_from_f32((float)r);", "nh = oracle_f16_from_f32((float)(r * 1.001));"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_planted_mistake(tmp_path, name, old, new):
+    import oracle
+    src = open(SRC).read()
+    assert src.count(old) == 1, "mutation anchor must be unique: %r" % old
+    variant = tmp_path / "qamw_oracle_mutant.c"
+    variant.write_text(src.replace(old, new))
+    lib = str(tmp_path / "libmutant.so")
+    oracle.compile_to(str(variant), lib)
+    env = dict(os.environ, ORACLE_LIB=lib, OMP_NUM_THREADS="4")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, "planted mistake '%s' passed every pin:\n%s" % (name, r.stdout[-2000:])
