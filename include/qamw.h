@@ -1,0 +1,157 @@
+/*
+ * qamw.h -- C ABI of libqamw.so, the QAM-W weight codec on AMD Instinct MI355X (gfx950).
+ *
+ * QAM-W is defined in "QAM-W: Joint 2D Codebook Quantization for LLM Weights via Hadamard
+ * Rotation and Activation-Aware Scaling" (Sharma and Dobek, arXiv 2605.26339), section 3.
+ * Each entry point below names the passage that defines the operation it computes.
+ *
+ * General conventions
+ *   - Pointers prefixed d_ are device pointers (HBM of the current HIP device), owned by the
+ *     caller, and must stay valid until the work queued on `stream` has finished.
+ *   - `stream` is a hipStream_t passed as void*; NULL selects the default stream.  Every call
+ *     only queues work on that stream and never synchronizes with the host.
+ *   - The library keeps no state between calls and allocates no device memory: scratch lives
+ *     in the caller's workspace (sizes from the *_workspace / qamw_index_bytes helpers).
+ *   - Return value: QAMW_OK, or a negative QAMW_ERR_* code computed by host code before any
+ *     launch (bad argument, unsupported shape, short workspace) or from a failed launch.
+ *     Nothing is queued when an argument error is returned.
+ *   - Data faults found while running (non-finite weights, non-positive scale, row norm out
+ *     of f16 range, training point out of range) are OR-ed as QAMW_FLAG_* bits into *d_status
+ *     when d_status is not NULL; outputs for the affected rows/points are then unspecified.
+ *   - Matrices are row-major: element (i, j) of W is at d_w[i * ld_w + j].
+ *   - Concurrent calls on different streams are safe when they use different workspaces.
+ */
+#ifndef QAMW_H
+#define QAMW_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { QAMW_F32 = 0, QAMW_BF16 = 1 } qamw_dtype;
+
+enum {
+    QAMW_OK = 0,
+    QAMW_ERR_ARG = -1,         /* invalid argument (shape, pointer, range)                   */
+    QAMW_ERR_UNSUPPORTED = -2, /* valid by the paper but outside what the kernels implement  */
+    QAMW_ERR_WORKSPACE = -3,   /* workspace / index buffer smaller than required             */
+    QAMW_ERR_HIP = -4          /* a HIP launch failed                                        */
+};
+
+enum {
+    QAMW_FLAG_NONFINITE = 1,   /* w_ij * s_j or the row norm is not finite                    */
+    QAMW_FLAG_BAD_SCALE = 2,   /* some s_j <= 0 or NaN                                        */
+    QAMW_FLAG_NORM_RANGE = 4,  /* the row norm overflows f16                                  */
+    QAMW_FLAG_POINT_RANGE = 8  /* a training point is non-finite or out of the fixed-point range */
+};
+
+/* Bytes per row of the packed index stream: ceil((d_in/2) * bits / 8) rounded up to 16.
+ * Index k of a row occupies stream bits k*bits .. k*bits+bits-1, least significant first;
+ * stream bit q is bit q%8 of byte q/8; padding bytes are zero.
+ * (Section 3.1 step 6 and section 3.7: bit-packed indices with row-level alignment.)
+ * Returns 0 for invalid arguments. */
+size_t qamw_row_stride(int32_t d_in, int32_t bits);
+
+/* Section 3.3: the block size used when `block` is 0 -- the largest power of two dividing
+ * d_in, at most 1024.  Returns 0 when d_in <= 0. */
+int32_t qamw_default_block(int32_t d_in);
+
+/* Size of the search index that qamw_codebook_index writes for a 2^bits-entry codebook. */
+size_t qamw_index_bytes(int32_t bits);
+
+/* Workspace bytes for qamw_encode on a d_out x d_in matrix (calibration partial sums). */
+size_t qamw_encode_workspace(int32_t d_out, int32_t d_in, int32_t bits);
+
+/* Workspace bytes for qamw_codebook_train. */
+size_t qamw_train_workspace(int64_t n_points, int32_t bits);
+
+/* Section 3.6, eq. 2: train the single 2D codebook C = {c_0 .. c_{K-1}}, K = 2^bits, by Lloyd
+ * iterations on samples of the unit circular Gaussian.
+ *   d_points   n_points x 2 fp32, (x, y) interleaved.  n_points >= K.
+ *   iters      number of Lloyd iterations (>= 0).
+ *   d_init     K x 2 fp32 starting codebook, or NULL to start from the first K points.
+ *   d_codebook K x 2 fp32 output (may alias d_init).
+ *   d_err_trace NULL or iters int64 entries: entry t = sum over points of round(D * 2^32)
+ *              (modulo 2^64) for the assignment of iteration t, D the squared distance to the
+ *              assigned codeword; MSE_t = entry / 2^32 / n_points.
+ * Each iteration assigns every point to its nearest codeword (fp32 distance
+ * fl(fl(dx*dx) + fl(dy*dy)), dx = fl(px - cx); ties to the lowest index), sums the assigned
+ * points as 64-bit integers of round(x * 2^32), and moves each non-empty codeword to
+ * fl32((sum * 2^-32) / count); an empty cell keeps its codeword.  Integer sums make the result
+ * independent of thread order.  Points that are non-finite or have |x| or |y| >=
+ * min(2^(31 - ceil(log2 n_points)), 4096) are skipped and set QAMW_FLAG_POINT_RANGE.
+ * Limits: 1 <= bits <= 12. */
+int qamw_codebook_train(const float* d_points, int64_t n_points, int32_t bits, int32_t iters,
+                        const float* d_init, float* d_codebook, int64_t* d_err_trace,
+                        int32_t* d_status, void* d_ws, size_t ws_bytes, void* stream);
+
+/* Build the nearest-codeword search index of a codebook (section 3.6: encoding maps each
+ * normalized pair to its Euclidean-nearest entry).  The index is a uniform grid over the
+ * codebook's extent; each cell lists, in increasing order, every codeword that can be the
+ * nearest (or tied nearest) to a point of the cell, with a margin that covers fp32 rounding,
+ * so searching a cell's list returns exactly what a search over all K codewords returns.
+ *   d_index  device buffer of at least qamw_index_bytes(bits) bytes; it stays valid for this
+ *            codebook until the codebook changes.  Limits: 1 <= bits <= 12. */
+int qamw_codebook_index(const float* d_codebook, int32_t bits, void* d_index, size_t index_bytes,
+                        void* stream);
+
+/* Section 3.6: nearest codeword of n 2D points (fp32, interleaved), written to d_idx (int32),
+ * using an index from qamw_codebook_index.  Same distance and tie rule as above. */
+int qamw_nearest(const float* d_points, int64_t n, const float* d_codebook, int32_t bits,
+                 const void* d_index, int32_t* d_idx, void* stream);
+
+/* Section 3.1 (encoder) with section 3.4 (pair calibration) and section 3.8 (activation-aware
+ * per-channel scale).  For every row i of W:
+ *   a_j = w_ij * s_j (double), r = ||a||_2; r == 0 gives a zero row (norm 0, all indices 0);
+ *   y = blockdiag(H_b) (eps . a / r), H_b the Sylvester-ordered Hadamard matrix / sqrt(b),
+ *   eps_j = -1 where bit j%32 of d_sign_bits[j/32] is set, else +1 (section 3.3);
+ *   p_k = (fl32(y_2k / sigma_k), fl32(y_2k+1 / sigma_k)), idx_k = nearest codeword;
+ *   norm_i = f16(fl32(r)) round-to-nearest-even (section 3.2: 16-bit row norm);
+ *   indices packed as in qamw_row_stride.
+ * Arguments:
+ *   d_w, w_dtype   weights (QAMW_F32 or QAMW_BF16), d_out x d_in, leading dimension ld_w >= d_in.
+ *   d_scale        d_in fp32 channel scales s_j > 0, or NULL for all ones.
+ *   d_sign_bits    (d_in + 31) / 32 words of sign-mask bits, or NULL for all +1.
+ *   block          Hadamard block size b: a power of two in [2, 1024] dividing d_in, or 0 for
+ *                  qamw_default_block(d_in).  d_in must be even; d_in / E must be at most 1024
+ *                  for E = 16 (b <= 128) and at most 512 for E = 32 (b = 256, 512) or E = 64
+ *                  (b = 1024), i.e. d_in <= 16384, 16384 and 32768; else QAMW_ERR_UNSUPPORTED.
+ *   d_codebook, bits, d_index   K = 2^bits codebook and its index; 1 <= bits <= 12.
+ *   d_sigma_in     d_in/2 fp32 per-pair scales to use, or NULL to calibrate (eq. 1):
+ *                  sigma_k = fl32(mean |z_k| / sqrt(pi/2)), mean in double over the non-zero
+ *                  finite rows among rows 0 .. min(d_out, 1024) - 1; 1/sqrt(d_in) when there
+ *                  is no such row or the mean is 0.
+ *   d_sigma_out    d_in/2 fp32 output of the sigma used (written when calibrating; when
+ *                  d_sigma_in is given it may be NULL or receives a copy).
+ *   d_norm_f16     d_out uint16 (IEEE binary16 bit patterns).
+ *   d_codes        d_out x qamw_row_stride(d_in, bits) bytes.
+ *   d_ws, ws_bytes at least qamw_encode_workspace(d_out, d_in, bits) bytes. */
+int qamw_encode(const void* d_w, qamw_dtype w_dtype, int32_t d_out, int32_t d_in, int64_t ld_w,
+                const float* d_scale, const uint32_t* d_sign_bits, int32_t block,
+                const float* d_codebook, int32_t bits, const void* d_index,
+                const float* d_sigma_in, float* d_sigma_out, uint16_t* d_norm_f16, uint8_t* d_codes,
+                int32_t* d_status, void* d_ws, size_t ws_bytes, void* stream);
+
+/* Section 3.2 (decoder) and section 1 (dequantize to BF16 before the matrix product):
+ * unpack the indices, look up c[idx_k], rescale by sigma_k, apply R_inv = diag(eps)
+ * blockdiag(H_b), multiply by the stored f16 row norm and divide by s_j:
+ *   w^_ij = f16(norm_i) * eps_j * (H_b x)_j / s_j,  x_2k = sigma_k c_x[idx_k], x_2k+1 = sigma_k c_y[idx_k]
+ * computed in double and rounded to fp32 (QAMW_F32) or to fp32 then BF16 with
+ * round-to-nearest-even (QAMW_BF16).  A zero norm gives a row of +0.
+ * Arguments mirror qamw_encode; d_out_w is d_out x d_in with leading dimension ld_out >= d_in
+ * (ld_out even).  Same block / d_in limits as qamw_encode. */
+int qamw_decode(const uint8_t* d_codes, const uint16_t* d_norm_f16, const float* d_sigma,
+                const float* d_codebook, int32_t bits, const float* d_scale,
+                const uint32_t* d_sign_bits, int32_t d_out, int32_t d_in, int32_t block,
+                void* d_out_w, qamw_dtype out_dtype, int64_t ld_out, void* stream);
+
+/* Human-readable text for a return code. */
+const char* qamw_status_string(int code);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QAMW_H */

@@ -1,0 +1,135 @@
+"""The C ABI without a GPU: libqamw.so loads, exports every function include/qamw.h declares,
+and its host-side helpers and argument checks behave as documented.  Every call below is
+rejected by host code before any HIP call is made."""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import weight_quantization_codec_amd as q
+
+ARG, UNSUP, WS = q.ERR_ARG, q.ERR_UNSUPPORTED, q.ERR_WORKSPACE
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(q.LIB_PATH):
+        from weight_quantization_codec_amd import _build
+        _build.build()
+    return q.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = q.header_symbols()
+    assert len(names) == 11
+    out = subprocess.run(["nm", "-D", "--defined-only", q.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for n in names:
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+def test_header_is_plain_c():
+    import re
+    text = re.sub(r"/\*.*?\*/", "", open(q.HEADER_PATH).read(), flags=re.S)
+    for bad in ("hip_runtime", "torch", "hipStream_t", "namespace", "template"):
+        assert bad not in text
+    r = subprocess.run(["gcc", "-std=c99", "-fsyntax-only", "-x", "c", q.HEADER_PATH], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_row_stride_and_block_rule(lib, orc):
+    for d_in in (2, 6, 64, 512, 4096, 5120, 11008, 13824):
+        for bits in range(1, 17):
+            assert lib.qamw_row_stride(d_in, bits) == orc.row_stride(d_in, bits)
+        assert lib.qamw_default_block(d_in) == orc.default_block(d_in)
+    assert lib.qamw_row_stride(4096, 11) == 2816 and lib.qamw_row_stride(5120, 7) == 2240
+    assert lib.qamw_row_stride(0, 8) == 0 and lib.qamw_row_stride(7, 8) == 0 and lib.qamw_row_stride(8, 0) == 0
+    assert lib.qamw_default_block(0) == 0
+
+
+def test_sizes(lib):
+    assert lib.qamw_index_bytes(11) > 0 and lib.qamw_index_bytes(13) == 0 and lib.qamw_index_bytes(0) == 0
+    assert lib.qamw_index_bytes(11) >= lib.qamw_index_bytes(7)
+    assert lib.qamw_encode_workspace(4096, 4096, 11) >= 128 * 2048 * 8
+    assert lib.qamw_encode_workspace(4096, 4095, 11) == 0
+    assert lib.qamw_train_workspace(1 << 20, 11) >= 3 * 2048 * 8
+
+
+FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation first
+
+
+def _enc(lib, **kw):
+    a = dict(w=FAKE, dt=q.BF16, d_out=16, d_in=256, ld=256, scale=None, sign=None, block=64, cb=FAKE, bits=8,
+             index=FAKE, sig_in=FAKE, sig_out=None, norm=FAKE, codes=FAKE, status=None, ws=None, ws_bytes=0)
+    a.update(kw)
+    return lib.qamw_encode(a["w"], a["dt"], a["d_out"], a["d_in"], a["ld"], a["scale"], a["sign"], a["block"],
+                           a["cb"], a["bits"], a["index"], a["sig_in"], a["sig_out"], a["norm"], a["codes"],
+                           a["status"], a["ws"], a["ws_bytes"], None)
+
+
+def _dec(lib, **kw):
+    a = dict(codes=FAKE, norm=FAKE, sigma=FAKE, cb=FAKE, bits=8, scale=None, sign=None, d_out=16, d_in=256,
+             block=64, out=FAKE, dt=q.BF16, ld=256)
+    a.update(kw)
+    return lib.qamw_decode(a["codes"], a["norm"], a["sigma"], a["cb"], a["bits"], a["scale"], a["sign"],
+                           a["d_out"], a["d_in"], a["block"], a["out"], a["dt"], a["ld"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d_in=255, ld=255), ARG), (dict(d_in=0), ARG), (dict(d_out=-1), ARG), (dict(dt=7), ARG),
+    (dict(block=3), ARG), (dict(block=48), ARG), (dict(block=2048), ARG), (dict(block=512), ARG),
+    (dict(ld=128), ARG), (dict(bits=0), ARG), (dict(bits=17), ARG), (dict(bits=13), UNSUP),
+    (dict(sig_in=None, sig_out=None), ARG), (dict(w=None), ARG), (dict(codes=None), ARG),
+    (dict(index=None), ARG), (dict(codes=FAKE + 2), ARG), (dict(cb=FAKE + 4), ARG), (dict(w=FAKE + 1), ARG),
+    (dict(sig_in=None, sig_out=FAKE, ws=None), WS), (dict(sig_in=None, sig_out=FAKE, ws=FAKE, ws_bytes=64), WS),
+    (dict(d_in=16384 + 256, ld=16384 + 256, block=64), UNSUP), (dict(d_in=16384 + 256, ld=16640, block=256), UNSUP),
+])
+def test_encode_rejects(lib, kw, code):
+    assert _enc(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d_in=255), ARG), (dict(block=12), ARG), (dict(ld=255), ARG), (dict(ld=128), ARG), (dict(dt=3), ARG),
+    (dict(bits=14), UNSUP), (dict(bits=0), ARG), (dict(codes=None), ARG), (dict(out=FAKE + 2), ARG),
+    (dict(out=FAKE + 4, dt=q.F32), ARG), (dict(sigma=None), ARG), (dict(d_out=-3), ARG),
+])
+def test_decode_rejects(lib, kw, code):
+    assert _dec(lib, **kw) == code
+
+
+def test_empty_decode_is_a_noop(lib):
+    assert _dec(lib, d_out=0, codes=None, norm=None, sigma=None, cb=None, out=None) == q.OK
+
+
+def test_train_and_index_reject(lib):
+    assert lib.qamw_codebook_train(FAKE, 100, 8, 5, None, FAKE, None, None, FAKE, 1 << 20, None) == ARG  # n < K
+    assert lib.qamw_codebook_train(FAKE, 1000, 8, -1, None, FAKE, None, None, FAKE, 1 << 20, None) == ARG
+    assert lib.qamw_codebook_train(FAKE, 1000, 13, 5, None, FAKE, None, None, FAKE, 1 << 20, None) == UNSUP
+    assert lib.qamw_codebook_train(FAKE, 1000, 8, 5, None, FAKE, None, None, FAKE, 16, None) == WS
+    assert lib.qamw_codebook_train(FAKE + 4, 1000, 8, 5, None, FAKE, None, None, FAKE, 1 << 20, None) == ARG
+    assert lib.qamw_codebook_index(FAKE, 11, FAKE, 100, None) == WS
+    assert lib.qamw_codebook_index(FAKE, 11, FAKE + 8, 1 << 24, None) == WS
+    assert lib.qamw_codebook_index(None, 11, FAKE, 1 << 24, None) == ARG
+    assert lib.qamw_nearest(FAKE, -1, FAKE, 8, FAKE, FAKE, None) == ARG
+    assert lib.qamw_nearest(None, 0, None, 8, None, None, None) == q.OK
+
+
+def test_status_strings(lib):
+    for c in (0, -1, -2, -3, -4, 99):
+        assert isinstance(q.status_string(c), str) and q.status_string(c)
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(RuntimeError):
+        q.load(str(tmp_path / "missing.so"))
+
+
+def test_product_path_does_not_use_the_oracle():
+    pkg = os.path.dirname(q.__file__)
+    for root, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(root, f)).read()
+                assert "oracle" not in text.lower(), f

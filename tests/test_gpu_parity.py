@@ -1,0 +1,277 @@
+"""GPU parity: libqamw.so (HIP, gfx950) against the CPU oracle on seeded inputs.
+
+Covers the search index (exact nearest codeword), decode cross-fed with oracle codes, encode
+(calibration, norms, indices, packed bytes), the encode -> decode round trip, Lloyd training,
+data-fault flags, and edge shapes: ragged row counts, partial wavefronts, every block size from
+2 to 1024, index widths 1..12 bits, padded leading dimensions and zero rows.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from helpers import (DEV, assert_bf16_within_1ulp, assert_rel_l2, check_indices, gpu_decode, gpu_encode, log, t,
+                     unpack_rows)
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+@pytest.fixture(scope="module")
+def q():
+    import weight_quantization_codec_amd as q
+    q.load()
+    assert torch.cuda.is_available()
+    return q
+
+
+def golden_cb(name):
+    z = np.load(os.path.join(GOLDEN, name + ".npz"))
+    return z["codebook"], z["trace"], z["meta"]
+
+
+def rand_problem(seed, d_out, d_in, dtype="bf16", heavy=True):
+    rng = np.random.default_rng(seed)
+    if heavy:
+        w = rng.standard_t(5, size=(d_out, d_in)) * 0.015
+        cols = rng.choice(d_in, size=max(1, d_in // 100), replace=False)
+        w[:, cols] *= 10
+    else:
+        w = rng.standard_normal((d_out, d_in)) * 0.02
+    w = w.astype(np.float32)
+    if dtype == "bf16":
+        w = torch.from_numpy(w).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    s = (np.abs(rng.standard_normal(d_in)) ** 0.5 + 0.1).astype(np.float32)
+    sb = rng.integers(0, 2**32, size=(d_in + 31) // 32, dtype=np.uint64).astype(np.uint32)
+    return w, s, sb
+
+
+def rand_cb(seed, bits):
+    rng = np.random.default_rng(1000 + seed)
+    return rng.standard_normal((1 << bits, 2)).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------- search index
+
+def _probes(cb, n, seed):
+    rng = np.random.default_rng(seed)
+    parts = [rng.standard_normal((n, 2)) * sc for sc in (0.5, 1.0, 2.0, 4.0)]
+    ext = float(np.abs(cb).max())
+    parts.append(rng.uniform(-1.5 * ext, 1.5 * ext, size=(n, 2)))
+    parts.append(cb.astype(np.float64))
+    # midpoints between each codeword and a close neighbour: near-exact ties
+    j = np.arange(len(cb))
+    k = (j * 7 + 1) % len(cb)
+    d = ((cb[:, None, :].astype(np.float64) - cb[None, :, :]) ** 2).sum(-1) if len(cb) <= 4096 else None
+    if d is not None:
+        d[j, j] = np.inf
+        k = d.argmin(1)
+    parts.append((cb.astype(np.float64) + cb[k]) / 2)
+    parts.append(np.array([[ext * 3, 0], [0, -ext * 5], [1e30, 1e30], [np.nan, 0], [np.inf, 1.0], [0, 0]]))
+    return np.concatenate(parts).astype(np.float32)
+
+
+@pytest.mark.parametrize("name", ["cfg0", "cfg1", "cfg3", "rand12", "rand1", "dup4", "grid8"])
+def test_nearest_matches_bruteforce(q, orc, name):
+    if name == "cfg0":
+        cb, bits = golden_cb("cb_cfg0_k256")[0], 8
+    elif name == "cfg1":
+        cb, bits = golden_cb("cb_cfg1_k2048")[0], 11
+    elif name == "cfg3":
+        cb, bits = golden_cb("cb_cfg3_k128")[0], 7
+    elif name == "rand12":
+        cb, bits = rand_cb(12, 12), 12
+    elif name == "rand1":
+        cb, bits = rand_cb(1, 1), 1
+    elif name == "dup4":  # repeated codewords: ties must go to the lowest index
+        base = rand_cb(4, 2)
+        cb, bits = np.concatenate([base, base, base[::-1], base]).astype(np.float32), 4
+    else:  # lattice codebook: many exact ties on the cell boundaries
+        g = np.arange(16) - 7.5
+        cb, bits = np.stack(np.meshgrid(g, g), -1).reshape(-1, 2).astype(np.float32) * 0.25, 8
+    n = 60000 if bits >= 11 else 200000
+    p = _probes(cb, n, bits)
+    log("nearest %s: K=%d probes=%d" % (name, len(cb), len(p)))
+    cbd = t(cb)
+    idx = q.codebook_index(cbd, bits)
+    got = q.nearest(t(p), cbd, bits, idx).cpu().numpy()
+    ref, _ = orc.nearest(p, cb)
+    np.testing.assert_array_equal(got, ref)
+
+
+# ----------------------------------------------------------------------------- decode (oracle codes)
+
+SHAPES = [  # d_out, d_in, block, bits
+    (64, 512, 64, 8), (37, 320, 64, 5), (17, 256, 2, 3), (9, 128, 16, 7), (33, 1024, 32, 11),
+    (12, 2048, 256, 11), (8, 4096, 512, 12), (5, 2048, 1024, 1), (40, 4096, 128, 11),
+    (3, 13824, 128, 11), (4, 11008, 256, 11), (6, 5120, 128, 7), (7, 192, 4, 9), (11, 96, 8, 6),
+]
+
+
+def _shape_id(s):
+    return "x".join(map(str, s))
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=_shape_id)
+def test_decode_crossfed(q, orc, shape):
+    d_out, d_in, block, bits = shape
+    w, s, sb = rand_problem(d_out * 31 + d_in, d_out, d_in)
+    w[min(2, d_out - 1)] = 0
+    cb = rand_cb(bits, bits)
+    sigma, _ = orc.calibrate(w, s, sb, block)
+    enc = orc.encode(w, s, sb, block, cb, bits, sigma, want_idx=False)
+    ref = orc.decode(enc["codes"], enc["norm"], d_in, sigma, cb, bits, s, sb, block)
+    log("decode %s" % (shape,))
+    got16 = gpu_decode(q, enc["codes"], enc["norm"], sigma, cb, bits, s, sb, d_in, block)
+    n_diff = assert_bf16_within_1ulp(got16, ref["bf16"])
+    got32 = gpu_decode(q, enc["codes"], enc["norm"], sigma, cb, bits, s, sb, d_in, block, out_dtype=torch.float32)
+    assert_rel_l2(got32, ref["f32"], 1e-5)
+    assert n_diff <= max(2, got16.size // 100000)
+    assert not got16[min(2, d_out - 1)].any()
+
+
+def test_decode_padded_output_and_defaults(q, orc):
+    d_out, d_in, block, bits = 21, 640, 128, 8
+    w, _, _ = rand_problem(5, d_out, d_in)
+    cb = rand_cb(8, bits)
+    ones = np.ones(d_in, np.float32)
+    plus = np.zeros((d_in + 31) // 32, np.uint32)
+    sigma, _ = orc.calibrate(w, ones, plus, block)
+    enc = orc.encode(w, ones, plus, block, cb, bits, sigma, want_idx=False)
+    ref = orc.decode(enc["codes"], enc["norm"], d_in, sigma, cb, bits, ones, plus, block)
+    got = gpu_decode(q, enc["codes"], enc["norm"], sigma, cb, bits, None, None, d_in, block, ld=d_in + 64)
+    assert_bf16_within_1ulp(got, ref["bf16"])
+
+
+# ----------------------------------------------------------------------------- encode
+
+def _encode_case(q, orc, shape, dtype="bf16", given_sigma=False, ld=None, seed=0):
+    d_out, d_in, block, bits = shape
+    w, s, sb = rand_problem(seed + d_out * 7 + d_in, d_out, d_in, dtype=dtype)
+    w[min(1, d_out - 1)] = 0
+    cb = rand_cb(bits + 50, bits)
+    sig_ref, st_ref = orc.calibrate(w[:1024], s, sb, block)
+    sigma_in = None
+    if given_sigma:
+        sig_ref = (np.abs(np.random.default_rng(seed).standard_normal(d_in // 2)) * 0.05 + 0.01).astype(np.float32)
+        sigma_in = sig_ref
+    ref = orc.encode(w, s, sb, block, cb, bits, sig_ref, want_p=True)
+    log("encode %s %s sigma=%s ld=%s" % (shape, dtype, "given" if given_sigma else "calibrated", ld))
+    got = gpu_encode(q, w, s, sb, block, cb, bits, sigma=sigma_in, ld=ld)
+    np.testing.assert_array_equal(got["sigma"], sig_ref)
+    np.testing.assert_array_equal(got["norm"], ref["norm"])
+    assert got["status"] == ref["status"] == 0
+    gidx = unpack_rows(orc, got["codes"], bits, d_in)
+    flips = check_indices(gidx, ref["idx"], ref["p"], cb)
+    if flips == 0:
+        np.testing.assert_array_equal(got["codes"], ref["codes"])
+    return got, ref, cb, sig_ref, s, sb
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=_shape_id)
+def test_encode_matches_oracle(q, orc, shape):
+    _encode_case(q, orc, shape)
+
+
+@pytest.mark.parametrize("variant", ["fp32", "given_sigma", "padded_ld", "many_rows"])
+def test_encode_variants(q, orc, variant):
+    if variant == "fp32":
+        _encode_case(q, orc, (50, 512, 64, 8), dtype="fp32")
+    elif variant == "given_sigma":
+        _encode_case(q, orc, (30, 1024, 128, 11), given_sigma=True)
+    elif variant == "padded_ld":
+        _encode_case(q, orc, (25, 768, 256, 10), ld=768 + 40)
+    else:  # more rows than the calibration window and than the grid
+        _encode_case(q, orc, (1300, 256, 64, 6))
+
+
+def test_roundtrip_gpu_encode_gpu_decode(q, orc):
+    got, ref, cb, sigma, s, sb = _encode_case(q, orc, (48, 2048, 128, 11), seed=3)
+    dec_ref = orc.decode(ref["codes"], ref["norm"], 2048, sigma, cb, 11, s, sb, 128)
+    dec = gpu_decode(q, got["codes"], got["norm"], got["sigma"], cb, 11, s, sb, 2048, 128)
+    if np.array_equal(got["codes"], ref["codes"]):
+        assert_bf16_within_1ulp(dec, dec_ref["bf16"])
+
+
+def test_encode_is_deterministic(q):
+    w, s, sb = rand_problem(99, 300, 4096)
+    cb = rand_cb(11, 11)
+    a = gpu_encode(q, w, s, sb, 128, cb, 11)
+    b = gpu_encode(q, w, s, sb, 128, cb, 11)
+    for k in ("codes", "norm", "sigma"):
+        np.testing.assert_array_equal(a[k], b[k])
+
+
+def test_empty_matrix(q, orc):
+    d_in = 256
+    w = np.zeros((0, d_in), np.uint16)
+    cb = rand_cb(3, 6)
+    got = gpu_encode(q, w, None, None, 64, cb, 6)
+    assert got["codes"].shape == (0, q.row_stride(d_in, 6))
+    np.testing.assert_array_equal(got["sigma"], np.float32(1 / np.sqrt(d_in)))
+
+
+# ----------------------------------------------------------------------------- data-fault flags
+
+def test_status_flags(q):
+    d_out, d_in = 6, 256
+    w, s, sb = rand_problem(7, d_out, d_in, dtype="fp32")
+    cb = rand_cb(5, 6)
+    sig = np.full(d_in // 2, 0.05, np.float32)
+    assert gpu_encode(q, w, s, sb, 64, cb, 6, sigma=sig)["status"] == 0
+    w2 = w.copy()
+    w2[3, 17] = np.nan
+    assert gpu_encode(q, w2, s, sb, 64, cb, 6, sigma=sig)["status"] & 1
+    s2 = s.copy()
+    s2[9] = -1.0
+    assert gpu_encode(q, w, s2, sb, 64, cb, 6, sigma=sig)["status"] & 2
+    w3 = w.copy()
+    w3[2] *= 1e6
+    assert gpu_encode(q, w3, s, sb, 64, cb, 6, sigma=sig)["status"] == 4
+
+
+# ----------------------------------------------------------------------------- Lloyd
+
+def test_lloyd_bit_identical_small(q, orc, synth):
+    pts = synth.points(synth.CONFIG_SEED_BASE + 9, 4, 20000)
+    for bits, iters in ((1, 5), (4, 9), (8, 6), (10, 3)):
+        ref_cb, ref_tr, _ = orc.lloyd(pts, bits, iters)
+        cb, tr = q.codebook_train(t(pts), bits, iters)
+        np.testing.assert_array_equal(cb.cpu().numpy(), ref_cb)
+        np.testing.assert_array_equal(tr.cpu().numpy(), ref_tr)
+
+
+@pytest.mark.parametrize("name", ["cb_cfg0_k256", "cb_cfg3_k128", "cb_cfg1_k2048", "cb_cfg2_k2048"])
+def test_lloyd_matches_golden(q, synth, name):
+    path = os.path.join(GOLDEN, name + ".npz")
+    if not os.path.exists(path):
+        pytest.skip("golden codebook %s not generated" % name)
+    cb_ref, tr_ref, meta = golden_cb(name)
+    cfg_i, sid, n, bits, iters = [int(x) for x in meta]
+    pts = synth.points(synth.config(cfg_i).seed, sid, n)
+    log("lloyd %s: n=%d K=%d iters=%d" % (name, n, 1 << bits, iters))
+    cb, tr = q.codebook_train(t(pts), bits, iters)
+    np.testing.assert_array_equal(cb.cpu().numpy(), cb_ref)
+    np.testing.assert_array_equal(tr.cpu().numpy(), tr_ref)
+
+
+def test_lloyd_resume_and_init(q, orc, synth):
+    pts = synth.points(synth.CONFIG_SEED_BASE + 11, 4, 30000)
+    full, trf = q.codebook_train(t(pts), 7, 8)
+    a, tra = q.codebook_train(t(pts), 7, 3)
+    b, trb = q.codebook_train(t(pts), 7, 5, init=a.clone())
+    np.testing.assert_array_equal(b.cpu().numpy(), full.cpu().numpy())
+    np.testing.assert_array_equal(torch.cat([tra, trb]).cpu().numpy(), trf.cpu().numpy())
+    ref, _, _ = orc.lloyd(pts, 7, 5, init=a.cpu().numpy())
+    np.testing.assert_array_equal(b.cpu().numpy(), ref)
+
+
+def test_lloyd_point_range_flag(q):
+    pts = np.random.default_rng(3).standard_normal((5000, 2)).astype(np.float32)
+    pts[17, 0] = 1e5
+    st = torch.zeros((1,), dtype=torch.int32, device=DEV)
+    q.codebook_train(t(pts), 4, 2, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) & 8

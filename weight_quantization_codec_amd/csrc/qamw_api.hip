@@ -1,0 +1,211 @@
+// C ABI of libqamw.so (declared in include/qamw.h).  Every argument is checked here, in host
+// code, before anything is queued; then the kernels are launched on the caller's stream.
+#include <cmath>
+
+#include "qamw.h"
+#include "qamw_device.hpp"
+#include "qamw_launch.hpp"
+
+using namespace qamw;
+
+namespace {
+
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+int log2i(int v) {
+    int l = 0;
+    while ((1 << l) < v) ++l;
+    return l;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Resolve and check the Hadamard block size; returns L = log2(b) or a negative error.
+int check_shape(int32_t d_in, int32_t block) {
+    if (d_in <= 0 || (d_in & 1)) return QAMW_ERR_ARG;
+    int32_t b = block == 0 ? qamw_default_block(d_in) : block;
+    if (b < 2 || b > 1024 || !is_pow2(b) || d_in % b) return QAMW_ERR_ARG;
+    int L = log2i(b);
+    int E = lane_elems(L);
+    // one lane per E columns, one workgroup per row: at most 1024 lanes (512 when E >= 32)
+    if (E <= 0 || d_in / E > (E >= 32 ? 512 : 1024)) return QAMW_ERR_UNSUPPORTED;
+    return L;
+}
+
+int check_bits(int32_t bits) {
+    if (bits < 1 || bits > 16) return QAMW_ERR_ARG;
+    if (bits > 12) return QAMW_ERR_UNSUPPORTED;
+    return QAMW_OK;
+}
+
+int hip_rc(hipError_t e) { return e == hipSuccess ? QAMW_OK : QAMW_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+size_t qamw_row_stride(int32_t d_in, int32_t bits) {
+    if (d_in <= 0 || (d_in & 1) || bits < 1 || bits > 16) return 0;
+    size_t used = ((size_t)(d_in / 2) * (size_t)bits + 7) / 8;
+    return (used + 15) / 16 * 16;
+}
+
+int32_t qamw_default_block(int32_t d_in) {
+    if (d_in <= 0) return 0;
+    int32_t b = 1;
+    while (b < 1024 && d_in % (2 * b) == 0) b *= 2;
+    return b;
+}
+
+size_t qamw_index_bytes(int32_t bits) {
+    if (check_bits(bits) != QAMW_OK) return 0;
+    size_t G = (size_t)index_grid_size(bits);
+    return (size_t)kIndexHeaderBytes + G * G * kIndexCap * sizeof(uint16_t);
+}
+
+size_t qamw_encode_workspace(int32_t d_out, int32_t d_in, int32_t bits) {
+    if (d_out < 0 || d_in <= 0 || (d_in & 1) || check_bits(bits) != QAMW_OK) return 0;
+    return calib_workspace(d_out, d_in);
+}
+
+size_t qamw_train_workspace(int64_t n_points, int32_t bits) {
+    if (n_points < 0 || check_bits(bits) != QAMW_OK) return 0;
+    return lloyd_workspace(bits);
+}
+
+int qamw_codebook_train(const float* d_points, int64_t n_points, int32_t bits, int32_t iters, const float* d_init,
+                        float* d_codebook, int64_t* d_err_trace, int32_t* d_status, void* d_ws, size_t ws_bytes,
+                        void* stream) {
+    int rc = check_bits(bits);
+    if (rc) return rc;
+    if (iters < 0 || !d_points || !d_codebook || n_points < ((int64_t)1 << bits)) return QAMW_ERR_ARG;
+    if (!aligned(d_points, 8) || !aligned(d_codebook, 8) || (d_init && !aligned(d_init, 8))) return QAMW_ERR_ARG;
+    if (!d_ws || !aligned(d_ws, 16) || ws_bytes < qamw_train_workspace(n_points, bits)) return QAMW_ERR_WORKSPACE;
+    return hip_rc(launch_lloyd(d_points, n_points, bits, iters, d_init, d_codebook, d_err_trace, d_status, d_ws,
+                               (hipStream_t)stream));
+}
+
+int qamw_codebook_index(const float* d_codebook, int32_t bits, void* d_index, size_t index_bytes, void* stream) {
+    int rc = check_bits(bits);
+    if (rc) return rc;
+    if (!d_codebook || !aligned(d_codebook, 8)) return QAMW_ERR_ARG;
+    if (!d_index || !aligned(d_index, 16) || index_bytes < qamw_index_bytes(bits)) return QAMW_ERR_WORKSPACE;
+    return hip_rc(launch_index_build(d_codebook, bits, d_index, (hipStream_t)stream));
+}
+
+int qamw_nearest(const float* d_points, int64_t n, const float* d_codebook, int32_t bits, const void* d_index,
+                 int32_t* d_idx, void* stream) {
+    int rc = check_bits(bits);
+    if (rc) return rc;
+    if (n < 0) return QAMW_ERR_ARG;
+    if (n == 0) return QAMW_OK;
+    if (!d_points || !d_codebook || !d_index || !d_idx || !aligned(d_points, 8) || !aligned(d_codebook, 8) ||
+        !aligned(d_index, 16))
+        return QAMW_ERR_ARG;
+    return hip_rc(launch_nearest(d_points, n, d_codebook, bits, d_index, d_idx, (hipStream_t)stream));
+}
+
+int qamw_encode(const void* d_w, qamw_dtype w_dtype, int32_t d_out, int32_t d_in, int64_t ld_w, const float* d_scale,
+                const uint32_t* d_sign_bits, int32_t block, const float* d_codebook, int32_t bits, const void* d_index,
+                const float* d_sigma_in, float* d_sigma_out, uint16_t* d_norm_f16, uint8_t* d_codes,
+                int32_t* d_status, void* d_ws, size_t ws_bytes, void* stream) {
+    if (d_out < 0 || (w_dtype != QAMW_F32 && w_dtype != QAMW_BF16)) return QAMW_ERR_ARG;
+    int L = check_shape(d_in, block);
+    if (L < 0) return L;
+    int rc = check_bits(bits);
+    if (rc) return rc;
+    if (ld_w < d_in) return QAMW_ERR_ARG;
+    if (!d_sigma_in && !d_sigma_out) return QAMW_ERR_ARG;
+    if (d_out > 0 && (!d_w || !d_codebook || !d_index || !d_norm_f16 || !d_codes)) return QAMW_ERR_ARG;
+    if (d_out > 0 && (!aligned(d_codes, 4) || !aligned(d_codebook, 8) || !aligned(d_index, 16) ||
+                      !aligned(d_w, w_dtype == QAMW_BF16 ? 2 : 4) || !aligned(d_norm_f16, 2)))
+        return QAMW_ERR_ARG;
+    const bool calibrate = d_sigma_in == nullptr;
+    if (calibrate && (!d_ws || !aligned(d_ws, 16) || ws_bytes < qamw_encode_workspace(d_out, d_in, bits)))
+        return QAMW_ERR_WORKSPACE;
+    hipStream_t st = (hipStream_t)stream;
+    const float* sigma = d_sigma_in;
+    if (calibrate) {
+        CalibArgs c{};
+        c.w = d_w;
+        c.w_bf16 = w_dtype == QAMW_BF16;
+        c.n_rows = d_out < 1024 ? d_out : 1024;
+        c.d_in = d_in;
+        c.ld = ld_w;
+        c.scale = d_scale;
+        c.sign = d_sign_bits;
+        c.n_groups = calib_groups(c.n_rows);
+        const size_t part_bytes = (size_t)(c.n_groups > 0 ? c.n_groups : 1) * (size_t)(d_in / 2) * sizeof(double);
+        c.partial = reinterpret_cast<double*>(d_ws);
+        c.nz = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(d_ws) + (part_bytes + 255) / 256 * 256);
+        hipError_t e = launch_calibrate(c, L, d_sigma_out, st);
+        if (e != hipSuccess) return QAMW_ERR_HIP;
+        sigma = d_sigma_out;
+    } else if (d_sigma_out && d_sigma_out != d_sigma_in) {
+        if (hipMemcpyAsync(d_sigma_out, d_sigma_in, sizeof(float) * (size_t)(d_in / 2), hipMemcpyDeviceToDevice, st) !=
+            hipSuccess)
+            return QAMW_ERR_HIP;
+    }
+    if (d_out == 0) return QAMW_OK;
+    EncodeArgs a{};
+    a.w = d_w;
+    a.w_bf16 = w_dtype == QAMW_BF16;
+    a.d_out = d_out;
+    a.d_in = d_in;
+    a.ld = ld_w;
+    a.scale = d_scale;
+    a.sign = d_sign_bits;
+    a.sigma = sigma;
+    a.cb = d_codebook;
+    a.bits = bits;
+    a.index = d_index;
+    a.norm = d_norm_f16;
+    a.codes = d_codes;
+    a.stride = qamw_row_stride(d_in, bits);
+    a.status = d_status;
+    return hip_rc(launch_encode(a, L, st));
+}
+
+int qamw_decode(const uint8_t* d_codes, const uint16_t* d_norm_f16, const float* d_sigma, const float* d_codebook,
+                int32_t bits, const float* d_scale, const uint32_t* d_sign_bits, int32_t d_out, int32_t d_in,
+                int32_t block, void* d_out_w, qamw_dtype out_dtype, int64_t ld_out, void* stream) {
+    if (d_out < 0 || (out_dtype != QAMW_F32 && out_dtype != QAMW_BF16)) return QAMW_ERR_ARG;
+    int L = check_shape(d_in, block);
+    if (L < 0) return L;
+    int rc = check_bits(bits);
+    if (rc) return rc;
+    if (ld_out < d_in || (ld_out & 1)) return QAMW_ERR_ARG;
+    if (d_out == 0) return QAMW_OK;
+    if (!d_codes || !d_norm_f16 || !d_sigma || !d_codebook || !d_out_w) return QAMW_ERR_ARG;
+    if (!aligned(d_codebook, 8) || !aligned(d_codes, 4) || !aligned(d_norm_f16, 2) ||
+        !aligned(d_out_w, out_dtype == QAMW_BF16 ? 4 : 8))
+        return QAMW_ERR_ARG;
+    DecodeArgs a{};
+    a.codes = d_codes;
+    a.stride = qamw_row_stride(d_in, bits);
+    a.norm = d_norm_f16;
+    a.sigma = d_sigma;
+    a.cb = d_codebook;
+    a.bits = bits;
+    a.scale = d_scale;
+    a.sign = d_sign_bits;
+    a.d_out = d_out;
+    a.d_in = d_in;
+    a.out = d_out_w;
+    a.out_bf16 = out_dtype == QAMW_BF16;
+    a.ld = ld_out;
+    return hip_rc(launch_decode(a, L, (hipStream_t)stream));
+}
+
+const char* qamw_status_string(int code) {
+    switch (code) {
+    case QAMW_OK: return "ok";
+    case QAMW_ERR_ARG: return "invalid argument";
+    case QAMW_ERR_UNSUPPORTED: return "unsupported shape or codebook size";
+    case QAMW_ERR_WORKSPACE: return "workspace or index buffer too small";
+    case QAMW_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

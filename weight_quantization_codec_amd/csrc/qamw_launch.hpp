@@ -1,0 +1,81 @@
+// Host-side launchers of the QAM-W kernels.  Arguments are validated by the C ABI layer
+// (qamw_api.cpp) before any of these is called.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qamw {
+
+// Let `kernel` use more than the default 64 KiB of dynamic LDS (gfx950 has 160 KiB per CU).
+template <typename K>
+inline void allow_lds(K kernel, size_t bytes) {
+    if (bytes > 65536)
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)bytes);
+}
+
+int index_grid_size(int bits);
+hipError_t launch_index_build(const float* cb, int bits, void* index, hipStream_t st);
+hipError_t launch_nearest(const float* pts, int64_t n, const float* cb, int bits, const void* index, int32_t* out,
+                          hipStream_t st);
+
+struct EncodeArgs {
+    const void* w;
+    int w_bf16;
+    int d_out, d_in;
+    int64_t ld;
+    const float* scale;        // may be null (all ones)
+    const uint32_t* sign;      // may be null (all +1)
+    const float* sigma;        // d_in/2
+    const float* cb;
+    int bits;
+    const void* index;
+    uint16_t* norm;
+    uint8_t* codes;
+    size_t stride;
+    int32_t* status;
+};
+
+struct CalibArgs {
+    const void* w;
+    int w_bf16;
+    int n_rows, d_in;
+    int64_t ld;
+    const float* scale;
+    const uint32_t* sign;
+    double* partial;           // [n_groups][d_in/2]
+    int32_t* nz;               // [n_groups]
+    int n_groups;
+};
+
+struct DecodeArgs {
+    const uint8_t* codes;
+    size_t stride;
+    const uint16_t* norm;
+    const float* sigma;
+    const float* cb;
+    int bits;
+    const float* scale;
+    const uint32_t* sign;
+    int d_out, d_in;
+    void* out;
+    int out_bf16;
+    int64_t ld;
+};
+
+// Elements per lane of the transform layout for block size 2^L.
+int lane_elems(int L);
+int calib_groups(int n_rows);
+size_t calib_workspace(int d_out, int d_in);
+
+hipError_t launch_calibrate(const CalibArgs& a, int L, float* sigma_out, hipStream_t st);
+hipError_t launch_encode(const EncodeArgs& a, int L, hipStream_t st);
+hipError_t launch_decode(const DecodeArgs& a, int L, hipStream_t st);
+
+struct LloydAcc;   // device accumulators, defined in k_lloyd.hip
+size_t lloyd_workspace(int bits);
+hipError_t launch_lloyd(const float* pts, int64_t n, int bits, int iters, const float* init, float* cb,
+                        int64_t* trace, int32_t* status, void* ws, hipStream_t st);
+
+}  // namespace qamw
