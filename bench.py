@@ -1,0 +1,232 @@
+"""Benchmark of the QAM-W codec hot path on one MI355X.
+
+Workload (the configuration the headline metric is quoted on): one attention-projection-shaped
+weight matrix W of 4096 x 4096 bf16 (Student-t(5) x 0.015, 41 outlier columns x 10, channel scale
+s_j = |N(0,1)|^0.5 + 0.1), Hadamard block 128, K = 2048 codebook (11-bit pair index) trained by 20
+Lloyd iterations on 2^20 unit-circular-Gaussian points.
+
+One step = encode (pair calibration over the first 1024 rows + encode of all rows) followed by
+decode to BF16, with W, the codes and the output already in HBM.  Steps rotate over enough
+copies of the buffers (>= 1 GiB) that the 256 MiB last-level cache cannot serve repeats.
+The codebook training and the search-index build depend on the codebook only; they run and
+are timed once in the same run and reported beside the step.
+
+Prints one JSON line.  --gpus N with N > 1 is not supported (single-GPU build).
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "encode Mweights/s + decode GB/s (BF16 out), 4096×4096 W, K=2048 codebook"
+HBM_PEAK_GBPS = 8000.0
+# 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz: one 32/64-bit VALU lane operation per lane per clock
+VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--rot-gib", type=float, default=1.25, help="bytes of rotated buffers")
+    return ap.parse_args()
+
+
+def source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(kernel_key, src_files, per_launch_alg_bytes):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it is current."""
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+        k = d["kernels"][kernel_key]
+        if k.get("source_hash") != source_hash(src_files):
+            return None
+        return k["hbm_bytes_per_dispatch"]
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (got --gpus %d)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth_inputs as synth
+    import weight_quantization_codec_amd as q
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q.load()
+    cfg = synth.config(1)
+    m = cfg.matrices[0]
+    d_out, d_in, block, bits = m.d_out, m.d_in, cfg.block, cfg.bits[0]
+    n_w = d_out * d_in
+
+    # ---------------------------------------------------------------- inputs (host -> HBM, untimed)
+    w_host = m.weights()
+    s_host = m.channel_scale()
+    sb_host = synth.sign_bits(d_in)
+    pts_host = synth.points(cfg.seed, synth.SID_POINTS, cfg.n_points)
+    w0 = torch.from_numpy(w_host.view(np.int16)).view(torch.bfloat16).to(dev)
+    scale = torch.from_numpy(s_host).to(dev)
+    sign = torch.from_numpy(sb_host.view(np.int32)).to(dev)
+    pts = torch.from_numpy(pts_host).to(dev)
+
+    # plain copy of known size: calibrates the FETCH_SIZE / WRITE_SIZE counters in profiled runs
+    cp_src = torch.ones((128 << 20,), dtype=torch.float32, device=dev)   # 512 MiB read, 512 MiB written
+    cp_dst = torch.empty_like(cp_src)
+    torch.mul(cp_src, 1.0, out=cp_dst)
+    torch.cuda.synchronize()
+    del cp_src, cp_dst
+
+    # ---------------------------------------------------------------- codebook + index (timed once)
+    stream = torch.cuda.current_stream()
+    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    e0.record(stream)
+    cb, trace = q.codebook_train(pts, bits, cfg.lloyd_iters)
+    e1.record(stream)
+    index = q.codebook_index(cb, bits)
+    e2.record(stream)
+    torch.cuda.synchronize()
+    train_ms, index_ms = e0.elapsed_time(e1), e1.elapsed_time(e2)
+    mse = float(trace[-1].item()) / 2**32 / cfg.n_points
+
+    # ---------------------------------------------------------------- rotated buffers
+    stride = q.row_stride(d_in, bits)
+    per_set = n_w * 2 + d_out * stride + n_w * 2 + d_out * 2
+    n_sets = max(2, int(math.ceil(args.rot_gib * (1 << 30) / per_set)))
+    sets = []
+    for _ in range(n_sets):
+        sets.append({
+            "w": w0.clone(),
+            "codes": torch.empty((d_out, stride), dtype=torch.uint8, device=dev),
+            "norm": torch.empty((d_out,), dtype=torch.int16, device=dev),
+            "sigma": torch.empty((d_in // 2,), dtype=torch.float32, device=dev),
+            "out": torch.empty((d_out, d_in), dtype=torch.bfloat16, device=dev),
+        })
+    ws = torch.empty((q.encode_workspace(d_out, d_in, bits),), dtype=torch.uint8, device=dev)
+    status = torch.zeros((1,), dtype=torch.int32, device=dev)
+
+    def enc(bset, sigma=None):
+        q.encode(bset["w"], cb, bits, index, scale=scale, sign_bits=sign, block=block, sigma=sigma, status=status,
+                 workspace=ws, out={"codes": bset["codes"], "norm": bset["norm"], "sigma": bset["sigma"]})
+
+    def dec(bset):
+        q.decode(bset["codes"], bset["norm"], bset["sigma"], cb, bits, d_in, scale=scale, sign_bits=sign,
+                 block=block, out=bset["out"])
+
+    def step(i):
+        bset = sets[i % n_sets]
+        enc(bset)
+        dec(bset)
+
+    # ---------------------------------------------------------------- warmup + timed steps
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = n_w * args.steps / elapsed / 1e6
+    assert int(status.item()) == 0, "data-fault flags raised: %d" % int(status.item())
+
+    # ---------------------------------------------------------------- per-kernel timing (HIP events)
+    def timed(fn, n):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(n):
+            fn(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n   # ms per call
+
+    n_k = max(args.steps, 50)
+    sigma_fixed = sets[0]["sigma"].clone()
+    enc_full_ms = timed(lambda i: enc(sets[i % n_sets]), n_k)
+    enc_kernel_ms = timed(lambda i: enc(sets[i % n_sets], sigma=sigma_fixed), n_k)  # k_encode alone
+    dec_ms = timed(lambda i: dec(sets[i % n_sets]), n_k)                          # k_decode alone
+
+    # algorithmic bytes per weight (B-bit pair index = B/16 bytes per weight, f16 norm per row)
+    code_b = bits / 16.0 + 2.0 / d_in
+    dec_bytes = n_w * (code_b + 2.0)
+    enc_bytes = n_w * (2.0 + code_b)
+    dec_gbps = dec_bytes / (dec_ms * 1e-3) / 1e9
+    # algorithmic lane operations per weight of the encoder: scale (1), square-accumulate (2),
+    # log2(b) butterflies, pair scaling (1), fp32 rounding (1), one fp32 distance evaluation per
+    # pair (6 per pair = 3), packing (1 per pair = 0.5)
+    L = int(round(math.log2(block)))
+    enc_ops_per_w = 1 + 2 + L + 1 + 1 + 3 + 0.5
+    enc_tops = n_w * enc_ops_per_w / (enc_kernel_ms * 1e-3) / 1e12
+
+    src_enc = ["weight_quantization_codec_amd/csrc/k_encode.hip", "weight_quantization_codec_amd/csrc/qamw_device.hpp"]
+    src_dec = ["weight_quantization_codec_amd/csrc/k_decode.hip", "weight_quantization_codec_amd/csrc/qamw_device.hpp"]
+    roof_enc = {"bound": "alu", "kernel": "k_encode", "achieved": round(enc_tops, 3), "peak": round(VALU_PEAK_TOPS, 2),
+                "unit": "Tops/s", "frac": round(enc_tops / VALU_PEAK_TOPS, 4),
+                "traffic": traffic_from_profile("k_encode", src_enc, enc_bytes),
+                "alg_ops_per_weight": enc_ops_per_w, "launch_ms": round(enc_kernel_ms, 5),
+                "hbm_GBps": round(enc_bytes / (enc_kernel_ms * 1e-3) / 1e9, 1)}
+    roof_dec = {"bound": "hbm", "kernel": "k_decode", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
+                "traffic": traffic_from_profile("k_decode", src_dec, dec_bytes),
+                "alg_bytes_per_launch": int(dec_bytes), "launch_ms": round(dec_ms, 5)}
+
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "Mweights/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f64", "data": "synthetic",
+        "config": {"workload": "attn-4096x4096 bf16 Student-t(5)x0.015, 41 outlier cols x10, b=128, K=2048 (B=11)",
+                   "d_out": d_out, "d_in": d_in, "block": block, "bits": bits, "rotated_sets": n_sets},
+        "encode_Mweights_per_s": round(n_w / (enc_full_ms * 1e-3) / 1e6, 1),
+        "decode_GB_per_s": round(dec_gbps, 1),
+        "decode_Mweights_per_s": round(n_w / (dec_ms * 1e-3) / 1e6, 1),
+        "encode_ms": round(enc_full_ms, 5), "decode_ms": round(dec_ms, 5),
+        "train_ms": round(train_ms, 3), "index_ms": round(index_ms, 4), "lloyd_final_mse": round(mse, 7),
+        "bpw": round(q.row_stride(d_in, bits) * 8 / d_in + 16.0 / d_in, 4),
+        "roofline": roof_enc, "roofline_decode": roof_dec,
+    }
+
+    # ---------------------------------------------------------------- CPU oracle baseline (whole workload)
+    if not args.no_cpu:
+        import oracle
+        orc = oracle.get()
+        cb_h = cb.cpu().numpy()
+        threads = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+        t0 = time.perf_counter()
+        sig, _ = orc.calibrate(w_host[:1024], s_host, sb_host, block)
+        e = orc.encode(w_host, s_host, sb_host, block, cb_h, bits, sig, want_idx=False)
+        orc.decode(e["codes"], e["norm"], d_in, sig, cb_h, bits, s_host, sb_host, block)
+        t_cpu = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": round(n_w / t_cpu / 1e6, 3), "unit": "Mweights/s", "cores": threads,
+                                  "kind": "oracle",
+                                  "sample": "whole 4096x4096 round trip (calibrate 1024 rows, encode, decode), "
+                                            "%.1f s" % t_cpu}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

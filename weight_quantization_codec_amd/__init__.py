@@ -192,8 +192,10 @@ def encode(w: torch.Tensor, codebook: torch.Tensor, bits: int, index: torch.Tens
     if norm is None:
         norm = torch.empty((d_out,), dtype=torch.int16, device=dev)
     sig_out = out.get("sigma")
-    if sig_out is None:
+    if sig_out is None and sigma is None:
         sig_out = torch.empty((d_in // 2,), dtype=torch.float32, device=dev)
+    if sigma is not None:
+        sig_out = None   # the given sigma is used as is; nothing is copied
     if scale is not None:
         _dev(scale, torch.float32, "scale")
     if sign_bits is not None:
@@ -208,7 +210,7 @@ def encode(w: torch.Tensor, codebook: torch.Tensor, bits: int, index: torch.Tens
                             _ptr(sig_out), _ptr(norm), _ptr(codes), _ptr(status), _ptr(ws),
                             0 if ws is None else ws.numel(), _stream())
     _check(rc, "qamw_encode")
-    return {"codes": codes, "norm": norm, "sigma": sig_out}
+    return {"codes": codes, "norm": norm, "sigma": sigma if sigma is not None else sig_out}
 
 
 def decode(codes: torch.Tensor, norm: torch.Tensor, sigma: torch.Tensor, codebook: torch.Tensor, bits: int,

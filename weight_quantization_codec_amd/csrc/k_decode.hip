@@ -32,19 +32,39 @@ __device__ __forceinline__ int dcol_B(int tid, int m) {
     }
 }
 
-// The NP fields of `bits` bits starting at stream bit `bitpos` of a row.  BITS > 0 makes the
-// field width a compile-time constant so that every shift is static.
+// Code words of one lane for one row: the NP fields of `bits` bits starting at stream bit
+// `bitpos`.  BITS > 0 makes the field width a compile-time constant so that every shift is static;
+// the dwords are loaded first (so that the next row can be prefetched) and unpacked later.
 template <int NP, int BITS>
-__device__ __forceinline__ void unpack_fields(__amdgpu_buffer_rsrc_t rs, uint32_t bitpos, int bits, int (&idx)[NP]) {
+struct CodeWords {
+    static constexpr int NA = BITS > 0 ? (NP * BITS + 31) / 32 : 1;
+    uint32_t dw[NA + 1];
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const uint8_t* codes, size_t stride, int row) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(codes + (size_t)row * stride), (short)0, (int)stride,
+                                             0x00020000);
+}
+
+template <int NP, int BITS>
+__device__ __forceinline__ void load_codes(__amdgpu_buffer_rsrc_t rs, uint32_t bitpos, CodeWords<NP, BITS>& c) {
     if constexpr (BITS > 0) {
-        constexpr int NA = (NP * BITS + 31) / 32;
-        uint32_t dw[NA + 1];
-        const uint32_t d0 = bitpos >> 5, s0 = bitpos & 31;
+        const uint32_t d0 = bitpos >> 5;
 #pragma unroll
-        for (int t = 0; t <= NA; ++t) dw[t] = __builtin_amdgcn_raw_buffer_load_b32(rs, (d0 + t) * 4, 0, 0);
+        for (int t = 0; t <= CodeWords<NP, BITS>::NA; ++t)
+            c.dw[t] = __builtin_amdgcn_raw_buffer_load_b32(rs, (d0 + t) * 4, 0, 0);
+    }
+}
+
+template <int NP, int BITS>
+__device__ __forceinline__ void unpack_codes(const CodeWords<NP, BITS>& c, __amdgpu_buffer_rsrc_t rs, uint32_t bitpos,
+                                             int bits, int (&idx)[NP]) {
+    if constexpr (BITS > 0) {
+        constexpr int NA = CodeWords<NP, BITS>::NA;
+        const uint32_t s0 = bitpos & 31;
         uint32_t al[NA];
 #pragma unroll
-        for (int t = 0; t < NA; ++t) al[t] = __builtin_amdgcn_alignbit(dw[t + 1], dw[t], s0);
+        for (int t = 0; t < NA; ++t) al[t] = __builtin_amdgcn_alignbit(c.dw[t + 1], c.dw[t], s0);
         constexpr uint32_t mask = (1u << BITS) - 1u;
 #pragma unroll
         for (int i = 0; i < NP; ++i) {
@@ -76,29 +96,48 @@ __global__ __launch_bounds__(MAXT) void k_decode(DecodeArgs a) {
     double2* tab = reinterpret_cast<double2*>(smem);
     double* xb = reinterpret_cast<double*>(smem + (size_t)K * sizeof(double2)) + (tid / kWave) * Lo::xbuf;
 
+    const int units = a.d_in / E;
+    const bool active = tid < units;
+    const uint32_t bitpos = (uint32_t)(tid * NP) * (uint32_t)bits;
+
+    // first row's codes in flight while the tables are set up
+    int row = blockIdx.x;
+    CodeWords<NP, BITS> nxt;
+    uint16_t nh_next = 0;
+    if (row < a.d_out) {
+        nh_next = a.norm[row];
+        if (active) load_codes<NP, BITS>(row_rsrc(a.codes, a.stride, row), bitpos, nxt);
+    }
+
     for (int j = tid; j < K; j += blockDim.x) {
         float2 c = reinterpret_cast<const float2*>(a.cb)[j];
         tab[j] = make_double2((double)c.x + (double)c.y, (double)c.x - (double)c.y);   // exact in double
     }
-
-    const int units = a.d_in / E;
-    const bool active = tid < units;
     double sg[NP];
 #pragma unroll
-    for (int i = 0; i < NP; ++i) sg[i] = (double)a.sigma[min(tid * NP + i, a.d_in / 2 - 1)];
+    for (int i = 0; i < NP; ++i) {
+        sg[i] = (double)a.sigma[min(tid * NP + i, a.d_in / 2 - 1)];
+        pin_reg(sg[i]);
+    }
     double cf[E];
 #pragma unroll
     for (int m = 0; m < E; ++m) {
         int j = min(dcol_B<L>(tid, m), a.d_in - 1);
         double e = (a.sign && ((a.sign[j >> 5] >> (j & 31)) & 1u)) ? -1.0 : 1.0;
         cf[m] = e * (1.0 / (a.scale ? (double)a.scale[j] : 1.0));
+        pin_reg(cf[m]);
     }
     const double inv_sqrt_b = 1.0 / __builtin_sqrt((double)Lo::b);
-    const uint32_t bitpos = (uint32_t)(tid * NP) * (uint32_t)bits;
     __syncthreads();
 
-    for (int row = blockIdx.x; row < a.d_out; row += gridDim.x) {
-        const uint16_t nh = a.norm[row];
+    for (; row < a.d_out; row += gridDim.x) {
+        const uint16_t nh = nh_next;
+        const CodeWords<NP, BITS> cur = nxt;
+        const int rnext = row + (int)gridDim.x;
+        if (rnext < a.d_out) {   // prefetch the next row
+            nh_next = a.norm[rnext];
+            if (active) load_codes<NP, BITS>(row_rsrc(a.codes, a.stride, rnext), bitpos, nxt);
+        }
         const float rn = __half2float(__ushort_as_half(nh));
         char* orow = reinterpret_cast<char*>(a.out) + (size_t)row * a.ld * (a.out_bf16 ? 2 : 4);
         if (rn == 0.0f) {
@@ -116,11 +155,8 @@ __global__ __launch_bounds__(MAXT) void k_decode(DecodeArgs a) {
         }
         double x[E];
         if (active) {
-            __amdgpu_buffer_rsrc_t rs =
-                __builtin_amdgcn_make_buffer_rsrc((void*)(a.codes + (size_t)row * a.stride), (short)0,
-                                                  (int)a.stride, 0x00020000);
             int idx[NP];
-            unpack_fields<NP, BITS>(rs, bitpos, bits, idx);
+            unpack_codes<NP, BITS>(cur, row_rsrc(a.codes, a.stride, row), bitpos, bits, idx);
             const double g = (double)rn * inv_sqrt_b;
 #pragma unroll
             for (int i = 0; i < NP; ++i) {

@@ -21,7 +21,7 @@ namespace qamw {
 namespace {
 
 constexpr int kMaxWaves = 16;
-constexpr int kCalibMaxGroups = 128;
+constexpr int kCalibMaxGroups = 256;
 
 __device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll
@@ -44,64 +44,77 @@ __device__ __forceinline__ int col_B(int tid, int m) {
     }
 }
 
-// Load E consecutive weights of one row starting at column col0 and multiply by cf (= s_j eps_j).
-template <int E>
-__device__ __forceinline__ void load_scaled(const void* w, int bf16, bool vec, int64_t off, const double (&cf)[E],
-                                            double (&x)[E], double& ss, int32_t& flags) {
-    float f[E];
-    if (bf16) {
+// Raw bits of the E consecutive weights a lane reads from one row (bf16: two per dword).
+template <int E, bool BF>
+struct RawW {
+    static constexpr int N = BF ? E / 2 : E;
+    uint32_t u[N];
+};
+
+template <int E, bool BF>
+__device__ __forceinline__ void load_raw(const void* w, bool vec, int64_t off, RawW<E, BF>& r) {
+    if constexpr (BF) {
         const uint16_t* p = reinterpret_cast<const uint16_t*>(w) + off;
         if (vec) {
 #pragma unroll
             for (int v = 0; v < E / 8; ++v) {
-                uint4 u = reinterpret_cast<const uint4*>(p)[v];
-                uint32_t uu[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    f[8 * v + 2 * t] = __uint_as_float(uu[t] << 16);
-                    f[8 * v + 2 * t + 1] = __uint_as_float(uu[t] & 0xFFFF0000u);
-                }
+                uint4 q = reinterpret_cast<const uint4*>(p)[v];
+                r.u[4 * v] = q.x;
+                r.u[4 * v + 1] = q.y;
+                r.u[4 * v + 2] = q.z;
+                r.u[4 * v + 3] = q.w;
             }
         } else {
 #pragma unroll
-            for (int m = 0; m < E; ++m) f[m] = bf16_bits_to_float(p[m]);
+            for (int m = 0; m < E / 2; ++m) r.u[m] = (uint32_t)p[2 * m] | ((uint32_t)p[2 * m + 1] << 16);
         }
     } else {
-        const float* p = reinterpret_cast<const float*>(w) + off;
+        const uint32_t* p = reinterpret_cast<const uint32_t*>(w) + off;
         if (vec) {
 #pragma unroll
             for (int v = 0; v < E / 4; ++v) {
-                float4 u = reinterpret_cast<const float4*>(p)[v];
-                f[4 * v] = u.x;
-                f[4 * v + 1] = u.y;
-                f[4 * v + 2] = u.z;
-                f[4 * v + 3] = u.w;
+                uint4 q = reinterpret_cast<const uint4*>(p)[v];
+                r.u[4 * v] = q.x;
+                r.u[4 * v + 1] = q.y;
+                r.u[4 * v + 2] = q.z;
+                r.u[4 * v + 3] = q.w;
             }
         } else {
 #pragma unroll
-            for (int m = 0; m < E; ++m) f[m] = p[m];
+            for (int m = 0; m < E; ++m) r.u[m] = p[m];
         }
     }
+}
+
+// a_j = w_j * s_j * eps_j in double (exact), accumulating sum a_j^2.
+template <int E, bool BF>
+__device__ __forceinline__ void scale_raw(const RawW<E, BF>& r, const double (&cf)[E], double (&x)[E], double& ss,
+                                          int32_t& flags) {
 #pragma unroll
     for (int m = 0; m < E; ++m) {
-        double a = (double)f[m] * cf[m];
+        float f;
+        if constexpr (BF)
+            f = __uint_as_float((m & 1) ? (r.u[m >> 1] & 0xFFFF0000u) : (r.u[m >> 1] << 16));
+        else
+            f = __uint_as_float(r.u[m]);
+        double a = (double)f * cf[m];
         if (!__builtin_isfinite(a)) flags |= 1;
         x[m] = a;
         ss += a * a;
     }
 }
 
-// Front end for one row: x <- unnormalized transform (phase B layout), returns sum a^2 of the
-// whole row (deterministic: fixed shuffle tree, then waves in order).
-template <int L>
-__device__ __forceinline__ double front_end(const void* w, int bf16, bool vec, int64_t row_off, bool active, int tid,
+// Front end for one row given its raw weights: x <- unnormalized transform (phase B layout);
+// returns sum a^2 over the whole row (fixed shuffle tree, then wavefronts in order).
+template <int L, bool BF>
+__device__ __forceinline__ double front_end(const RawW<Layout<L>::E, BF>& raw, bool active, int tid,
                                             const double (&cf)[Layout<L>::E], double (&x)[Layout<L>::E],
                                             double* red, double* xb, int nwaves, int32_t& flags) {
     using Lo = Layout<L>;
     constexpr int E = Lo::E;
     double ss = 0.0;
     if (active) {
-        load_scaled<E>(w, bf16, vec, row_off + (int64_t)tid * E, cf, x, ss, flags);
+        scale_raw<E, BF>(raw, cf, x, ss, flags);
     } else {
 #pragma unroll
         for (int m = 0; m < E; ++m) x[m] = 0.0;
@@ -125,7 +138,7 @@ __device__ __forceinline__ double front_end(const void* w, int bf16, bool vec, i
     return r2;
 }
 
-template <int L, int MAXT>
+template <int L, int MAXT, bool BF>
 __global__ __launch_bounds__(MAXT) void k_calibrate(CalibArgs a) {
     using Lo = Layout<L>;
     constexpr int E = Lo::E, NP = E / 2;
@@ -135,7 +148,7 @@ __global__ __launch_bounds__(MAXT) void k_calibrate(CalibArgs a) {
     const int tid = threadIdx.x, nwaves = blockDim.x / kWave;
     const int units = a.d_in / E;
     const bool active = tid < units;
-    const bool vec = (((uintptr_t)a.w & 15) == 0) && (((a.ld * (a.w_bf16 ? 2 : 4)) & 15) == 0);
+    const bool vec = (((uintptr_t)a.w & 15) == 0) && (((a.ld * (BF ? 2 : 4)) & 15) == 0);
     double cf[E];
 #pragma unroll
     for (int m = 0; m < E; ++m) {
@@ -148,10 +161,15 @@ __global__ __launch_bounds__(MAXT) void k_calibrate(CalibArgs a) {
     for (int i = 0; i < NP; ++i) acc[i] = 0.0;
     int nz = 0;
     int32_t flags = 0;
-    for (int row = blockIdx.x; row < a.n_rows; row += gridDim.x) {
+    RawW<E, BF> nxt;
+    int row = blockIdx.x;
+    if (active && row < a.n_rows) load_raw<E, BF>(a.w, vec, (int64_t)row * a.ld + (int64_t)tid * E, nxt);
+    for (; row < a.n_rows; row += gridDim.x) {
+        const RawW<E, BF> cur = nxt;
+        if (active && row + (int)gridDim.x < a.n_rows)
+            load_raw<E, BF>(a.w, vec, (int64_t)(row + gridDim.x) * a.ld + (int64_t)tid * E, nxt);
         double x[E];
-        double r2 = front_end<L>(a.w, a.w_bf16, vec, (int64_t)row * a.ld, active, tid, cf, x, red, xb, nwaves,
-                                 flags);
+        double r2 = front_end<L, BF>(cur, active, tid, cf, x, red, xb, nwaves, flags);
         double r = __builtin_sqrt(r2);
         if (r > 0.0 && __builtin_isfinite(r)) {
             ++nz;
@@ -172,43 +190,58 @@ __global__ __launch_bounds__(MAXT) void k_calibrate(CalibArgs a) {
     if (tid == 0) a.nz[blockIdx.x] = nz;
 }
 
+// sigma_k from the per-group sums: each pair's groups are split over 4 threads, every thread adds
+// its groups in increasing order, and the 4 partial sums are added in a fixed order.
 __global__ __launch_bounds__(256) void k_calibrate_finish(const double* __restrict__ partial,
                                                           const int32_t* __restrict__ nzs, int n_groups, int n_pairs,
                                                           int d_in, float* __restrict__ sigma) {
-    int k = blockIdx.x * blockDim.x + threadIdx.x;
-    if (k >= n_pairs) return;
-    int64_t n = 0;
+    __shared__ double part[4][64];
+    const int kl = threadIdx.x & 63, quarter = threadIdx.x >> 6;
+    const int k = blockIdx.x * 64 + kl;
     double s = 0.0;
-    for (int g = 0; g < n_groups; ++g) {
-        n += nzs[g];
-        s += partial[(size_t)g * n_pairs + k];
+    if (k < n_pairs) {
+        const int per = (n_groups + 3) / 4;
+        const int g0 = quarter * per, g1 = min(n_groups, g0 + per);
+        int g = g0;
+        for (; g + 8 <= g1; g += 8) {
+            double v[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) v[t] = partial[(size_t)(g + t) * n_pairs + k];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) s += v[t];
+        }
+        for (; g < g1; ++g) s += partial[(size_t)g * n_pairs + k];
     }
-    double m = (n > 0) ? s / (double)n : 0.0;
+    part[quarter][kl] = s;
+    __syncthreads();
+    if (quarter != 0 || k >= n_pairs) return;
+    int64_t n = 0;
+    for (int g = 0; g < n_groups; ++g) n += nzs[g];
+    double tot = ((part[0][kl] + part[1][kl]) + part[2][kl]) + part[3][kl];
+    double m = (n > 0) ? tot / (double)n : 0.0;
     const double rayleigh_mean = __builtin_sqrt(3.14159265358979323846 / 2.0);   // E|z| = sigma sqrt(pi/2)
     sigma[k] = (m > 0.0) ? (float)(m / rayleigh_mean) : (float)(1.0 / __builtin_sqrt((double)d_in));
 }
 
-template <int L, int MAXT>
+template <int L, int MAXT, bool BF>
 __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a) {
     using Lo = Layout<L>;
     constexpr int E = Lo::E, NP = E / 2;
     extern __shared__ __align__(16) char smem[];
     const int K = 1 << a.bits;
     const int tid = threadIdx.x, nwaves = blockDim.x / kWave;
-    float2* scb = reinterpret_cast<float2*>(smem);
-    double* red = reinterpret_cast<double*>(smem + (size_t)K * sizeof(float2));
+    const char* index = reinterpret_cast<const char*>(a.index);
+    const IndexHeader ih = *reinterpret_cast<const IndexHeader*>(index);
+    const SearchLds sl = search_lds_carve(smem, K, ih);
+    double* red = reinterpret_cast<double*>(smem + search_lds_bytes(K, ih.G));
     double* xb_all = red + kMaxWaves;
     double* xb = xb_all + (tid / kWave) * Lo::xbuf;
     uint16_t* idxrow = reinterpret_cast<uint16_t*>(xb_all + (Lo::two_phase ? nwaves * Lo::xbuf : 0));
-
-    for (int j = tid; j < K; j += blockDim.x) scb[j] = reinterpret_cast<const float2*>(a.cb)[j];
-    const IndexHeader ih = *reinterpret_cast<const IndexHeader*>(a.index);
-    const uint16_t* slots =
-        reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(a.index) + kIndexHeaderBytes);
+    search_lds_fill(sl, a.cb, K, index, tid, blockDim.x);
 
     const int units = a.d_in / E, n_pairs = a.d_in / 2;
     const bool active = tid < units;
-    const bool vec = (((uintptr_t)a.w & 15) == 0) && (((a.ld * (a.w_bf16 ? 2 : 4)) & 15) == 0);
+    const bool vec = (((uintptr_t)a.w & 15) == 0) && (((a.ld * (BF ? 2 : 4)) & 15) == 0);
     int32_t flags = 0;
     double cf[E];
 #pragma unroll
@@ -217,40 +250,51 @@ __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a) {
         float s = a.scale ? a.scale[j] : 1.0f;
         if (active && !(s > 0.0f)) flags |= 2;
         cf[m] = (double)s * eps_of(a.sign, j);
+        pin_reg(cf[m]);
     }
     double isg[NP];
-    int kpair[NP];
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
-        kpair[i] = min(col_B<L>(tid, 2 * i) / 2, n_pairs - 1);
-        isg[i] = 1.0 / (double)a.sigma[kpair[i]];
+        isg[i] = 1.0 / (double)a.sigma[min(col_B<L>(tid, 2 * i) / 2, n_pairs - 1)];
+        pin_reg(isg[i]);
     }
     if (blockIdx.x != 0) flags &= ~2;   // report a bad scale once
     const double inv_sqrt_b = 1.0 / __builtin_sqrt((double)Lo::b);
     const int bits = a.bits;
     const int nwords = (int)(a.stride / 4);
+
+    RawW<E, BF> nxt;
+    int row = blockIdx.x;
+    if (active && row < a.d_out) load_raw<E, BF>(a.w, vec, (int64_t)row * a.ld + (int64_t)tid * E, nxt);
     __syncthreads();
 
-    for (int row = blockIdx.x; row < a.d_out; row += gridDim.x) {
+    for (; row < a.d_out; row += gridDim.x) {
+        const RawW<E, BF> cur = nxt;
+        if (active && row + (int)gridDim.x < a.d_out)   // prefetch the next row while this one is encoded
+            load_raw<E, BF>(a.w, vec, (int64_t)(row + gridDim.x) * a.ld + (int64_t)tid * E, nxt);
         double x[E];
         int32_t rf = 0;
-        double r2 = front_end<L>(a.w, a.w_bf16, vec, (int64_t)row * a.ld, active, tid, cf, x, red, xb, nwaves, rf);
+        double r2 = front_end<L, BF>(cur, active, tid, cf, x, red, xb, nwaves, rf);
         double r = __builtin_sqrt(r2);
         bool nonzero = r > 0.0 && __builtin_isfinite(r);
         if (!__builtin_isfinite(r)) rf |= 1;
         if (active) {
             if (nonzero) {
-                double hr = inv_sqrt_b / r;
+                const double hr = inv_sqrt_b / r;
+                float px[NP], py[NP];
 #pragma unroll
                 for (int i = 0; i < NP; ++i) {
                     double g = isg[i] * hr;
-                    float px = (float)(x[2 * i] * g);
-                    float py = (float)(x[2 * i + 1] * g);
-                    idxrow[kpair[i]] = (uint16_t)nearest_indexed(px, py, scb, K, ih, slots);
+                    px[i] = (float)(x[2 * i] * g);
+                    py[i] = (float)(x[2 * i + 1] * g);
                 }
+                int idx[NP];
+                nearest_lds_batch<NP>(px, py, sl, index, idx);
+#pragma unroll
+                for (int i = 0; i < NP; ++i) idxrow[col_B<L>(tid, 2 * i) / 2] = (uint16_t)idx[i];
             } else {
 #pragma unroll
-                for (int i = 0; i < NP; ++i) idxrow[kpair[i]] = 0;
+                for (int i = 0; i < NP; ++i) idxrow[col_B<L>(tid, 2 * i) / 2] = 0;
             }
         }
         if (tid == 0) {
@@ -284,7 +328,9 @@ __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a) {
 template <int L>
 size_t encode_smem(int K, int nwaves, int d_in) {
     using Lo = Layout<L>;
-    return (size_t)K * sizeof(float2) + kMaxWaves * sizeof(double) +
+    int bits = 0;
+    while ((1 << bits) < K) ++bits;
+    return search_lds_bytes(K, index_grid_size(bits)) + kMaxWaves * sizeof(double) +
            (Lo::two_phase ? (size_t)nwaves * Lo::xbuf * sizeof(double) : 0) + (size_t)(d_in / 2) * sizeof(uint16_t);
 }
 
@@ -294,8 +340,8 @@ size_t calib_smem(int nwaves) {
     return kMaxWaves * sizeof(double) + (Lo::two_phase ? (size_t)nwaves * Lo::xbuf * sizeof(double) : 0);
 }
 
-template <int L>
-hipError_t encode_L(const EncodeArgs& a, hipStream_t st) {
+template <int L, bool BF>
+hipError_t encode_LB(const EncodeArgs& a, hipStream_t st) {
     using Lo = Layout<L>;
     int threads = ((a.d_in / Lo::E) + kWave - 1) / kWave * kWave;
     int nwaves = threads / kWave;
@@ -308,38 +354,49 @@ hipError_t encode_L(const EncodeArgs& a, hipStream_t st) {
     if (grid > a.d_out) grid = a.d_out;
     if (grid < 1) return hipSuccess;
     if (threads <= 512) {
-        allow_lds(k_encode<L, 512>, smem);
-        hipLaunchKernelGGL((k_encode<L, 512>), dim3(grid), dim3(threads), smem, st, a);
+        allow_lds(k_encode<L, 512, BF>, smem);
+        hipLaunchKernelGGL((k_encode<L, 512, BF>), dim3(grid), dim3(threads), smem, st, a);
     } else if constexpr (L <= 7) {
-        allow_lds(k_encode<L, 1024>, smem);
-        hipLaunchKernelGGL((k_encode<L, 1024>), dim3(grid), dim3(threads), smem, st, a);
+        allow_lds(k_encode<L, 1024, BF>, smem);
+        hipLaunchKernelGGL((k_encode<L, 1024, BF>), dim3(grid), dim3(threads), smem, st, a);
     } else {
         return hipErrorInvalidConfiguration;
     }
     return hipGetLastError();
 }
 
-template <int L>
-hipError_t calibrate_L(const CalibArgs& a, float* sigma, hipStream_t st) {
+template <int L, bool BF>
+hipError_t calibrate_LB(const CalibArgs& a, float* sigma, hipStream_t st) {
     using Lo = Layout<L>;
     int threads = ((a.d_in / Lo::E) + kWave - 1) / kWave * kWave;
     int nwaves = threads / kWave;
     if (a.n_groups > 0) {
         if (threads <= 512) {
-            allow_lds(k_calibrate<L, 512>, calib_smem<L>(nwaves));
-            hipLaunchKernelGGL((k_calibrate<L, 512>), dim3(a.n_groups), dim3(threads), calib_smem<L>(nwaves), st, a);
+            allow_lds(k_calibrate<L, 512, BF>, calib_smem<L>(nwaves));
+            hipLaunchKernelGGL((k_calibrate<L, 512, BF>), dim3(a.n_groups), dim3(threads), calib_smem<L>(nwaves), st,
+                               a);
         } else if constexpr (L <= 7) {
-            allow_lds(k_calibrate<L, 1024>, calib_smem<L>(nwaves));
-            hipLaunchKernelGGL((k_calibrate<L, 1024>), dim3(a.n_groups), dim3(threads), calib_smem<L>(nwaves), st,
+            allow_lds(k_calibrate<L, 1024, BF>, calib_smem<L>(nwaves));
+            hipLaunchKernelGGL((k_calibrate<L, 1024, BF>), dim3(a.n_groups), dim3(threads), calib_smem<L>(nwaves), st,
                                a);
         } else {
             return hipErrorInvalidConfiguration;
         }
     }
     int n_pairs = a.d_in / 2;
-    hipLaunchKernelGGL(k_calibrate_finish, dim3((n_pairs + 255) / 256), dim3(256), 0, st, a.partial, a.nz,
+    hipLaunchKernelGGL(k_calibrate_finish, dim3((n_pairs + 63) / 64), dim3(256), 0, st, a.partial, a.nz,
                        a.n_groups, n_pairs, a.d_in, sigma);
     return hipGetLastError();
+}
+
+template <int L>
+hipError_t encode_L(const EncodeArgs& a, hipStream_t st) {
+    return a.w_bf16 ? encode_LB<L, true>(a, st) : encode_LB<L, false>(a, st);
+}
+
+template <int L>
+hipError_t calibrate_L(const CalibArgs& a, float* sigma, hipStream_t st) {
+    return a.w_bf16 ? calibrate_LB<L, true>(a, sigma, st) : calibrate_LB<L, false>(a, sigma, st);
 }
 
 }  // namespace
@@ -358,6 +415,15 @@ int lane_elems(int L) {
     case 10: return Layout<10>::E;
     default: return 0;
     }
+}
+
+size_t encode_lds_bytes(int L, int bits, int d_in) {
+    const int E = lane_elems(L);
+    if (E <= 0) return 0;
+    const int nwaves = ((d_in / E) + kWave - 1) / kWave;
+    const size_t xb = (L > 4) ? (size_t)nwaves * (kWave * (E / 2) + kWave) * sizeof(double) : 0;
+    return search_lds_bytes(1 << bits, index_grid_size(bits)) + kMaxWaves * sizeof(double) + xb +
+           (size_t)(d_in / 2) * sizeof(uint16_t);
 }
 
 int calib_groups(int n_rows) { return n_rows < kCalibMaxGroups ? n_rows : kCalibMaxGroups; }

@@ -1,129 +1,326 @@
 // Search index for the nearest-codeword step (paper section 3.6: each normalized pair maps to
-// its Euclidean-nearest codebook entry).
+// its Euclidean-nearest codebook entry), built on the GPU once per codebook.
 //
-// A uniform G x G grid covers [-R, R]^2, R = 1.3 * max_j max(|c_jx|, |c_jy|).  For a cell Q
-// (widened by 1e-3 of a cell on each side to absorb the fp32 rounding of the cell lookup),
-//   U_Q = min_j maxdist^2(Q, c_j)            (every point of Q has a codeword within sqrt(U_Q)),
-//   cand(Q) = { j : mindist^2(Q, c_j) <= U_Q * (1 + 1e-5) }   in increasing j,
-// computed in double.  A codeword outside cand(Q) is farther than the nearest one by more than
-// the relative error of the fp32 distance (about 2.4e-7), so the fp32 argmin over cand(Q), with
-// ties to the lowest index, equals the argmin over all K codewords.  Cells with more than
-// kIndexCap-1 candidates are marked as overflow and searched exhaustively.
+// Grid.  A G x G grid over [-Rg, Rg]^2, Rg = 1.5 max_j max(|c_jx|, |c_jy|), whose cell edges sit
+// at quantiles of the codeword coordinates (both axes share one set of edges): a point is
+// located by a uniform fine bin (W bins over [-Rg, Rg]) and a table fine bin -> cell, so that
+// every cell holds about one codeword wherever the codebook is dense or sparse.
+//
+// Candidates.  Codeword j is listed for cell Q when its Voronoi region, widened to absorb fp32
+// distance rounding, meets Q widened by 1e-3 of a fine bin (the lookup's own rounding):
+//   1. prefilter: mindist^2(Q, c_j) <= U_Q (1 + 1e-5), U_Q = min_k maxdist^2(Q, c_k);
+//   2. clip Q by the half-planes |p - c_j|^2 - |p - c_k|^2 <= 1e-6 (maxdist^2(Q, c_j) +
+//      maxdist^2(Q, c_k)) for every other prefiltered k (double precision); j stays if the
+//      polygon is not empty.
+// The fp32 distance fl(fl(dx*dx) + fl(dy*dy)) is within 2.4e-7 relative of the exact one, so a
+// codeword outside the list can neither beat nor tie the listed ones in fp32: the fp32 argmin
+// over the list, ties to the lowest index (lists are in increasing index order), equals the
+// argmin over all K codewords.  Points outside the grid use a scan in decreasing |c| that stops
+// once |p| - |c| exceeds the distance to a known codeword (plus a 1e-5 margin).
+#include <cmath>
+
 #include "qamw_device.hpp"
 #include "qamw_launch.hpp"
 
 namespace qamw {
 
-__global__ __launch_bounds__(256) void k_index_header(const float* __restrict__ cb, int K, int G, int bits,
-                                                      IndexHeader* hdr) {
-    __shared__ float red[256];
+namespace {
+
+constexpr int kPolyMax = 48;
+
+// Convex polygon clipped by a.x*px + a.y*py <= b (Sutherland-Hodgman, double precision).
+__device__ int clip_poly(double* vx, double* vy, int n, double ax, double ay, double b, double* tx, double* ty) {
+    int m = 0;
+    const double tol = 1e-12 * (fabs(b) + 1.0);
+    for (int i = 0; i < n; ++i) {
+        const int i2 = (i + 1 == n) ? 0 : i + 1;
+        const double s1 = ax * vx[i] + ay * vy[i] - b;
+        const double s2 = ax * vx[i2] + ay * vy[i2] - b;
+        const bool in1 = s1 <= tol, in2 = s2 <= tol;
+        if (in1 && m < kPolyMax) {
+            tx[m] = vx[i];
+            ty[m] = vy[i];
+            ++m;
+        }
+        if (in1 != in2 && m < kPolyMax) {
+            const double t = s1 / (s1 - s2);
+            tx[m] = vx[i] + t * (vx[i2] - vx[i]);
+            ty[m] = vy[i] + t * (vy[i2] - vy[i]);
+            ++m;
+        }
+    }
+    for (int i = 0; i < m; ++i) {
+        vx[i] = tx[i];
+        vy[i] = ty[i];
+    }
+    return m;
+}
+
+struct CellBox {
+    double x0, x1, y0, y1;
+};
+
+__device__ CellBox cell_box(const IndexHeader& ih, const uint16_t* __restrict__ lo, int cell) {
+    const int cx = cell % ih.G, cy = cell / ih.G;
+    const double w = 1.0 / (double)ih.inv_w;   // the lookup bins by fp32 (p + R) * inv_w
+    const double d = 1e-3 * w;
+    CellBox q;
+    q.x0 = -(double)ih.R + lo[cx] * w - d;
+    q.x1 = -(double)ih.R + lo[cx + 1] * w + d;
+    q.y0 = -(double)ih.R + lo[cy] * w - d;
+    q.y1 = -(double)ih.R + lo[cy + 1] * w + d;
+    return q;
+}
+
+__device__ __forceinline__ double maxd2(const CellBox& q, double px, double py) {
+    double ax = fmax(fabs(px - q.x0), fabs(px - q.x1));
+    double ay = fmax(fabs(py - q.y0), fabs(py - q.y1));
+    return ax * ax + ay * ay;
+}
+
+__device__ __forceinline__ double mind2(const CellBox& q, double px, double py) {
+    double dx = fmax(fmax(q.x0 - px, px - q.x1), 0.0);
+    double dy = fmax(fmax(q.y0 - py, py - q.y1), 0.0);
+    return dx * dx + dy * dy;
+}
+
+// Is codeword j a candidate of the (non-empty) cell box q?  pre[] holds the prefiltered set.
+__device__ bool voronoi_meets(const CellBox& q, const float2* __restrict__ cb, int j, const uint16_t* pre, int npre) {
+    double vx[kPolyMax], vy[kPolyMax], tx[kPolyMax], ty[kPolyMax];
+    vx[0] = q.x0; vy[0] = q.y0;
+    vx[1] = q.x1; vy[1] = q.y0;
+    vx[2] = q.x1; vy[2] = q.y1;
+    vx[3] = q.x0; vy[3] = q.y1;
+    int n = 4;
+    const double cjx = cb[j].x, cjy = cb[j].y;
+    const double mj = maxd2(q, cjx, cjy);
+    const double nj = cjx * cjx + cjy * cjy;
+    for (int t = 0; t < npre && n > 0; ++t) {
+        const int k = pre[t];
+        if (k == j) continue;
+        const double ckx = cb[k].x, cky = cb[k].y;
+        const double m = 1e-6 * (mj + maxd2(q, ckx, cky));
+        // |p-cj|^2 - |p-ck|^2 <= m   <=>   2 (ck - cj).p <= |ck|^2 - |cj|^2 + m
+        n = clip_poly(vx, vy, n, 2.0 * (ckx - cjx), 2.0 * (cky - cjy), (ckx * ckx + cky * cky) - nj + m, tx, ty);
+    }
+    return n > 0;
+}
+
+// ---------------------------------------------------------------------------------------------
+// 1. Header, fine-bin table and cell edges (one workgroup).
+__global__ __launch_bounds__(1024) void k_ix_grid(const float* __restrict__ cb, int K, int G, int W, int bits,
+                                                  char* __restrict__ index) {
+    __shared__ float red[1024];
+    __shared__ int hist[kIndexFineMax];
+    IndexHeader* hdr = reinterpret_cast<IndexHeader*>(index);
+    uint8_t* fine = reinterpret_cast<uint8_t*>(index + kIndexFineOff);
+    uint16_t* lo = reinterpret_cast<uint16_t*>(index + kIndexEdgeOff);
+    const int tid = threadIdx.x;
     float m = 0.f;
-    for (int j = threadIdx.x; j < K; j += blockDim.x) {
+    for (int j = tid; j < K; j += blockDim.x) {
         float2 c = reinterpret_cast<const float2*>(cb)[j];
         m = fmaxf(m, fmaxf(fabsf(c.x), fabsf(c.y)));   // NaN codewords are ignored by fmaxf
     }
-    red[threadIdx.x] = m;
+    red[tid] = m;
+    for (int b = tid; b < W; b += blockDim.x) hist[b] = 0;
     __syncthreads();
-    for (int s = 128; s > 0; s >>= 1) {
-        if (threadIdx.x < s) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + s]);
+    for (int s = 512; s > 0; s >>= 1) {
+        if (tid < s) red[tid] = fmaxf(red[tid], red[tid + s]);
         __syncthreads();
     }
-    if (threadIdx.x == 0) {
-        float R = 1.3f * red[0];
-        if (!(R >= 1e-3f) || !(R < 1e30f)) R = 1.0f;
+    float R = 1.5f * red[0];
+    if (!(R >= 1e-3f) || !(R < 1e30f)) R = 1.0f;
+    const float inv_w = (float)W / (2.0f * R);
+    for (int j = tid; j < 2 * K; j += blockDim.x) {
+        float v = cb[j];
+        int b = (int)((v + R) * inv_w);
+        b = b < 0 ? 0 : (b >= W ? W - 1 : b);
+        if (v == v) atomicAdd(&hist[b], 1);
+    }
+    __syncthreads();
+    if (tid == 0) {
+        // fine bin b -> cell min(G-1, C(b) * G / (2K)), C(b) = coordinates in bins before b
+        int c = 0, prev = -1;
+        for (int b = 0; b < W; ++b) {
+            int cell = (int)(((int64_t)c * G) / (2 * K));
+            if (cell > G - 1) cell = G - 1;
+            fine[b] = (uint8_t)cell;
+            for (int e = prev + 1; e <= cell; ++e) lo[e] = (uint16_t)b;   // first fine bin of each cell
+            prev = cell;
+            c += hist[b];
+        }
+        for (int e = prev + 1; e <= G; ++e) lo[e] = (uint16_t)W;
         hdr->K = K;
         hdr->G = G;
-        hdr->cap = kIndexCap;
+        hdr->W = W;
         hdr->bits = bits;
         hdr->R = R;
-        hdr->inv_h = (float)G / (2.0f * R);
-        hdr->ready = 1;
-        hdr->max_count = 0;
+        hdr->inv_w = inv_w;
+        hdr->n_entries = 0;
+        hdr->overflow = 0;
     }
 }
 
-__global__ __launch_bounds__(256) void k_index_cells(const float* __restrict__ cb, int K, IndexHeader* hdr,
-                                                     uint16_t* __restrict__ slots) {
-    extern __shared__ float2 scb[];
-    for (int j = threadIdx.x; j < K; j += blockDim.x) scb[j] = reinterpret_cast<const float2*>(cb)[j];
-    __syncthreads();
-    const int G = hdr->G;
-    const int cell = blockIdx.x * blockDim.x + threadIdx.x;
-    if (cell >= G * G) return;
-    const int cx = cell % G, cy = cell / G;
-    const double R = (double)hdr->R;
-    const double h = 1.0 / (double)hdr->inv_h;
-    const double d = 1e-3 * h;
-    const double x0 = cx * h - R - d, x1 = (cx + 1) * h - R + d;
-    const double y0 = cy * h - R - d, y1 = (cy + 1) * h - R + d;
-    double U = 1e300;
-    for (int j = 0; j < K; ++j) {
-        double px = scb[j].x, py = scb[j].y;
-        double ax = fmax(fabs(px - x0), fabs(px - x1));
-        double ay = fmax(fabs(py - y0), fabs(py - y1));
-        U = fmin(U, ax * ax + ay * ay);
+// 2./4. Candidate lists: one workgroup per cell.  pass 0 counts, pass 1 writes the list in
+// increasing codeword order at the cell's offset.
+__global__ __launch_bounds__(256) void k_ix_cells(const float* __restrict__ cb, int K, char* __restrict__ index,
+                                                  int pass) {
+    extern __shared__ __align__(16) char smem[];
+    float2* scb = reinterpret_cast<float2*>(smem);
+    uint16_t* pre = reinterpret_cast<uint16_t*>(smem + (size_t)K * sizeof(float2));
+    __shared__ double redU[256];
+    __shared__ int npre, wbase;
+    __shared__ int scan[256];
+    const IndexHeader ih = *reinterpret_cast<const IndexHeader*>(index);
+    const uint16_t* lo = reinterpret_cast<const uint16_t*>(index + kIndexEdgeOff);
+    uint32_t* offs = reinterpret_cast<uint32_t*>(index + kIndexOffsOff);
+    uint16_t* ent = reinterpret_cast<uint16_t*>(index + kIndexEntOff);
+    const int cell = blockIdx.x, tid = threadIdx.x;
+    if (pass && reinterpret_cast<const uint8_t*>(index + kIndexOvfOff)[cell]) return;   // uniform per block
+    for (int j = tid; j < K; j += blockDim.x) scb[j] = reinterpret_cast<const float2*>(cb)[j];
+    if (tid == 0) {
+        npre = 0;
+        wbase = 0;
     }
-    const double lim = U * (1.0 + 1e-5);
-    uint16_t* s = slots + (size_t)cell * kIndexCap;
-    int n = 0;
-    for (int j = 0; j < K; ++j) {
-        double px = scb[j].x, py = scb[j].y;
-        double dx = fmax(fmax(x0 - px, px - x1), 0.0);
-        double dy = fmax(fmax(y0 - py, py - y1), 0.0);
-        if (dx * dx + dy * dy <= lim) {
-            if (n + 1 < kIndexCap) s[n + 1] = (uint16_t)j;
-            ++n;
+    const int cx = cell % ih.G, cy = cell / ih.G;
+    const bool empty = lo[cx] == lo[cx + 1] || lo[cy] == lo[cy + 1];
+    __syncthreads();
+    const CellBox q = cell_box(ih, lo, cell);
+    double U = 1e300;
+    for (int j = tid; j < K; j += blockDim.x) U = fmin(U, maxd2(q, scb[j].x, scb[j].y));
+    redU[tid] = U;
+    __syncthreads();
+    for (int s = 128; s > 0; s >>= 1) {
+        if (tid < s) redU[tid] = fmin(redU[tid], redU[tid + s]);
+        __syncthreads();
+    }
+    const double lim = redU[0] * (1.0 + 1e-5);
+    // prefilter (order within pre[] does not matter)
+    for (int j = tid; j < K; j += blockDim.x) {
+        if (!empty && mind2(q, scb[j].x, scb[j].y) <= lim) {
+            int at = atomicAdd(&npre, 1);
+            pre[at] = (uint16_t)j;
         }
     }
-    s[0] = (n + 1 < kIndexCap) ? (uint16_t)n : kCellOverflow;
-    for (int t = (n + 1 < kIndexCap ? n + 1 : kIndexCap); t < kIndexCap; ++t) s[t] = 0;
-    atomicMax(&hdr->max_count, n);
+    __syncthreads();
+    const int np = npre;
+    uint32_t count = 0;
+    const uint32_t base = pass ? offs[cell] : 0u;
+    // candidates in increasing j: chunks of 256 codewords, ordered by a workgroup prefix sum
+    for (int j0 = 0; j0 < K; j0 += blockDim.x) {
+        const int j = j0 + tid;
+        int is = 0;
+        if (!empty && j < K && mind2(q, scb[j].x, scb[j].y) <= lim) is = voronoi_meets(q, scb, j, pre, np) ? 1 : 0;
+        scan[tid] = is;
+        __syncthreads();
+        for (int s = 1; s < 256; s <<= 1) {
+            int v = (tid >= s) ? scan[tid - s] : 0;
+            __syncthreads();
+            scan[tid] += v;
+            __syncthreads();
+        }
+        const int total = scan[255];
+        if (pass && is) ent[base + count + scan[tid] - 1] = (uint16_t)j;
+        count += total;
+        __syncthreads();
+    }
+    if (tid == 0 && !pass) offs[cell] = count;   // counts; turned into offsets by k_ix_scan
 }
 
+// 3. Exclusive prefix sum of the counts (one workgroup); cells beyond the entry budget are
+// marked as overflow (count 0, searched exhaustively).
+__global__ __launch_bounds__(1024) void k_ix_scan(char* __restrict__ index, int max_entries) {
+    IndexHeader* hdr = reinterpret_cast<IndexHeader*>(index);
+    uint32_t* offs = reinterpret_cast<uint32_t*>(index + kIndexOffsOff);
+    uint8_t* ovf = reinterpret_cast<uint8_t*>(index + kIndexOvfOff);
+    if (threadIdx.x != 0) return;
+    const int cells = hdr->G * hdr->G;
+    uint32_t acc = 0;
+    int over = 0;
+    for (int c = 0; c < cells; ++c) {
+        uint32_t n = offs[c];
+        offs[c] = acc;
+        if (acc + n > (uint32_t)max_entries || n > kIndexCellCap) {
+            ovf[c] = 1;
+            ++over;
+        } else {
+            ovf[c] = 0;
+            acc += n;
+        }
+    }
+    offs[cells] = acc;
+    hdr->n_entries = (int)acc;
+    hdr->overflow = over;
+}
+
+// 5. Codewords in decreasing |c| (ties: lower index first), for points outside the grid.
+__global__ __launch_bounds__(256) void k_ix_order(const float* __restrict__ cb, int K, char* __restrict__ index) {
+    uint16_t* order = reinterpret_cast<uint16_t*>(index + kIndexOrderOff);
+    const int j = blockIdx.x * blockDim.x + threadIdx.x;
+    if (j >= K) return;
+    const float2 cj = reinterpret_cast<const float2*>(cb)[j];
+    const double nj = __builtin_sqrt((double)cj.x * cj.x + (double)cj.y * cj.y);
+    int rank = 0;
+    for (int k = 0; k < K; ++k) {
+        const float2 ck = reinterpret_cast<const float2*>(cb)[k];
+        const double nk = __builtin_sqrt((double)ck.x * ck.x + (double)ck.y * ck.y);
+        rank += (nk > nj || (nk == nj && k < j)) ? 1 : 0;
+    }
+    order[rank] = (uint16_t)j;
+}
+
+}  // namespace
+
 int index_grid_size(int bits) {
-    // about two cells per codeword spacing at the centre of a Gaussian-trained codebook
-    double K = (double)(1 << bits);
-    int G = 16;
-    while (G < 256 && G < 5.6 * __builtin_sqrt(K)) G *= 2;
-    return G;
+    // about one codeword per cell
+    int G = (int)std::lround(1.07 * std::sqrt((double)(1 << bits)));
+    return G < 4 ? 4 : (G > kIndexGMax ? kIndexGMax : G);
+}
+
+size_t index_bytes_for(int bits) {
+    return (size_t)kIndexEntOff + (size_t)kIndexMaxEntries * sizeof(uint16_t);
 }
 
 hipError_t launch_index_build(const float* cb, int bits, void* index, hipStream_t st) {
     const int K = 1 << bits;
     const int G = index_grid_size(bits);
-    IndexHeader* hdr = reinterpret_cast<IndexHeader*>(index);
-    uint16_t* slots = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(index) + kIndexHeaderBytes);
-    hipLaunchKernelGGL(k_index_header, dim3(1), dim3(256), 0, st, cb, K, G, bits, hdr);
-    const int cells = G * G;
-    hipLaunchKernelGGL(k_index_cells, dim3((cells + 255) / 256), dim3(256), K * sizeof(float2), st, cb, K, hdr,
-                       slots);
+    char* ix = reinterpret_cast<char*>(index);
+    hipLaunchKernelGGL(k_ix_grid, dim3(1), dim3(1024), 0, st, cb, K, G, kIndexFine, bits, ix);
+    const size_t smem = (size_t)K * sizeof(float2) + (size_t)K * sizeof(uint16_t);
+    allow_lds(k_ix_cells, smem);
+    hipLaunchKernelGGL(k_ix_cells, dim3(G * G), dim3(256), smem, st, cb, K, ix, 0);
+    hipLaunchKernelGGL(k_ix_scan, dim3(1), dim3(64), 0, st, ix, index_lds_entries(K));
+    hipLaunchKernelGGL(k_ix_cells, dim3(G * G), dim3(256), smem, st, cb, K, ix, 1);
+    hipLaunchKernelGGL(k_ix_order, dim3((K + 255) / 256), dim3(256), 0, st, cb, K, ix);
     return hipGetLastError();
 }
 
+namespace {
+
 __global__ __launch_bounds__(256) void k_nearest(const float* __restrict__ pts, int64_t n, const float* __restrict__ cb,
-                                                 int K, const IndexHeader* __restrict__ hdr,
-                                                 const uint16_t* __restrict__ slots, int32_t* __restrict__ out) {
-    extern __shared__ float2 scb[];
-    for (int j = threadIdx.x; j < K; j += blockDim.x) scb[j] = reinterpret_cast<const float2*>(cb)[j];
+                                                 int K, const char* __restrict__ index, int32_t* __restrict__ out) {
+    extern __shared__ __align__(16) char smem[];
+    SearchLds s = search_lds_carve(smem, K, *reinterpret_cast<const IndexHeader*>(index));
+    search_lds_fill(s, cb, K, index, threadIdx.x, blockDim.x);
     __syncthreads();
-    const IndexHeader ih = *hdr;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
         float2 p = reinterpret_cast<const float2*>(pts)[i];
-        out[i] = nearest_indexed(p.x, p.y, scb, K, ih, slots);
+        out[i] = nearest_lds(p.x, p.y, s, index);
     }
 }
+
+}  // namespace
 
 hipError_t launch_nearest(const float* pts, int64_t n, const float* cb, int bits, const void* index, int32_t* out,
                           hipStream_t st) {
     const int K = 1 << bits;
-    const IndexHeader* hdr = reinterpret_cast<const IndexHeader*>(index);
-    const uint16_t* slots =
-        reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(index) + kIndexHeaderBytes);
     int64_t blocks = (n + 255) / 256;
-    if (blocks > 4096) blocks = 4096;
+    if (blocks > 2048) blocks = 2048;
     if (blocks < 1) return hipSuccess;
-    hipLaunchKernelGGL(k_nearest, dim3((unsigned)blocks), dim3(256), K * sizeof(float2), st, pts, n, cb, K, hdr,
-                       slots, out);
+    const size_t smem = search_lds_bytes(K, index_grid_size(bits));
+    allow_lds(k_nearest, smem);
+    hipLaunchKernelGGL(k_nearest, dim3((unsigned)blocks), dim3(256), smem, st, pts, n, cb, K,
+                       reinterpret_cast<const char*>(index), out);
     return hipGetLastError();
 }
 

@@ -59,8 +59,7 @@ int32_t qamw_default_block(int32_t d_in) {
 
 size_t qamw_index_bytes(int32_t bits) {
     if (check_bits(bits) != QAMW_OK) return 0;
-    size_t G = (size_t)index_grid_size(bits);
-    return (size_t)kIndexHeaderBytes + G * G * kIndexCap * sizeof(uint16_t);
+    return index_bytes_for(bits);
 }
 
 size_t qamw_encode_workspace(int32_t d_out, int32_t d_in, int32_t bits) {
@@ -115,6 +114,7 @@ int qamw_encode(const void* d_w, qamw_dtype w_dtype, int32_t d_out, int32_t d_in
     int rc = check_bits(bits);
     if (rc) return rc;
     if (ld_w < d_in) return QAMW_ERR_ARG;
+    if (encode_lds_bytes(L, bits, d_in) > kLdsBytes) return QAMW_ERR_UNSUPPORTED;
     if (!d_sigma_in && !d_sigma_out) return QAMW_ERR_ARG;
     if (d_out > 0 && (!d_w || !d_codebook || !d_index || !d_norm_f16 || !d_codes)) return QAMW_ERR_ARG;
     if (d_out > 0 && (!aligned(d_codes, 4) || !aligned(d_codebook, 8) || !aligned(d_index, 16) ||

@@ -17,20 +17,55 @@
 namespace qamw {
 
 constexpr int kWave = 64;
+
+// Search-index layout (bytes from the start of the index buffer written by qamw_codebook_index).
+constexpr int kIndexFine = 2048;                          // W: fine bins per axis
+constexpr int kIndexFineMax = 2048;
+constexpr int kIndexGMax = 64;                            // cells per axis, at most
+constexpr int kIndexCellCap = 64;                         // longer lists: cell searched exhaustively
+constexpr int kIndexMaxEntries = 24576;                   // candidate-list budget (u16 entries)
 constexpr int kIndexHeaderBytes = 256;
-constexpr int kIndexCap = 32;         // uint16 slots per grid cell: [0] = count, then candidates
-constexpr uint16_t kCellOverflow = 0xFFFF;
+constexpr int kIndexFineOff = 256;                        // u8[W]   fine bin -> cell
+constexpr int kIndexEdgeOff = kIndexFineOff + 2048;       // u16[G+1] first fine bin of each cell
+constexpr int kIndexOvfOff = kIndexEdgeOff + 256;         // u8[G*G] overflow flags
+constexpr int kIndexOrderOff = kIndexOvfOff + 4096;       // u16[K]  codewords by decreasing norm
+constexpr int kIndexOffsOff = kIndexOrderOff + 8192;      // u32[G*G+1] list offsets
+constexpr int kIndexEntOff = kIndexOffsOff + 16384 + 256; // u16[]    candidate lists
 
 struct IndexHeader {
     int32_t K;
-    int32_t G;       // grid is G x G cells over [-R, R]^2
-    int32_t cap;
+    int32_t G;        // grid is G x G cells over [-R, R]^2
+    int32_t W;        // fine bins per axis
     int32_t bits;
     float R;
-    float inv_h;     // G / (2R)
-    int32_t ready;
-    int32_t max_count;
+    float inv_w;      // W / (2R)
+    int32_t n_entries;
+    int32_t overflow; // cells searched exhaustively
 };
+
+// Candidate-list entries kept in LDS for a 2^bits codebook: enough for Gaussian-trained
+// codebooks (about 5 per cell); a codebook needing more gets exhaustive cells instead.
+__host__ __device__ constexpr int index_lds_entries(int K) {
+    return (6 * K < kIndexMaxEntries) ? (6 * K < 64 ? 64 : 6 * K) : kIndexMaxEntries;
+}
+
+__host__ __device__ constexpr size_t align16(size_t v) { return (v + 15) & ~(size_t)15; }
+
+// LDS image of the codebook and its index used by the search.
+struct SearchLds {
+    float2* cb;
+    uint16_t* order;   // codewords by decreasing norm
+    uint8_t* fine;
+    uint16_t* offs;
+    uint16_t* ent;
+    float R, inv_w;
+    int W, G, K;
+};
+
+__host__ __device__ inline size_t search_lds_bytes(int K, int G) {
+    return align16((size_t)K * 8) + align16((size_t)K * 2) + align16(kIndexFine) + align16((size_t)(G * G + 1) * 2) +
+           align16((size_t)index_lds_entries(K) * 2);
+}
 
 template <int L>
 struct Layout {
@@ -57,6 +92,13 @@ __device__ __forceinline__ void butterfly(double (&x)[E], int rbit) {
             x[m | (1 << rbit)] = a - c;
         }
     }
+}
+
+// Keep a value in a register: the empty asm hides how it was computed, so the compiler cannot
+// rematerialize it (e.g. redo a division) inside a loop.
+template <typename T>
+__device__ __forceinline__ void pin_reg(T& v) {
+    asm volatile("" : "+v"(v));
 }
 
 // Make LDS writes of this wavefront visible to its other lanes before the reads that follow.
@@ -93,61 +135,156 @@ __device__ __forceinline__ void exchange_AB(double (&x)[Layout<L>::E], double* x
     }
 }
 
-// Exact nearest codeword (fp32 distance fl(fl(dx*dx) + fl(dy*dy)), ties to the lowest index)
-// of (px, py) among the candidates of its grid cell; points outside the grid, non-finite
-// points and overflowing cells search all K codewords.
-__device__ __forceinline__ void eval_cw(float px, float py, float2 c, int j, float& bd, int& bj) {
+// Exact nearest codeword (fp32 distance fl(fl(dx*dx) + fl(dy*dy)), ties to the lowest index).
+__device__ __forceinline__ float dist_f32(float px, float py, float2 c) {
     float dx = px - c.x;
     float dy = py - c.y;
-    float d = dx * dx + dy * dy;   // built with -ffp-contract=off: three rounded operations
+    return dx * dx + dy * dy;   // built with -ffp-contract=off: three rounded operations
+}
+
+__device__ __forceinline__ void eval_cw(float px, float py, float2 c, int j, float& bd, int& bj) {
+    float d = dist_f32(px, py, c);
     if (d < bd) {
         bd = d;
         bj = j;
     }
 }
 
-__device__ __forceinline__ int nearest_indexed(float px, float py, const float2* __restrict__ cb, int K,
-                                               const IndexHeader& ih, const uint16_t* __restrict__ slots) {
+__device__ inline SearchLds search_lds_carve(char* smem, int K, const IndexHeader& ih) {
+    SearchLds s;
+    char* p = smem;
+    s.cb = reinterpret_cast<float2*>(p);
+    p += align16((size_t)K * 8);
+    s.order = reinterpret_cast<uint16_t*>(p);
+    p += align16((size_t)K * 2);
+    s.fine = reinterpret_cast<uint8_t*>(p);
+    p += align16(kIndexFine);
+    s.offs = reinterpret_cast<uint16_t*>(p);
+    p += align16((size_t)(ih.G * ih.G + 1) * 2);
+    s.ent = reinterpret_cast<uint16_t*>(p);
+    s.R = ih.R;
+    s.inv_w = ih.inv_w;
+    s.W = ih.W;
+    s.G = ih.G;
+    s.K = K;
+    return s;
+}
+
+// Copy the codebook and the index into LDS (the caller synchronizes afterwards).
+__device__ inline void search_lds_fill(const SearchLds& s, const float* __restrict__ cb, int K,
+                                       const char* __restrict__ index, int tid, int nthreads) {
+    const IndexHeader& ih = *reinterpret_cast<const IndexHeader*>(index);
+    const uint32_t* offs = reinterpret_cast<const uint32_t*>(index + kIndexOffsOff);
+    const uint16_t* ent = reinterpret_cast<const uint16_t*>(index + kIndexEntOff);
+    const uint8_t* fine = reinterpret_cast<const uint8_t*>(index + kIndexFineOff);
+    const int ne = min(ih.n_entries, index_lds_entries(K));   // the builder keeps n_entries within this
+    const uint16_t* order = reinterpret_cast<const uint16_t*>(index + kIndexOrderOff);
+    for (int j = tid; j < K; j += nthreads) {
+        s.cb[j] = reinterpret_cast<const float2*>(cb)[j];
+        s.order[j] = order[j];
+    }
+    for (int b = tid; b < s.W; b += nthreads) s.fine[b] = fine[b];
+    const int cells = s.G * s.G;
+    for (int c = tid; c <= cells; c += nthreads) {
+        uint32_t o = offs[c];
+        s.offs[c] = (uint16_t)(o < (uint32_t)ne ? o : (uint32_t)ne);
+    }
+    for (int e = tid; e < ne; e += nthreads) s.ent[e] = ent[e];
+}
+
+// Points outside the grid: scan codewords by decreasing norm, stopping once |p| - |c| exceeds
+// sqrt(D_a (1 + 1e-5)) for a known codeword a -- no later codeword can then beat or tie a.
+__device__ __attribute__((noinline)) int nearest_exterior(float px, float py, const SearchLds& s) {
+    const float lim_in = s.R * 0.999f;
+    const float qx = fminf(fmaxf(px, -lim_in), lim_in), qy = fminf(fmaxf(py, -lim_in), lim_in);
+    const int bx = min((int)((qx + s.R) * s.inv_w), s.W - 1), by = min((int)((qy + s.R) * s.inv_w), s.W - 1);
+    const int cell = s.fine[by] * s.G + s.fine[bx];
+    const int a = (s.offs[cell + 1] > s.offs[cell]) ? s.ent[s.offs[cell]] : 0;
+    const float da = dist_f32(px, py, s.cb[a]);
+    const double pn = __builtin_sqrt((double)px * px + (double)py * py);
+    const double lim = pn - __builtin_sqrt((double)da * (1.0 + 1e-5));
+    const double lim2 = lim > 0.0 ? lim * lim : -1.0;
     float bd = __builtin_inff();
-    int bj = 0;
-    bool inside = fabsf(px) < ih.R && fabsf(py) < ih.R;
-    int n = 0;
-    const uint16_t* list = nullptr;
-    if (inside) {
-        int cx = min((int)((px + ih.R) * ih.inv_h), ih.G - 1);
-        int cy = min((int)((py + ih.R) * ih.inv_h), ih.G - 1);
-        list = slots + (size_t)(cy * ih.G + cx) * ih.cap;
-        uint4 head = *reinterpret_cast<const uint4*>(list);
-        n = head.x & 0xFFFF;
-        if (n == kCellOverflow) {
-            inside = false;
-        } else {
-            // first seven candidates come with the count
-            uint32_t w[4] = {head.x, head.y, head.z, head.w};
-#pragma unroll
-            for (int t = 1; t < 8; ++t) {
-                if (t <= n) {
-                    int j = (w[t >> 1] >> ((t & 1) * 16)) & 0xFFFF;
-                    eval_cw(px, py, cb[j], j, bd, bj);
-                }
-            }
-            for (int t0 = 8; t0 <= n; t0 += 8) {
-                uint4 v = *reinterpret_cast<const uint4*>(list + t0);
-                uint32_t u[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    if (t0 + t <= n) {
-                        int j = (u[t >> 1] >> ((t & 1) * 16)) & 0xFFFF;
-                        eval_cw(px, py, cb[j], j, bd, bj);
-                    }
-                }
-            }
+    int bj = s.K;
+    for (int t = 0; t < s.K; ++t) {
+        const int j = s.order[t];
+        const float2 c = s.cb[j];
+        if ((double)c.x * c.x + (double)c.y * c.y < lim2) break;   // |c| < lim, exact squares in double
+        const float d = dist_f32(px, py, c);
+        if (d < bd || (d == bd && j < bj)) {
+            bd = d;
+            bj = j;
         }
     }
-    if (!inside) {
-        for (int j = 0; j < K; ++j) eval_cw(px, py, cb[j], j, bd, bj);
-    }
     return bj;
+}
+
+__device__ __forceinline__ int nearest_lds(float px, float py, const SearchLds& s, const char* __restrict__ index) {
+    if (fabsf(px) < s.R && fabsf(py) < s.R) {
+        const int bx = min((int)((px + s.R) * s.inv_w), s.W - 1);
+        const int by = min((int)((py + s.R) * s.inv_w), s.W - 1);
+        const int cell = s.fine[by] * s.G + s.fine[bx];
+        const int o0 = s.offs[cell], o1 = s.offs[cell + 1];
+        float bd = __builtin_inff();
+        int bj = 0;
+        if (o1 > o0) {
+            for (int o = o0; o < o1; ++o) {
+                const int j = s.ent[o];
+                eval_cw(px, py, s.cb[j], j, bd, bj);
+            }
+        } else {   // cell searched exhaustively (its list did not fit)
+            for (int j = 0; j < s.K; ++j) eval_cw(px, py, s.cb[j], j, bd, bj);
+        }
+        return bj;
+    }
+    if (!(__builtin_isfinite(px) && __builtin_isfinite(py))) return 0;   // every distance is NaN or inf
+    return nearest_exterior(px, py, s);
+}
+
+// NP points searched in lockstep: step t evaluates the t-th listed candidate of every point (the
+// last one again once a list is exhausted, which cannot change a strict-< argmin), so each step
+// issues NP independent LDS lookups.  Points outside the grid, in exhaustive cells or non-finite
+// take the single-point paths afterwards.
+template <int NP>
+__device__ __forceinline__ void nearest_lds_batch(const float (&px)[NP], const float (&py)[NP], const SearchLds& s,
+                                                  const char* __restrict__ index, int (&out)[NP]) {
+    int o[NP], last[NP];
+    float bd[NP];
+    uint32_t slow = 0;
+    int steps = 0;
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+        bd[i] = __builtin_inff();
+        out[i] = 0;
+        int o0 = 0, o1 = 0;   // empty: points outside the grid take the slow path
+        if (fabsf(px[i]) < s.R && fabsf(py[i]) < s.R) {
+            const int bx = min((int)((px[i] + s.R) * s.inv_w), s.W - 1);
+            const int by = min((int)((py[i] + s.R) * s.inv_w), s.W - 1);
+            const int cell = s.fine[by] * s.G + s.fine[bx];
+            o0 = s.offs[cell];
+            o1 = s.offs[cell + 1];
+        }
+        if (o1 <= o0) {   // outside the grid, non-finite, or exhaustive cell
+            slow |= 1u << i;
+            o0 = 0;
+            o1 = 1;
+        }
+        o[i] = o0;
+        last[i] = o1 - 1;
+        steps = max(steps, o1 - o0);
+    }
+    for (int t = 0; t < steps; ++t) {
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+            const int j = s.ent[min(o[i] + t, last[i])];
+            eval_cw(px[i], py[i], s.cb[j], j, bd[i], out[i]);
+        }
+    }
+    if (slow) {
+#pragma unroll
+        for (int i = 0; i < NP; ++i)
+            if (slow & (1u << i)) out[i] = nearest_lds(px[i], py[i], s, index);
+    }
 }
 
 __device__ __forceinline__ float bf16_bits_to_float(uint16_t h) {

@@ -16,6 +16,7 @@ inline void allow_lds(K kernel, size_t bytes) {
 }
 
 int index_grid_size(int bits);
+size_t index_bytes_for(int bits);
 hipError_t launch_index_build(const float* cb, int bits, void* index, hipStream_t st);
 hipError_t launch_nearest(const float* pts, int64_t n, const float* cb, int bits, const void* index, int32_t* out,
                           hipStream_t st);
@@ -66,6 +67,8 @@ struct DecodeArgs {
 
 // Elements per lane of the transform layout for block size 2^L.
 int lane_elems(int L);
+size_t encode_lds_bytes(int L, int bits, int d_in);
+constexpr size_t kLdsBytes = 160 * 1024;   // LDS per CU on gfx950
 int calib_groups(int n_rows);
 size_t calib_workspace(int d_out, int d_in);
 
