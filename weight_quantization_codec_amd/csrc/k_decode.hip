@@ -33,6 +33,14 @@ __device__ __forceinline__ int dcol_B(int tid, int m) {
 }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 values to a BF16 pair (RNE), one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    const f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const uint8_t* codes, size_t stride, int row) {
     return __builtin_amdgcn_make_buffer_rsrc((void*)(codes + (size_t)row * stride), (short)0, (int)stride,
@@ -125,7 +133,6 @@ __global__ __launch_bounds__(MAXT) void k_decode(DecodeArgs a, int T, int R) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave_in_row = tid / kWave;
     const bool active = tid < a.d_in / E;
-    const uint16_t* __restrict__ norms = a.norm;
     const int rstride = gridDim.x * R;
 
     // this wave's code span: E*bits dwords from dword wave_in_row*E*bits of the row
@@ -137,39 +144,125 @@ __global__ __launch_bounds__(MAXT) void k_decode(DecodeArgs a, int T, int R) {
         coff[c] = d < span_dw ? (uint32_t)((wave_in_row * span_dw + d) * 4) : 0x7FFFFFF0u;
     }
 
+    // Row loads never branch: a row past the end gets a descriptor covering no bytes (the loads
+    // return 0), so the loop body is straight-line code and the wait for the prefetched row can
+    // leave the previous row's stores in flight.
+    const __amdgpu_buffer_rsrc_t nrs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)a.norm, (short)0, a.d_out * 2, 0x00020000);
+    auto load_row = [&](int r, u32x4 (&dst)[DW::nload], uint16_t& nh) {
+        const bool ok = r < a.d_out;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(a.codes + (size_t)(ok ? r : 0) * a.stride), (short)0, ok ? (int)a.stride : 0, 0x00020000);
+        nh = __builtin_amdgcn_raw_buffer_load_b16(nrs, (uint32_t)r * 2u, 0, 0);
+#pragma unroll
+        for (int c = 0; c < DW::nload; ++c) dst[c] = __builtin_amdgcn_raw_buffer_load_b128(rs, coff[c], 0, 0);
+    };
+
     int row = blockIdx.x * R + grp;
     u32x4 nxt[DW::nload];
-    uint16_t nh_next = 0;
-    if (row < a.d_out) {
-        nh_next = norms[row];
-        const __amdgpu_buffer_rsrc_t rs = row_rsrc(a.codes, a.stride, row);
-#pragma unroll
-        for (int c = 0; c < DW::nload; ++c) nxt[c] = __builtin_amdgcn_raw_buffer_load_b128(rs, coff[c], 0, 0);
-    }
+    uint16_t nh_next;
+    load_row(row, nxt, nh_next);
 
-    for (int j = threadIdx.x; j < K; j += blockDim.x) {
-        float2 c = reinterpret_cast<const float2*>(a.cb)[j];
-        tab[j] = make_double2((double)c.x + (double)c.y, (double)c.x - (double)c.y);   // exact in double
+    // ---- once per workgroup: codebook table, sigma of this lane's pairs, eps_j / s_j of its columns
+    {   // table entry j = (c_x + c_y, c_x - c_y), exact in double; two codewords per 16-byte load
+        const __amdgpu_buffer_rsrc_t crs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)a.cb, (short)0, K * 8, 0x00020000);
+        for (int j = 2 * (int)threadIdx.x; j < K; j += 2 * (int)blockDim.x) {
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(crs, (uint32_t)j * 8u, 0, 0);
+            const double x0 = __uint_as_float(v[0]), y0 = __uint_as_float(v[1]);
+            const double x1 = __uint_as_float(v[2]), y1 = __uint_as_float(v[3]);
+            tab[j] = make_double2(x0 + y0, x0 - y0);
+            tab[j + 1] = make_double2(x1 + y1, x1 - y1);
+        }
     }
-    double sg[NP];
+    float sg[NP];   // kept in fp32 (half the registers); widened exactly where used
+    {
+        const __amdgpu_buffer_rsrc_t srs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)a.sigma, (short)0, (a.d_in / 2) * 4, 0x00020000);
 #pragma unroll
-    for (int i = 0; i < NP; ++i) {
-        sg[i] = (double)a.sigma[min(tid * NP + i, a.d_in / 2 - 1)];
-        pin_reg(sg[i]);
+        for (int c = 0; c < NP / 4; ++c) {
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(srs, (uint32_t)(tid * NP + 4 * c) * 4u, 0, 0);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) sg[4 * c + k] = __uint_as_float(v[k]);
+        }
     }
+#pragma unroll
+    for (int i = 0; i < NP; ++i) pin_reg(sg[i]);
+    // eps_j / s_j: the workgroup computes a chunk of columns into LDS (the staging buffers, not yet
+    // in use), four columns per thread, and each lane copies the columns it owns.  Chunks hold
+    // whole column groups (a lane's columns never straddle two chunks).
     double cf[E];
 #pragma unroll
-    for (int m = 0; m < E; ++m) {
-        int j = min(dcol_B<L>(tid, m), a.d_in - 1);
-        double e = (a.sign && ((a.sign[j >> 5] >> (j & 31)) & 1u)) ? -1.0 : 1.0;
-        cf[m] = e * recip(a.scale ? (double)a.scale[j] : 1.0);
-        pin_reg(cf[m]);
+    for (int m = 0; m < E; ++m) cf[m] = 1.0;
+    if (a.scale || a.sign) {
+        double* cfl = reinterpret_cast<double*>(smem + (size_t)K * sizeof(double2));
+        constexpr int CB = Lo::b > E ? Lo::b : E;
+        const int chunk = (int)(blockDim.x / kWave) * DW::dwords / 2 / CB * CB;
+        const int my0 = Lo::two_phase ? (tid / Lo::lanes) * Lo::b : tid * E;   // first column of the group
+        const __amdgpu_buffer_rsrc_t srs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)a.scale, (short)0, a.scale ? a.d_in * 4 : 0, 0x00020000);
+        for (int c0 = 0; c0 < a.d_in; c0 += chunk) {
+            const int n = min(chunk, a.d_in - c0);
+            for (int j = 4 * (int)threadIdx.x; j < n; j += 4 * (int)blockDim.x) {
+                const int col = c0 + j;   // a multiple of 4: the four sign bits share one word
+                double r[4] = {1.0, 1.0, 1.0, 1.0};
+                if (a.scale) {
+                    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(srs, (uint32_t)col * 4u, 0, 0);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) r[u] = recip((double)__uint_as_float(v[u]));
+                }
+                if (a.sign) {
+                    const uint32_t sw = a.sign[col >> 5] >> (col & 31);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        if ((sw >> u) & 1u) r[u] = -r[u];
+                }
+                if (j + 4 <= n) {
+                    *reinterpret_cast<double2*>(cfl + j) = make_double2(r[0], r[1]);
+                    *reinterpret_cast<double2*>(cfl + j + 2) = make_double2(r[2], r[3]);
+                } else {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        if (j + u < n) cfl[j + u] = r[u];
+                }
+            }
+            __syncthreads();
+            if (my0 >= c0 && my0 < c0 + n) {
+#pragma unroll
+                for (int m = 0; m < E; m += 2) {
+                    const int col = dcol_B<L>(tid, m);   // even; col + 1 is element m + 1
+                    if (col < a.d_in) {
+                        const double2 v = *reinterpret_cast<const double2*>(cfl + (col - c0));
+                        cf[m] = v.x;
+                        cf[m + 1] = v.y;
+                    }
+                }
+            }
+            __syncthreads();
+        }
     }
+#pragma unroll
+    for (int m = 0; m < E; ++m) pin_reg(cf[m]);
     // output: chunk c of this wave covers dwords [256 c, 256 c + 256) of the wave's span
     constexpr int out_dw = kWave * E * ESZ / 4;
     constexpr int nchunk = out_dw / 256;
     const uint32_t wave_byte0 = (uint32_t)(wave_in_row * out_dw * 4);
     const double inv_sqrt_b = 1.0 / __builtin_sqrt((double)Lo::b);
+    // Staged output: element m of this lane goes to dword pad(kb + o(m)) of the wave buffer, kb
+    // per lane and o(m) a compile-time offset.  kb's place within its 32-dword group plus o(m)'s
+    // never crosses a group, so pad(kb + o) = pad(kb) + o + 4*(o/32): one base register.
+    uint32_t* stg;
+    {
+        const unsigned ul = (unsigned)lane;
+        unsigned kb;
+        if constexpr (Lo::two_phase) {
+            const unsigned beta = ul / Lo::lanes, q = ul % Lo::lanes;
+            kb = OBF ? beta * (Lo::b / 2) + q : beta * Lo::b + 2 * q;
+        } else {
+            kb = OBF ? ul * (E / 2) : ul * E;
+        }
+        stg = wb + DW::pad((int)kb);
+    }
     __syncthreads();
 
     for (; row < a.d_out; row += rstride) {
@@ -177,13 +270,7 @@ __global__ __launch_bounds__(MAXT) void k_decode(DecodeArgs a, int T, int R) {
         u32x4 cur[DW::nload];
 #pragma unroll
         for (int c = 0; c < DW::nload; ++c) cur[c] = nxt[c];
-        const int rnext = row + rstride;
-        if (rnext < a.d_out) {   // keep the next row's codes in flight
-            nh_next = norms[rnext];
-            const __amdgpu_buffer_rsrc_t rs = row_rsrc(a.codes, a.stride, rnext);
-#pragma unroll
-            for (int c = 0; c < DW::nload; ++c) nxt[c] = __builtin_amdgcn_raw_buffer_load_b128(rs, coff[c], 0, 0);
-        }
+        load_row(row + rstride, nxt, nh_next);   // keep the next row in flight
         const float rn = __half2float(__ushort_as_half(nh));
         const bool zero_row = rn == 0.0f;
         // codes -> LDS -> fields of this lane
@@ -198,7 +285,7 @@ __global__ __launch_bounds__(MAXT) void k_decode(DecodeArgs a, int T, int R) {
 #pragma unroll
             for (int i = 0; i < NP; ++i) {
                 double2 t = tab[idx[i]];
-                double sc = sg[i] * g;
+                double sc = (double)sg[i] * g;
                 x[2 * i] = t.x * sc;
                 x[2 * i + 1] = t.y * sc;
             }
@@ -216,18 +303,18 @@ __global__ __launch_bounds__(MAXT) void k_decode(DecodeArgs a, int T, int R) {
             for (int r = 1; r < L; ++r) butterfly<E>(x, r);
         }
         // scale, round, and stage the output in wave order
+        const uint32_t keep = zero_row ? 0u : ~0u;   // a zero row decodes to +0
 #pragma unroll
         for (int m = 0; m < E; m += 2) {
-            float v0 = (float)(x[m] * cf[m]);
-            float v1 = (float)(x[m + 1] * cf[m + 1]);
-            const int e = dcol_B<L>(lane, m);   // element index within the wave's span
+            const float v0 = (float)(x[m] * cf[m]);
+            const float v1 = (float)(x[m + 1] * cf[m + 1]);
             if constexpr (OBF) {
-                __hip_bfloat162 p = __float22bfloat162_rn(make_float2(v0, v1));
-                uint32_t u = *reinterpret_cast<uint32_t*>(&p);
-                wb[DW::pad(e >> 1)] = zero_row ? 0u : u;   // a zero row decodes to +0
+                const int o = Lo::two_phase ? (m >> 1) * Lo::lanes : m / 2;
+                stg[o + 4 * (o >> 5)] = pack_bf16x2(v0, v1) & keep;
             } else {
-                wb[DW::pad(e)] = zero_row ? 0u : __float_as_uint(v0);
-                wb[DW::pad(e + 1)] = zero_row ? 0u : __float_as_uint(v1);
+                const int o = Lo::two_phase ? (m >> 1) * 2 * Lo::lanes : m;
+                stg[o + 4 * (o >> 5)] = __float_as_uint(v0) & keep;
+                stg[o + 1 + 4 * ((o + 1) >> 5)] = __float_as_uint(v1) & keep;
             }
         }
         wave_lds_sync();

@@ -110,27 +110,26 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 // Phase A -> phase B for one wavefront.  `xb` is the wavefront's exchange buffer
 // (Layout<L>::xbuf doubles).  lane = lane id in the wavefront.
+// Compact index c of a (block-local) element sits at c + c/H (one pad double per H).  The lanes
+// of a block divide H, so both address streams are one per-lane base plus compile-time offsets:
+//   write: element q*E + 2i + h -> c = base + q*H + i,        c/H = base/H + q
+//   read : element h | (q<<1) | (i<<(L-e+1)) -> c = base + q + i*lanes, c/H = base/H + i*lanes/H
 template <int L>
 __device__ __forceinline__ void exchange_AB(double (&x)[Layout<L>::E], double* xb, int lane) {
     using Lo = Layout<L>;
-    constexpr int E = Lo::E, H = Lo::half;
-    const int beta = lane / Lo::lanes, q = lane % Lo::lanes;
-    const int base = beta * (Lo::b / 2);
+    constexpr int H = Lo::half, NL = Lo::lanes;
+    static_assert(H % NL == 0, "lanes of a block must divide E/2");
+    const unsigned beta = (unsigned)lane / NL, q = (unsigned)lane % NL;
+    const unsigned base = beta * (Lo::b / 2);
+    double* wr = xb + (base + base / H + q * (H + 1));
+    double* rd = xb + (base + base / H + q);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        // write: element q*E + 2i + h  ->  compact index c = base + q*H + i
 #pragma unroll
-        for (int i = 0; i < H; ++i) {
-            int c = base + q * H + i;
-            xb[c + c / H] = x[2 * i + h];
-        }
+        for (int i = 0; i < H; ++i) wr[i] = x[2 * i + h];
         wave_lds_sync();
-        // read: element j = h | (q << 1) | (i << (L-e+1))  ->  c = base + q + (i << (L-e))
 #pragma unroll
-        for (int i = 0; i < H; ++i) {
-            int c = base + q + (i << (L - Lo::e));
-            x[2 * i + h] = xb[c + c / H];
-        }
+        for (int i = 0; i < H; ++i) x[2 * i + h] = rd[i * NL + (i * NL) / H];
         wave_lds_sync();
     }
 }
