@@ -42,6 +42,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
+// Cache policy of the output stores: non-temporal.  The decoded matrix is written once and
+// streamed; on gfx950 this raises the sustained rate of the mixed code-read / output-write
+// traffic from about 4.5 to about 6 TB/s (measured with 1 KiB-contiguous 16-byte stores).
+constexpr int kStoreNT = 2;
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const uint8_t* codes, size_t stride, int row) {
     return __builtin_amdgcn_make_buffer_rsrc((void*)(codes + (size_t)row * stride), (short)0, (int)stride,
                                              0x00020000);
@@ -324,12 +329,12 @@ __global__ __launch_bounds__(MAXT) void k_decode(DecodeArgs a, int T, int R) {
             const u32x4 v = *reinterpret_cast<const u32x4*>(wb + DW::pad(256 * c + 4 * lane));
             const uint32_t off = wave_byte0 + (uint32_t)(c * 1024 + 16 * lane);
             if constexpr (L >= 3) {   // d_in is a multiple of b >= 8: rows are whole 16-byte chunks
-                __builtin_amdgcn_raw_buffer_store_b128(v, ors, off, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(v, ors, off, 0, kStoreNT);
             } else {
-                __builtin_amdgcn_raw_buffer_store_b32(v[0], ors, off, 0, 0);
-                __builtin_amdgcn_raw_buffer_store_b32(v[1], ors, off + 4, 0, 0);
-                __builtin_amdgcn_raw_buffer_store_b32(v[2], ors, off + 8, 0, 0);
-                __builtin_amdgcn_raw_buffer_store_b32(v[3], ors, off + 12, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b32(v[0], ors, off, 0, kStoreNT);
+                __builtin_amdgcn_raw_buffer_store_b32(v[1], ors, off + 4, 0, kStoreNT);
+                __builtin_amdgcn_raw_buffer_store_b32(v[2], ors, off + 8, 0, kStoreNT);
+                __builtin_amdgcn_raw_buffer_store_b32(v[3], ors, off + 12, 0, kStoreNT);
             }
         }
         wave_lds_sync();
