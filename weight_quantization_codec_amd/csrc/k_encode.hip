@@ -29,8 +29,43 @@ __device__ __forceinline__ double wave_sum(double v) {
     return v;
 }
 
-__device__ __forceinline__ double eps_of(const uint32_t* sign, int j) {
-    return (sign && ((sign[j >> 5] >> (j & 31)) & 1u)) ? -1.0 : 1.0;
+// s_j * eps_j of the E consecutive columns tid*E .. tid*E + E - 1 of a lane (phase A), exact in
+// fp32: the scales with 16-byte buffer loads and the E sign bits from one 32-bit word (E >= 16
+// divides 32 or is a multiple of it).  Columns at or past d_in get 1.  bad is set when a scale
+// of the lane is not > 0 (NaN included).
+template <int E>
+__device__ __forceinline__ void load_cf(const float* scale, const uint32_t* sign, int tid, int d_in, float (&cf)[E],
+                                        bool& bad) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const int j0 = tid * E;
+    if (scale) {
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)scale, (short)0, d_in * 4, 0x00020000);
+#pragma unroll
+        for (int v = 0; v < E / 4; ++v) {
+            const u32x4 q = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)(j0 + 4 * v) * 4u, 0, 0);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) cf[4 * v + k] = __uint_as_float(q[k]);
+        }
+    } else {
+#pragma unroll
+        for (int m = 0; m < E; ++m) cf[m] = 1.0f;
+    }
+#pragma unroll
+    for (int m = 0; m < E; ++m) {
+        if (j0 + m >= d_in) cf[m] = 1.0f;
+        bad |= !(cf[m] > 0.0f);
+    }
+    if (sign) {
+        static_assert(E >= 16, "lane groups of at least 16 columns");
+#pragma unroll
+        for (int w = 0; w < (E + 31) / 32; ++w) {
+            const int jw = j0 + 32 * w;
+            const uint32_t bits = jw < d_in ? sign[jw >> 5] >> (jw & 31) : 0u;
+#pragma unroll
+            for (int m = 32 * w; m < E && m < 32 * (w + 1); ++m)
+                if ((bits >> (m - 32 * w)) & 1u) cf[m] = -cf[m];
+        }
+    }
 }
 
 // Column of register m of this lane in the final (phase B) layout.
@@ -88,7 +123,7 @@ __device__ __forceinline__ void load_raw(const void* w, bool vec, int64_t off, R
 
 // a_j = w_j * s_j * eps_j in double (exact), accumulating sum a_j^2.
 template <int E, bool BF>
-__device__ __forceinline__ void scale_raw(const RawW<E, BF>& r, const double (&cf)[E], double (&x)[E], double& ss,
+__device__ __forceinline__ void scale_raw(const RawW<E, BF>& r, const float (&cf)[E], double (&x)[E], double& ss,
                                           int32_t& flags) {
 #pragma unroll
     for (int m = 0; m < E; ++m) {
@@ -97,7 +132,7 @@ __device__ __forceinline__ void scale_raw(const RawW<E, BF>& r, const double (&c
             f = __uint_as_float((m & 1) ? (r.u[m >> 1] & 0xFFFF0000u) : (r.u[m >> 1] << 16));
         else
             f = __uint_as_float(r.u[m]);
-        double a = (double)f * cf[m];
+        double a = (double)f * (double)cf[m];   // exact: two 24-bit significands
         if (!__builtin_isfinite(a)) flags |= 1;
         x[m] = a;
         ss += a * a;
@@ -108,7 +143,7 @@ __device__ __forceinline__ void scale_raw(const RawW<E, BF>& r, const double (&c
 // returns sum a^2 over the whole row (fixed shuffle tree, then wavefronts in order).
 template <int L, bool BF>
 __device__ __forceinline__ double front_end(const RawW<Layout<L>::E, BF>& raw, bool active, int tid,
-                                            const double (&cf)[Layout<L>::E], double (&x)[Layout<L>::E],
+                                            const float (&cf)[Layout<L>::E], double (&x)[Layout<L>::E],
                                             double* red, double* xb, int nwaves, int32_t& flags) {
     using Lo = Layout<L>;
     constexpr int E = Lo::E;
@@ -138,40 +173,48 @@ __device__ __forceinline__ double front_end(const RawW<Layout<L>::E, BF>& raw, b
     return r2;
 }
 
+// Pair calibration, first pass.  A workgroup runs R rows at a time (R groups of T lanes, T =
+// lanes per row); group g takes rows base + g for base = R * blockIdx.x, R * (blockIdx.x +
+// gridDim.x), ...  Every group runs every pass (rows past the end are zero), so the barriers in
+// the front end are reached by the whole workgroup.  At the end the groups' |z_k| sums are added
+// in group order and written as the workgroup's partial sums.
 template <int L, int MAXT, bool BF>
-__global__ __launch_bounds__(MAXT) void k_calibrate(CalibArgs a) {
+__global__ __launch_bounds__(MAXT) void k_calibrate(CalibArgs a, int T, int R) {
     using Lo = Layout<L>;
     constexpr int E = Lo::E, NP = E / 2;
     extern __shared__ __align__(16) char smem[];
-    double* red = reinterpret_cast<double*>(smem);
-    double* xb = red + kMaxWaves + (threadIdx.x / kWave) * Lo::xbuf;
-    const int tid = threadIdx.x, nwaves = blockDim.x / kWave;
+    const int grp = __builtin_amdgcn_readfirstlane(threadIdx.x / T);
+    const int tid = threadIdx.x - grp * T, nwaves = T / kWave;
+    double* red = reinterpret_cast<double*>(smem) + grp * kMaxWaves;
+    double* xb_all = reinterpret_cast<double*>(smem) + R * kMaxWaves;
+    double* xb = xb_all + (threadIdx.x / kWave) * Lo::xbuf;
     const int units = a.d_in / E;
     const bool active = tid < units;
     const bool vec = (((uintptr_t)a.w & 15) == 0) && (((a.ld * (BF ? 2 : 4)) & 15) == 0);
-    double cf[E];
-#pragma unroll
-    for (int m = 0; m < E; ++m) {
-        int j = min(tid * E + m, a.d_in - 1);
-        cf[m] = (a.scale ? (double)a.scale[j] : 1.0) * eps_of(a.sign, j);
-    }
+    RawW<E, BF> nxt;
+    const int rstride = gridDim.x * R;
+    int base = blockIdx.x * R;
+    if (active && base + grp < a.n_rows) load_raw<E, BF>(a.w, vec, (int64_t)(base + grp) * a.ld + (int64_t)tid * E, nxt);
+    float cf[E];   // s_j * eps_j, exact in fp32 (scales are checked by the encoder)
+    bool bad_scale = false;
+    load_cf<E>(a.scale, a.sign, tid, a.d_in, cf, bad_scale);
+    (void)bad_scale;
     const double inv_sqrt_b = 1.0 / __builtin_sqrt((double)Lo::b);
     double acc[NP];
 #pragma unroll
     for (int i = 0; i < NP; ++i) acc[i] = 0.0;
     int nz = 0;
     int32_t flags = 0;
-    RawW<E, BF> nxt;
-    int row = blockIdx.x;
-    if (active && row < a.n_rows) load_raw<E, BF>(a.w, vec, (int64_t)row * a.ld + (int64_t)tid * E, nxt);
-    for (; row < a.n_rows; row += gridDim.x) {
+    for (; base < a.n_rows; base += rstride) {
+        const int row = base + grp;
+        const bool rv = row < a.n_rows;
         const RawW<E, BF> cur = nxt;
-        if (active && row + (int)gridDim.x < a.n_rows)
-            load_raw<E, BF>(a.w, vec, (int64_t)(row + gridDim.x) * a.ld + (int64_t)tid * E, nxt);
+        if (active && row + rstride < a.n_rows)
+            load_raw<E, BF>(a.w, vec, (int64_t)(row + rstride) * a.ld + (int64_t)tid * E, nxt);
         double x[E];
-        double r2 = front_end<L, BF>(cur, active, tid, cf, x, red, xb, nwaves, flags);
+        double r2 = front_end<L, BF>(cur, active && rv, tid, cf, x, red, xb, nwaves, flags);
         double r = __builtin_sqrt(r2);
-        if (r > 0.0 && __builtin_isfinite(r)) {
+        if (rv && r > 0.0 && __builtin_isfinite(r)) {
             ++nz;
             double hr = inv_sqrt_b / r;
 #pragma unroll
@@ -180,28 +223,61 @@ __global__ __launch_bounds__(MAXT) void k_calibrate(CalibArgs a) {
                 acc[i] += __builtin_sqrt(y0 * y0 + y1 * y1);
             }
         }
-        __syncthreads();   // red[] is rewritten by the next row
+        __syncthreads();   // red[] and the exchange buffers are rewritten by the next pass
     }
-    if (active) {
+    // groups' sums in group order, through LDS (the exchange buffers are free now)
+    double* comb = xb_all;
+    for (int g = 0; g < R; ++g) {
+        if (grp == g && active) {
+#pragma unroll
+            for (int i = 0; i < NP; ++i) {
+                const int k = col_B<L>(tid, 2 * i) / 2;
+                comb[k] = (g == 0) ? acc[i] : comb[k] + acc[i];
+            }
+        }
+        __syncthreads();
+    }
+    // rows with a non-zero norm: one count per group (lane 0 of its first wave), added in order
+    __shared__ int nz_grp[8];
+    if (tid == 0) nz_grp[grp] = nz;
+    __syncthreads();
+    if (grp == 0 && active) {
         double* part = a.partial + (size_t)blockIdx.x * (a.d_in / 2);
 #pragma unroll
-        for (int i = 0; i < NP; ++i) part[col_B<L>(tid, 2 * i) / 2] = acc[i];
+        for (int i = 0; i < NP; ++i) {
+            const int k = col_B<L>(tid, 2 * i) / 2;
+            part[k] = comb[k];
+        }
     }
-    if (tid == 0) a.nz[blockIdx.x] = nz;
+    if (threadIdx.x == 0) {
+        int n = 0;
+        for (int g = 0; g < R; ++g) n += nz_grp[g];
+        a.nz[blockIdx.x] = n;
+    }
 }
 
-// sigma_k from the per-group sums: each pair's groups are split over 4 threads, every thread adds
-// its groups in increasing order, and the 4 partial sums are added in a fixed order.
-__global__ __launch_bounds__(256) void k_calibrate_finish(const double* __restrict__ partial,
-                                                          const int32_t* __restrict__ nzs, int n_groups, int n_pairs,
-                                                          int d_in, float* __restrict__ sigma) {
-    __shared__ double part[4][64];
-    const int kl = threadIdx.x & 63, quarter = threadIdx.x >> 6;
+// sigma_k from the per-group sums.  A block owns 64 pairs; each pair's groups are split into 16
+// contiguous runs, one per thread, every thread adds its run in increasing group order, and the
+// 16 run sums are added in run order, so the result does not depend on scheduling.  The count of
+// non-zero rows is reduced by the whole block.
+constexpr int kFinishParts = 16;
+__global__ __launch_bounds__(1024) void k_calibrate_finish(const double* __restrict__ partial,
+                                                           const int32_t* __restrict__ nzs, int n_groups, int n_pairs,
+                                                           int d_in, float* __restrict__ sigma) {
+    __shared__ double part[kFinishParts][64];
+    __shared__ int64_t nzw[1024 / kWave];
+    const int kl = threadIdx.x & 63, q = threadIdx.x >> 6;
     const int k = blockIdx.x * 64 + kl;
+    // rows counted by the groups (each thread at most one group per pass)
+    int64_t nn = 0;
+    for (int g = threadIdx.x; g < n_groups; g += blockDim.x) nn += nzs[g];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) nn += __shfl_xor(nn, off, kWave);
+    if (kl == 0) nzw[q] = nn;
     double s = 0.0;
     if (k < n_pairs) {
-        const int per = (n_groups + 3) / 4;
-        const int g0 = quarter * per, g1 = min(n_groups, g0 + per);
+        const int per = (n_groups + kFinishParts - 1) / kFinishParts;
+        const int g0 = q * per, g1 = min(n_groups, g0 + per);
         int g = g0;
         for (; g + 8 <= g1; g += 8) {
             double v[8];
@@ -212,12 +288,14 @@ __global__ __launch_bounds__(256) void k_calibrate_finish(const double* __restri
         }
         for (; g < g1; ++g) s += partial[(size_t)g * n_pairs + k];
     }
-    part[quarter][kl] = s;
+    part[q][kl] = s;
     __syncthreads();
-    if (quarter != 0 || k >= n_pairs) return;
+    if (q != 0 || k >= n_pairs) return;
     int64_t n = 0;
-    for (int g = 0; g < n_groups; ++g) n += nzs[g];
-    double tot = ((part[0][kl] + part[1][kl]) + part[2][kl]) + part[3][kl];
+    for (int w = 0; w < (int)(blockDim.x / kWave); ++w) n += nzw[w];
+    double tot = part[0][kl];
+#pragma unroll
+    for (int r = 1; r < kFinishParts; ++r) tot += part[r][kl];
     double m = (n > 0) ? tot / (double)n : 0.0;
     const double rayleigh_mean = __builtin_sqrt(3.14159265358979323846 / 2.0);   // E|z| = sigma sqrt(pi/2)
     sigma[k] = (m > 0.0) ? (float)(m / rayleigh_mean) : (float)(1.0 / __builtin_sqrt((double)d_in));
@@ -243,15 +321,12 @@ __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a) {
     const bool active = tid < units;
     const bool vec = (((uintptr_t)a.w & 15) == 0) && (((a.ld * (BF ? 2 : 4)) & 15) == 0);
     int32_t flags = 0;
-    double cf[E];
+    float cf[E];   // s_j * eps_j, exact in fp32
+    bool bad_scale = false;
+    load_cf<E>(a.scale, a.sign, tid, a.d_in, cf, bad_scale);
+    if (active && bad_scale) flags |= 2;
 #pragma unroll
-    for (int m = 0; m < E; ++m) {
-        int j = min(tid * E + m, a.d_in - 1);
-        float s = a.scale ? a.scale[j] : 1.0f;
-        if (active && !(s > 0.0f)) flags |= 2;
-        cf[m] = (double)s * eps_of(a.sign, j);
-        pin_reg(cf[m]);
-    }
+    for (int m = 0; m < E; ++m) pin_reg(cf[m]);
     double isg[NP];
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
@@ -334,10 +409,14 @@ size_t encode_smem(int K, int nwaves, int d_in) {
            (Lo::two_phase ? (size_t)nwaves * Lo::xbuf * sizeof(double) : 0) + (size_t)(d_in / 2) * sizeof(uint16_t);
 }
 
+// R * kMaxWaves norm partials, then the exchange buffers (at least d_in/2 doubles: they also
+// hold the groups' combined sums at the end).
 template <int L>
-size_t calib_smem(int nwaves) {
+size_t calib_smem(int R, int nwaves) {
     using Lo = Layout<L>;
-    return kMaxWaves * sizeof(double) + (Lo::two_phase ? (size_t)nwaves * Lo::xbuf * sizeof(double) : 0);
+    const size_t xb = Lo::two_phase ? (size_t)nwaves * Lo::xbuf * sizeof(double) : 0;
+    const size_t comb = (size_t)nwaves * kWave * (Lo::E / 2) * sizeof(double);
+    return (size_t)R * kMaxWaves * sizeof(double) + (xb > comb ? xb : comb);
 }
 
 template <int L, bool BF>
@@ -368,24 +447,31 @@ hipError_t encode_LB(const EncodeArgs& a, hipStream_t st) {
 template <int L, bool BF>
 hipError_t calibrate_LB(const CalibArgs& a, float* sigma, hipStream_t st) {
     using Lo = Layout<L>;
-    int threads = ((a.d_in / Lo::E) + kWave - 1) / kWave * kWave;
-    int nwaves = threads / kWave;
-    if (a.n_groups > 0) {
+    constexpr int kMax = L <= 7 ? 1024 : 512;
+    const int T = ((a.d_in / Lo::E) + kWave - 1) / kWave * kWave;
+    if (T > kMax) return hipErrorInvalidConfiguration;
+    int R = kMax / T;
+    if (R > 4) R = 4;
+    int groups = 0;
+    if (a.n_rows > 0) {
+        if (R > a.n_rows) R = a.n_rows;
+        groups = (a.n_rows + R - 1) / R;
+        if (groups > a.n_groups) groups = a.n_groups;   // the workspace holds n_groups partial rows
+        const int threads = R * T;
+        const size_t smem = calib_smem<L>(R, threads / kWave);
         if (threads <= 512) {
-            allow_lds(k_calibrate<L, 512, BF>, calib_smem<L>(nwaves));
-            hipLaunchKernelGGL((k_calibrate<L, 512, BF>), dim3(a.n_groups), dim3(threads), calib_smem<L>(nwaves), st,
-                               a);
+            allow_lds(k_calibrate<L, 512, BF>, smem);
+            hipLaunchKernelGGL((k_calibrate<L, 512, BF>), dim3(groups), dim3(threads), smem, st, a, T, R);
         } else if constexpr (L <= 7) {
-            allow_lds(k_calibrate<L, 1024, BF>, calib_smem<L>(nwaves));
-            hipLaunchKernelGGL((k_calibrate<L, 1024, BF>), dim3(a.n_groups), dim3(threads), calib_smem<L>(nwaves), st,
-                               a);
+            allow_lds(k_calibrate<L, 1024, BF>, smem);
+            hipLaunchKernelGGL((k_calibrate<L, 1024, BF>), dim3(groups), dim3(threads), smem, st, a, T, R);
         } else {
             return hipErrorInvalidConfiguration;
         }
     }
     int n_pairs = a.d_in / 2;
-    hipLaunchKernelGGL(k_calibrate_finish, dim3((n_pairs + 63) / 64), dim3(256), 0, st, a.partial, a.nz,
-                       a.n_groups, n_pairs, a.d_in, sigma);
+    hipLaunchKernelGGL(k_calibrate_finish, dim3((n_pairs + 63) / 64), dim3(64 * kFinishParts), 0, st, a.partial, a.nz,
+                       groups, n_pairs, a.d_in, sigma);
     return hipGetLastError();
 }
 
