@@ -301,30 +301,80 @@ __global__ __launch_bounds__(1024) void k_calibrate_finish(const double* __restr
     sigma[k] = (m > 0.0) ? (float)(m / rayleigh_mean) : (float)(1.0 / __builtin_sqrt((double)d_in));
 }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Raw weights of one row for a lane through a buffer descriptor: a row past the end has a
+// descriptor covering no bytes and reads zeros, so the prefetch never branches.  Requires the
+// 16-byte vector path (row starts 16-byte aligned).
+template <int E, bool BF>
+__device__ __forceinline__ void load_raw_buf(const void* w, int64_t ld, int d_in, int d_out, int row, int tid,
+                                             RawW<E, BF>& r) {
+    constexpr int ESZ = BF ? 2 : 4;
+    const bool ok = row < d_out;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(reinterpret_cast<const char*>(w) + (size_t)(ok ? row : 0) * (size_t)ld * ESZ), (short)0,
+        ok ? d_in * ESZ : 0, 0x00020000);
+    const uint32_t off = (uint32_t)tid * (uint32_t)(E * ESZ);
+#pragma unroll
+    for (int v = 0; v < RawW<E, BF>::N / 4; ++v) {
+        const u32x4 q = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16u * v, 0, 0);
+        r.u[4 * v] = q[0];
+        r.u[4 * v + 1] = q[1];
+        r.u[4 * v + 2] = q[2];
+        r.u[4 * v + 3] = q[3];
+    }
+}
+
+// Encoder.  A workgroup runs R rows at a time (R groups of T lanes, T = lanes per row) over one
+// LDS image of the codebook and its search index; group g takes rows base + g for base = R *
+// blockIdx.x, R * (blockIdx.x + gridDim.x), ...  Every group runs every pass (a row past the end
+// is all zero and writes nothing), so the workgroup barriers are reached by all threads.
+// Per pass: front end (scale, norm, transform), pairs, lockstep search in batches of four pairs
+// per lane, indices to LDS, then the group packs its row into 16-byte words.
+constexpr int kSearchBatch = 4;
+
 template <int L, int MAXT, bool BF>
-__global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a) {
+__global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a, int T, int R) {
     using Lo = Layout<L>;
     constexpr int E = Lo::E, NP = E / 2;
     extern __shared__ __align__(16) char smem[];
     const int K = 1 << a.bits;
-    const int tid = threadIdx.x, nwaves = blockDim.x / kWave;
+    const int grp = __builtin_amdgcn_readfirstlane(threadIdx.x / T);
+    const int tid = threadIdx.x - grp * T, nwaves = T / kWave;
     const char* index = reinterpret_cast<const char*>(a.index);
     const IndexHeader ih = *reinterpret_cast<const IndexHeader*>(index);
     const SearchLds sl = search_lds_carve(smem, K, ih);
-    double* red = reinterpret_cast<double*>(smem + search_lds_bytes(K, ih.G));
-    double* xb_all = red + kMaxWaves;
-    double* xb = xb_all + (tid / kWave) * Lo::xbuf;
-    uint16_t* idxrow = reinterpret_cast<uint16_t*>(xb_all + (Lo::two_phase ? nwaves * Lo::xbuf : 0));
-    search_lds_fill(sl, a.cb, K, index, tid, blockDim.x);
+    double* red_all = reinterpret_cast<double*>(smem + search_lds_bytes(K, ih.G));
+    double* red = red_all + grp * kMaxWaves;
+    double* xb_all = red_all + R * kMaxWaves;
+    double* xb = xb_all + (threadIdx.x / kWave) * Lo::xbuf;
+    const int n_pairs = a.d_in / 2;
+    const int idx_stride = (n_pairs + 7) & ~7;   // u16 entries per group, 16-byte multiple
+    uint16_t* idxrow = reinterpret_cast<uint16_t*>(xb_all + (Lo::two_phase ? (R * T / kWave) * Lo::xbuf : 0)) +
+                       grp * idx_stride;
+    // this lane's pairs k = col_B(tid, 2i)/2 are base + i * (lanes per block): one base address
+    uint16_t* idxrow_l = idxrow + (Lo::two_phase ? ((unsigned)tid / Lo::lanes) * (Lo::b / 2) + (unsigned)tid % Lo::lanes
+                                                 : (unsigned)tid * NP);
 
-    const int units = a.d_in / E, n_pairs = a.d_in / 2;
+    const int units = a.d_in / E;
     const bool active = tid < units;
     const bool vec = (((uintptr_t)a.w & 15) == 0) && (((a.ld * (BF ? 2 : 4)) & 15) == 0);
+    const int rstride = gridDim.x * R;
+    int base = blockIdx.x * R;
+
+    RawW<E, BF> nxt;
+    if (vec) {
+        load_raw_buf<E, BF>(a.w, a.ld, a.d_in, a.d_out, base + grp, tid, nxt);
+    } else if (active && base + grp < a.d_out) {
+        load_raw<E, BF>(a.w, false, (int64_t)(base + grp) * a.ld + (int64_t)tid * E, nxt);
+    }
+    search_lds_fill(sl, a.cb, K, index, threadIdx.x, blockDim.x);
+
     int32_t flags = 0;
     float cf[E];   // s_j * eps_j, exact in fp32
     bool bad_scale = false;
     load_cf<E>(a.scale, a.sign, tid, a.d_in, cf, bad_scale);
-    if (active && bad_scale) flags |= 2;
+    if (active && bad_scale && blockIdx.x == 0) flags |= 2;   // reported once
 #pragma unroll
     for (int m = 0; m < E; ++m) pin_reg(cf[m]);
     double isg[NP];
@@ -333,46 +383,51 @@ __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a) {
         isg[i] = 1.0 / (double)a.sigma[min(col_B<L>(tid, 2 * i) / 2, n_pairs - 1)];
         pin_reg(isg[i]);
     }
-    if (blockIdx.x != 0) flags &= ~2;   // report a bad scale once
     const double inv_sqrt_b = 1.0 / __builtin_sqrt((double)Lo::b);
     const int bits = a.bits;
     const int nwords = (int)(a.stride / 4);
-
-    RawW<E, BF> nxt;
-    int row = blockIdx.x;
-    if (active && row < a.d_out) load_raw<E, BF>(a.w, vec, (int64_t)row * a.ld + (int64_t)tid * E, nxt);
     __syncthreads();
 
-    for (; row < a.d_out; row += gridDim.x) {
+    for (; base < a.d_out; base += rstride) {
+        const int row = base + grp;
+        const bool rv = row < a.d_out;
         const RawW<E, BF> cur = nxt;
-        if (active && row + (int)gridDim.x < a.d_out)   // prefetch the next row while this one is encoded
-            load_raw<E, BF>(a.w, vec, (int64_t)(row + gridDim.x) * a.ld + (int64_t)tid * E, nxt);
+        if (vec) {   // keep the next row in flight
+            load_raw_buf<E, BF>(a.w, a.ld, a.d_in, a.d_out, row + rstride, tid, nxt);
+        } else if (active && row + rstride < a.d_out) {
+            load_raw<E, BF>(a.w, false, (int64_t)(row + rstride) * a.ld + (int64_t)tid * E, nxt);
+        }
         double x[E];
         int32_t rf = 0;
-        double r2 = front_end<L, BF>(cur, active, tid, cf, x, red, xb, nwaves, rf);
-        double r = __builtin_sqrt(r2);
-        bool nonzero = r > 0.0 && __builtin_isfinite(r);
-        if (!__builtin_isfinite(r)) rf |= 1;
+        const double r2 = front_end<L, BF>(cur, active && rv, tid, cf, x, red, xb, nwaves, rf);
+        const double r = __builtin_sqrt(r2);
+        const bool nonzero = r > 0.0 && __builtin_isfinite(r);
+        if (rv && !__builtin_isfinite(r)) rf |= 1;
         if (active) {
-            if (nonzero) {
-                const double hr = inv_sqrt_b / r;
-                float px[NP], py[NP];
+            float px[NP], py[NP];
+            const double hr = inv_sqrt_b / r;
 #pragma unroll
-                for (int i = 0; i < NP; ++i) {
-                    double g = isg[i] * hr;
-                    px[i] = (float)(x[2 * i] * g);
-                    py[i] = (float)(x[2 * i + 1] * g);
+            for (int i = 0; i < NP; ++i) {
+                const double g = isg[i] * hr;
+                px[i] = (float)(x[2 * i] * g);
+                py[i] = (float)(x[2 * i + 1] * g);
+            }
+#pragma unroll
+            for (int h = 0; h < NP / kSearchBatch; ++h) {
+                float bx[kSearchBatch], by[kSearchBatch];
+                int bi[kSearchBatch];
+#pragma unroll
+                for (int i = 0; i < kSearchBatch; ++i) {
+                    bx[i] = px[h * kSearchBatch + i];
+                    by[i] = py[h * kSearchBatch + i];
                 }
-                int idx[NP];
-                nearest_lds_batch<NP>(px, py, sl, index, idx);
+                if (nonzero) nearest_lds_batch<kSearchBatch>(bx, by, sl, bi);
 #pragma unroll
-                for (int i = 0; i < NP; ++i) idxrow[col_B<L>(tid, 2 * i) / 2] = (uint16_t)idx[i];
-            } else {
-#pragma unroll
-                for (int i = 0; i < NP; ++i) idxrow[col_B<L>(tid, 2 * i) / 2] = 0;
+                for (int i = 0; i < kSearchBatch; ++i)
+                    idxrow_l[(h * kSearchBatch + i) * (Lo::two_phase ? Lo::lanes : 1)] = nonzero ? (uint16_t)bi[i] : (uint16_t)0;
             }
         }
-        if (tid == 0) {
+        if (tid == 0 && rv) {
             uint16_t nh = 0;
             if (nonzero) {
                 __half hv = __float2half_rn((float)r);
@@ -381,32 +436,44 @@ __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a) {
             }
             a.norm[row] = nh;
         }
-        flags |= rf;
+        if (rv) flags |= rf;
         __syncthreads();
-        uint32_t* crow = reinterpret_cast<uint32_t*>(a.codes + (size_t)row * a.stride);
-        for (int wd = tid; wd < nwords; wd += blockDim.x) {
-            const int bit0 = wd * 32;
-            const int k0 = bit0 / bits;
-            const int k1 = min((bit0 + 31) / bits, n_pairs - 1);
-            uint32_t v = 0;
-            for (int k = k0; k <= k1; ++k) {
-                uint32_t val = idxrow[k];
-                int pos = k * bits - bit0;
-                v |= (pos >= 0) ? (val << pos) : (val >> (-pos));
+        // pack: thread t of the group writes words 4t .. 4t+3 of the row with one 16-byte store
+        // (the row stride is a multiple of 16 bytes; words past the indices are zero padding)
+        const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(a.codes + (size_t)(rv ? row : 0) * a.stride), (short)0, rv ? (int)a.stride : 0, 0x00020000);
+        for (int w4 = tid; 4 * w4 < nwords; w4 += T) {
+            u32x4 q;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int bit0 = (4 * w4 + u) * 32;
+                const int k0 = bit0 / bits;
+                const int k1 = min((bit0 + 31) / bits, n_pairs - 1);
+                uint32_t v = 0;
+                for (int k = k0; k <= k1; ++k) {
+                    const uint32_t val = idxrow[k];
+                    const int pos = k * bits - bit0;
+                    v |= (pos >= 0) ? (val << pos) : (val >> (-pos));
+                }
+                q[u] = v;
             }
-            crow[wd] = v;
+            __builtin_amdgcn_raw_buffer_store_b128(q, crs, (uint32_t)w4 * 16u, 0, 0);
         }
     }
     flag_status(a.status, flags);
 }
 
+// LDS of the encoder: search image, R * kMaxWaves norm partials, one exchange buffer per
+// wavefront, and R rows of indices.
 template <int L>
-size_t encode_smem(int K, int nwaves, int d_in) {
+size_t encode_smem(int K, int R, int nwaves_total, int d_in) {
     using Lo = Layout<L>;
     int bits = 0;
     while ((1 << bits) < K) ++bits;
-    return search_lds_bytes(K, index_grid_size(bits)) + kMaxWaves * sizeof(double) +
-           (Lo::two_phase ? (size_t)nwaves * Lo::xbuf * sizeof(double) : 0) + (size_t)(d_in / 2) * sizeof(uint16_t);
+    const size_t idx_stride = (size_t)((d_in / 2 + 7) & ~7);
+    return search_lds_bytes(K, index_grid_size(bits)) + (size_t)R * kMaxWaves * sizeof(double) +
+           (Lo::two_phase ? (size_t)nwaves_total * Lo::xbuf * sizeof(double) : 0) +
+           (size_t)R * idx_stride * sizeof(uint16_t);
 }
 
 // R * kMaxWaves norm partials, then the exchange buffers (at least d_in/2 doubles: they also
@@ -422,22 +489,30 @@ size_t calib_smem(int R, int nwaves) {
 template <int L, bool BF>
 hipError_t encode_LB(const EncodeArgs& a, hipStream_t st) {
     using Lo = Layout<L>;
-    int threads = ((a.d_in / Lo::E) + kWave - 1) / kWave * kWave;
-    int nwaves = threads / kWave;
-    size_t smem = encode_smem<L>(1 << a.bits, nwaves, a.d_in);
-    int blocks_per_cu = (int)((160 * 1024) / smem);
-    if (blocks_per_cu < 1) return hipErrorInvalidConfiguration;
-    if (blocks_per_cu * nwaves > 32) blocks_per_cu = 32 / nwaves;
-    if (blocks_per_cu < 1) blocks_per_cu = 1;
-    int grid = 256 * blocks_per_cu;
-    if (grid > a.d_out) grid = a.d_out;
+    constexpr int kMax = L <= 7 ? 1024 : 512;
+    const int T = ((a.d_in / Lo::E) + kWave - 1) / kWave * kWave;
+    if (T > kMax) return hipErrorInvalidConfiguration;
+    const int K = 1 << a.bits;
+    int R = kMax / T;
+    if (R > 4) R = 4;
+    if (R > a.d_out) R = a.d_out > 0 ? a.d_out : 1;
+    while (R > 1 && encode_smem<L>(K, R, R * T / kWave, a.d_in) > kLdsBytes) --R;
+    const int threads = R * T;
+    const size_t smem = encode_smem<L>(K, R, threads / kWave, a.d_in);
+    if (smem > kLdsBytes) return hipErrorInvalidConfiguration;
+    int per_cu = (int)(kLdsBytes / smem);
+    if (per_cu * (threads / kWave) > 32) per_cu = 32 / (threads / kWave);
+    if (per_cu < 1) per_cu = 1;
+    int grid = 256 * per_cu;
+    const int need = (a.d_out + R - 1) / R;
+    if (grid > need) grid = need;
     if (grid < 1) return hipSuccess;
     if (threads <= 512) {
         allow_lds(k_encode<L, 512, BF>, smem);
-        hipLaunchKernelGGL((k_encode<L, 512, BF>), dim3(grid), dim3(threads), smem, st, a);
+        hipLaunchKernelGGL((k_encode<L, 512, BF>), dim3(grid), dim3(threads), smem, st, a, T, R);
     } else if constexpr (L <= 7) {
         allow_lds(k_encode<L, 1024, BF>, smem);
-        hipLaunchKernelGGL((k_encode<L, 1024, BF>), dim3(grid), dim3(threads), smem, st, a);
+        hipLaunchKernelGGL((k_encode<L, 1024, BF>), dim3(grid), dim3(threads), smem, st, a, T, R);
     } else {
         return hipErrorInvalidConfiguration;
     }
@@ -509,7 +584,7 @@ size_t encode_lds_bytes(int L, int bits, int d_in) {
     const int nwaves = ((d_in / E) + kWave - 1) / kWave;
     const size_t xb = (L > 4) ? (size_t)nwaves * (kWave * (E / 2) + kWave) * sizeof(double) : 0;
     return search_lds_bytes(1 << bits, index_grid_size(bits)) + kMaxWaves * sizeof(double) + xb +
-           (size_t)(d_in / 2) * sizeof(uint16_t);
+           (size_t)((d_in / 2 + 7) & ~7) * sizeof(uint16_t);
 }
 
 int calib_groups(int n_rows) { return n_rows < kCalibMaxGroups ? n_rows : kCalibMaxGroups; }

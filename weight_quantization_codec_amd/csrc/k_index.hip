@@ -305,7 +305,7 @@ __global__ __launch_bounds__(256) void k_nearest(const float* __restrict__ pts, 
     __syncthreads();
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
         float2 p = reinterpret_cast<const float2*>(pts)[i];
-        out[i] = nearest_lds(p.x, p.y, s, index);
+        out[i] = nearest_lds(p.x, p.y, s);
     }
 }
 

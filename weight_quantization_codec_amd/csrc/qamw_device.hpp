@@ -191,9 +191,12 @@ __device__ inline void search_lds_fill(const SearchLds& s, const float* __restri
     for (int e = tid; e < ne; e += nthreads) s.ent[e] = ent[e];
 }
 
+// True when any active lane of the wavefront has a non-zero value.
+__device__ __forceinline__ bool wave_any(uint32_t v) { return __builtin_amdgcn_ballot_w64(v != 0) != 0; }
+
 // Points outside the grid: scan codewords by decreasing norm, stopping once |p| - |c| exceeds
 // sqrt(D_a (1 + 1e-5)) for a known codeword a -- no later codeword can then beat or tie a.
-__device__ __attribute__((noinline)) int nearest_exterior(float px, float py, const SearchLds& s) {
+__device__ __forceinline__ int nearest_exterior(float px, float py, const SearchLds& s) {
     const float lim_in = s.R * 0.999f;
     const float qx = fminf(fmaxf(px, -lim_in), lim_in), qy = fminf(fmaxf(py, -lim_in), lim_in);
     const int bx = min((int)((qx + s.R) * s.inv_w), s.W - 1), by = min((int)((qy + s.R) * s.inv_w), s.W - 1);
@@ -218,35 +221,45 @@ __device__ __attribute__((noinline)) int nearest_exterior(float px, float py, co
     return bj;
 }
 
-__device__ __forceinline__ int nearest_lds(float px, float py, const SearchLds& s, const char* __restrict__ index) {
-    if (fabsf(px) < s.R && fabsf(py) < s.R) {
-        const int bx = min((int)((px + s.R) * s.inv_w), s.W - 1);
-        const int by = min((int)((py + s.R) * s.inv_w), s.W - 1);
-        const int cell = s.fine[by] * s.G + s.fine[bx];
-        const int o0 = s.offs[cell], o1 = s.offs[cell + 1];
+// The slow cases of one point: outside the grid, non-finite, or in a cell searched exhaustively.
+__device__ __forceinline__ int nearest_slow(float px, float py, const SearchLds& s) {
+    if (fabsf(px) < s.R && fabsf(py) < s.R) {   // exhaustive cell (its list did not fit)
         float bd = __builtin_inff();
         int bj = 0;
-        if (o1 > o0) {
-            for (int o = o0; o < o1; ++o) {
-                const int j = s.ent[o];
-                eval_cw(px, py, s.cb[j], j, bd, bj);
-            }
-        } else {   // cell searched exhaustively (its list did not fit)
-            for (int j = 0; j < s.K; ++j) eval_cw(px, py, s.cb[j], j, bd, bj);
-        }
+        for (int j = 0; j < s.K; ++j) eval_cw(px, py, s.cb[j], j, bd, bj);
         return bj;
     }
     if (!(__builtin_isfinite(px) && __builtin_isfinite(py))) return 0;   // every distance is NaN or inf
     return nearest_exterior(px, py, s);
 }
 
+__device__ __forceinline__ int nearest_lds(float px, float py, const SearchLds& s) {
+    if (fabsf(px) < s.R && fabsf(py) < s.R) {
+        const int bx = min((int)((px + s.R) * s.inv_w), s.W - 1);
+        const int by = min((int)((py + s.R) * s.inv_w), s.W - 1);
+        const int cell = s.fine[by] * s.G + s.fine[bx];
+        const int o0 = s.offs[cell], o1 = s.offs[cell + 1];
+        if (o1 > o0) {
+            float bd = __builtin_inff();
+            int bj = 0;
+            for (int o = o0; o < o1; ++o) {
+                const int j = s.ent[o];
+                eval_cw(px, py, s.cb[j], j, bd, bj);
+            }
+            return bj;
+        }
+    }
+    return nearest_slow(px, py, s);
+}
+
 // NP points searched in lockstep: step t evaluates the t-th listed candidate of every point (the
 // last one again once a list is exhausted, which cannot change a strict-< argmin), so each step
 // issues NP independent LDS lookups.  Points outside the grid, in exhaustive cells or non-finite
-// take the single-point paths afterwards.
+// take the single-point path afterwards, one point slot at a time (a uniform loop, so the slow
+// path exists once in the code).
 template <int NP>
 __device__ __forceinline__ void nearest_lds_batch(const float (&px)[NP], const float (&py)[NP], const SearchLds& s,
-                                                  const char* __restrict__ index, int (&out)[NP]) {
+                                                  int (&out)[NP]) {
     int o[NP], last[NP];
     float bd[NP];
     uint32_t slow = 0;
@@ -279,10 +292,22 @@ __device__ __forceinline__ void nearest_lds_batch(const float (&px)[NP], const f
             eval_cw(px[i], py[i], s.cb[j], j, bd[i], out[i]);
         }
     }
-    if (slow) {
+    if (wave_any(slow)) {
+#pragma unroll 1
+        for (int i = 0; i < NP; ++i) {
+            if (!wave_any(slow & (1u << i))) continue;
+            float qx = px[0], qy = py[0];
 #pragma unroll
-        for (int i = 0; i < NP; ++i)
-            if (slow & (1u << i)) out[i] = nearest_lds(px[i], py[i], s, index);
+            for (int k = 1; k < NP; ++k) {
+                qx = (i == k) ? px[k] : qx;
+                qy = (i == k) ? py[k] : qy;
+            }
+            int r = 0;
+            if (slow & (1u << i)) r = nearest_slow(qx, qy, s);
+#pragma unroll
+            for (int k = 0; k < NP; ++k)
+                if (i == k && (slow & (1u << i))) out[k] = r;
+        }
     }
 }
 
