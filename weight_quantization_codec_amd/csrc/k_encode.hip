@@ -333,6 +333,16 @@ __device__ __forceinline__ void load_raw_buf(const void* w, int64_t ld, int d_in
 // per lane, indices to LDS, then the group packs its row into 16-byte words.
 constexpr int kSearchBatch = 4;
 
+// LDS bytes per row group of the encoder: the indices (u16, zero-padded to a multiple of 32) and
+// the packed words, which cover whole 32-index chunks and at least the row stride.
+__host__ __device__ inline size_t encode_group_bytes(int n_pairs, int bits) {
+    const size_t idx_stride = (size_t)((n_pairs + 31) & ~31);
+    const size_t stride = (((size_t)n_pairs * bits + 7) / 8 + 15) / 16 * 16;
+    const size_t chunk_words = idx_stride * bits / 8;
+    const size_t stage = ((stride > chunk_words ? stride : chunk_words) + 15) / 16 * 16;
+    return idx_stride * 2 + stage;
+}
+
 template <int L, int MAXT, bool BF>
 __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a, int T, int R) {
     using Lo = Layout<L>;
@@ -349,9 +359,14 @@ __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a, int T, int R) {
     double* xb_all = red_all + R * kMaxWaves;
     double* xb = xb_all + (threadIdx.x / kWave) * Lo::xbuf;
     const int n_pairs = a.d_in / 2;
-    const int idx_stride = (n_pairs + 7) & ~7;   // u16 entries per group, 16-byte multiple
-    uint16_t* idxrow = reinterpret_cast<uint16_t*>(xb_all + (Lo::two_phase ? (R * T / kWave) * Lo::xbuf : 0)) +
-                       grp * idx_stride;
+    // per group: the row's indices (u16, padded with zeros to a multiple of 32), then its packed
+    // words (the row stride, a multiple of 16 bytes)
+    const int idx_stride = (n_pairs + 31) & ~31;
+    const int grp_bytes = (int)encode_group_bytes(n_pairs, a.bits);
+    char* gbuf = reinterpret_cast<char*>(xb_all + (Lo::two_phase ? (R * T / kWave) * Lo::xbuf : 0)) + grp * grp_bytes;
+    uint16_t* idxrow = reinterpret_cast<uint16_t*>(gbuf);
+    uint32_t* stage = reinterpret_cast<uint32_t*>(gbuf + idx_stride * 2);
+    for (int k = n_pairs + tid; k < idx_stride; k += T) idxrow[k] = 0;   // never written again
     // this lane's pairs k = col_B(tid, 2i)/2 are base + i * (lanes per block): one base address
     uint16_t* idxrow_l = idxrow + (Lo::two_phase ? ((unsigned)tid / Lo::lanes) * (Lo::b / 2) + (unsigned)tid % Lo::lanes
                                                  : (unsigned)tid * NP);
@@ -438,25 +453,36 @@ __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a, int T, int R) {
         }
         if (rv) flags |= rf;
         __syncthreads();
-        // pack: thread t of the group writes words 4t .. 4t+3 of the row with one 16-byte store
-        // (the row stride is a multiple of 16 bytes; words past the indices are zero padding)
+        // pack: 32 consecutive indices fill exactly `bits` words; thread t packs chunk t (the shift
+        // sequence is the same for every chunk, so the branches are uniform) into the staging words
+        const int nchunks = idx_stride / 32;
+        for (int c = tid; c < nchunks; c += T) {
+            uint64_t acc = 0;
+            int nb = 0;
+            uint32_t* wp = stage + c * bits;
+#pragma unroll
+            for (int k8 = 0; k8 < 4; ++k8) {
+                const uint4 q = *reinterpret_cast<const uint4*>(idxrow + 32 * c + 8 * k8);
+                const uint32_t v[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    acc |= (uint64_t)((v[u >> 1] >> (16 * (u & 1))) & 0xFFFFu) << nb;
+                    nb += bits;
+                    if (nb >= 32) {
+                        *wp++ = (uint32_t)acc;
+                        acc >>= 32;
+                        nb -= 32;
+                    }
+                }
+            }
+        }
+        for (int wd = nchunks * bits + tid; wd < nwords; wd += T) stage[wd] = 0;   // row padding
+        __syncthreads();
+        // 16-byte stores of the staged row
         const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(a.codes + (size_t)(rv ? row : 0) * a.stride), (short)0, rv ? (int)a.stride : 0, 0x00020000);
         for (int w4 = tid; 4 * w4 < nwords; w4 += T) {
-            u32x4 q;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int bit0 = (4 * w4 + u) * 32;
-                const int k0 = bit0 / bits;
-                const int k1 = min((bit0 + 31) / bits, n_pairs - 1);
-                uint32_t v = 0;
-                for (int k = k0; k <= k1; ++k) {
-                    const uint32_t val = idxrow[k];
-                    const int pos = k * bits - bit0;
-                    v |= (pos >= 0) ? (val << pos) : (val >> (-pos));
-                }
-                q[u] = v;
-            }
+            const u32x4 q = *reinterpret_cast<const u32x4*>(stage + 4 * w4);
             __builtin_amdgcn_raw_buffer_store_b128(q, crs, (uint32_t)w4 * 16u, 0, 0);
         }
     }
@@ -470,10 +496,9 @@ size_t encode_smem(int K, int R, int nwaves_total, int d_in) {
     using Lo = Layout<L>;
     int bits = 0;
     while ((1 << bits) < K) ++bits;
-    const size_t idx_stride = (size_t)((d_in / 2 + 7) & ~7);
     return search_lds_bytes(K, index_grid_size(bits)) + (size_t)R * kMaxWaves * sizeof(double) +
            (Lo::two_phase ? (size_t)nwaves_total * Lo::xbuf * sizeof(double) : 0) +
-           (size_t)R * idx_stride * sizeof(uint16_t);
+           (size_t)R * encode_group_bytes(d_in / 2, bits);
 }
 
 // R * kMaxWaves norm partials, then the exchange buffers (at least d_in/2 doubles: they also
@@ -584,7 +609,7 @@ size_t encode_lds_bytes(int L, int bits, int d_in) {
     const int nwaves = ((d_in / E) + kWave - 1) / kWave;
     const size_t xb = (L > 4) ? (size_t)nwaves * (kWave * (E / 2) + kWave) * sizeof(double) : 0;
     return search_lds_bytes(1 << bits, index_grid_size(bits)) + kMaxWaves * sizeof(double) + xb +
-           (size_t)((d_in / 2 + 7) & ~7) * sizeof(uint16_t);
+           encode_group_bytes(d_in / 2, bits);
 }
 
 int calib_groups(int n_rows) { return n_rows < kCalibMaxGroups ? n_rows : kCalibMaxGroups; }

@@ -57,14 +57,16 @@ struct SearchLds {
     uint16_t* order;   // codewords by decreasing norm
     uint8_t* fine;
     uint16_t* offs;
-    uint16_t* ent;
+    uint16_t* ent;     // candidate lists: byte offsets j * 8 into cb
     float R, inv_w;
     int W, G, K;
 };
 
+// The candidate lists in LDS hold byte offsets j * 8 of the codewords (K <= 4096 keeps them in
+// 16 bits) and are followed by kIndexCellCap zero entries, so a list can be read past its end.
 __host__ __device__ inline size_t search_lds_bytes(int K, int G) {
     return align16((size_t)K * 8) + align16((size_t)K * 2) + align16(kIndexFine) + align16((size_t)(G * G + 1) * 2) +
-           align16((size_t)index_lds_entries(K) * 2);
+           align16((size_t)(index_lds_entries(K) + kIndexCellCap) * 2);
 }
 
 template <int L>
@@ -188,7 +190,7 @@ __device__ inline void search_lds_fill(const SearchLds& s, const float* __restri
         uint32_t o = offs[c];
         s.offs[c] = (uint16_t)(o < (uint32_t)ne ? o : (uint32_t)ne);
     }
-    for (int e = tid; e < ne; e += nthreads) s.ent[e] = ent[e];
+    for (int e = tid; e < ne + kIndexCellCap; e += nthreads) s.ent[e] = e < ne ? (uint16_t)(ent[e] << 3) : (uint16_t)0;
 }
 
 // True when any active lane of the wavefront has a non-zero value.
@@ -201,7 +203,7 @@ __device__ __forceinline__ int nearest_exterior(float px, float py, const Search
     const float qx = fminf(fmaxf(px, -lim_in), lim_in), qy = fminf(fmaxf(py, -lim_in), lim_in);
     const int bx = min((int)((qx + s.R) * s.inv_w), s.W - 1), by = min((int)((qy + s.R) * s.inv_w), s.W - 1);
     const int cell = s.fine[by] * s.G + s.fine[bx];
-    const int a = (s.offs[cell + 1] > s.offs[cell]) ? s.ent[s.offs[cell]] : 0;
+    const int a = (s.offs[cell + 1] > s.offs[cell]) ? (s.ent[s.offs[cell]] >> 3) : 0;
     const float da = dist_f32(px, py, s.cb[a]);
     const double pn = __builtin_sqrt((double)px * px + (double)py * py);
     const double lim = pn - __builtin_sqrt((double)da * (1.0 + 1e-5));
@@ -243,7 +245,7 @@ __device__ __forceinline__ int nearest_lds(float px, float py, const SearchLds& 
             float bd = __builtin_inff();
             int bj = 0;
             for (int o = o0; o < o1; ++o) {
-                const int j = s.ent[o];
+                const int j = s.ent[o] >> 3;
                 eval_cw(px, py, s.cb[j], j, bd, bj);
             }
             return bj;
@@ -252,22 +254,32 @@ __device__ __forceinline__ int nearest_lds(float px, float py, const SearchLds& 
     return nearest_slow(px, py, s);
 }
 
-// NP points searched in lockstep: step t evaluates the t-th listed candidate of every point (the
-// last one again once a list is exhausted, which cannot change a strict-< argmin), so each step
-// issues NP independent LDS lookups.  Points outside the grid, in exhaustive cells or non-finite
-// take the single-point path afterwards, one point slot at a time (a uniform loop, so the slow
-// path exists once in the code).
+// Codeword at byte offset `off` of the LDS codebook.
+__device__ __forceinline__ float2 cw_at(const SearchLds& s, uint32_t off) {
+    return *reinterpret_cast<const float2*>(reinterpret_cast<const char*>(s.cb) + off);
+}
+
+// NP points searched in lockstep.  Step t evaluates entry o_i + t of every point's list.  The
+// loop runs until the longest list of the wavefront is done (a uniform loop) and reads shorter
+// lists past their end, into the following cells' lists and the zero padding: that is harmless,
+// because a list holds every codeword that can be nearest or tied anywhere in its cell, so an
+// extra codeword can neither be strictly closer nor tie with a lower index than the answer
+// (lists are in increasing index order and only a strictly smaller distance replaces the best).
+// Each step issues NP independent list loads, then NP codeword loads.  Points outside the grid,
+// in exhaustive cells or non-finite take the single-point path afterwards, one point slot at a
+// time (a uniform loop, so the slow path exists once in the code).
 template <int NP>
 __device__ __forceinline__ void nearest_lds_batch(const float (&px)[NP], const float (&py)[NP], const SearchLds& s,
                                                   int (&out)[NP]) {
-    int o[NP], last[NP];
+    const uint16_t* lp[NP];
     float bd[NP];
+    uint32_t bo[NP];
     uint32_t slow = 0;
     int steps = 0;
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
         bd[i] = __builtin_inff();
-        out[i] = 0;
+        bo[i] = 0;
         int o0 = 0, o1 = 0;   // empty: points outside the grid take the slow path
         if (fabsf(px[i]) < s.R && fabsf(py[i]) < s.R) {
             const int bx = min((int)((px[i] + s.R) * s.inv_w), s.W - 1);
@@ -279,19 +291,29 @@ __device__ __forceinline__ void nearest_lds_batch(const float (&px)[NP], const f
         if (o1 <= o0) {   // outside the grid, non-finite, or exhaustive cell
             slow |= 1u << i;
             o0 = 0;
-            o1 = 1;
+            o1 = 0;
         }
-        o[i] = o0;
-        last[i] = o1 - 1;
+        lp[i] = s.ent + o0;
         steps = max(steps, o1 - o0);
     }
-    for (int t = 0; t < steps; ++t) {
+    for (int t = 0; wave_any((uint32_t)(t < steps)); ++t) {
+        uint32_t off[NP];
+#pragma unroll
+        for (int i = 0; i < NP; ++i) off[i] = lp[i][t];
+        float2 c[NP];
+#pragma unroll
+        for (int i = 0; i < NP; ++i) c[i] = cw_at(s, off[i]);
 #pragma unroll
         for (int i = 0; i < NP; ++i) {
-            const int j = s.ent[min(o[i] + t, last[i])];
-            eval_cw(px[i], py[i], s.cb[j], j, bd[i], out[i]);
+            const float d = dist_f32(px[i], py[i], c[i]);
+            if (d < bd[i]) {
+                bd[i] = d;
+                bo[i] = off[i];
+            }
         }
     }
+#pragma unroll
+    for (int i = 0; i < NP; ++i) out[i] = (int)(bo[i] >> 3);
     if (wave_any(slow)) {
 #pragma unroll 1
         for (int i = 0; i < NP; ++i) {
