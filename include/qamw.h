@@ -116,9 +116,11 @@ int qamw_nearest(const float* d_points, int64_t n, const float* d_codebook, int3
  *   d_scale        d_in fp32 channel scales s_j > 0, or NULL for all ones.
  *   d_sign_bits    (d_in + 31) / 32 words of sign-mask bits, or NULL for all +1.
  *   block          Hadamard block size b: a power of two in [2, 1024] dividing d_in, or 0 for
- *                  qamw_default_block(d_in).  d_in must be even; d_in / E must be at most 1024
- *                  for E = 16 (b <= 128) and at most 512 for E = 32 (b = 256, 512) or E = 64
- *                  (b = 1024), i.e. d_in <= 16384, 16384 and 32768; else QAMW_ERR_UNSUPPORTED.
+ *                  qamw_default_block(d_in).  d_in must be even.  The kernels give each lane E
+ *                  consecutive columns (E = 16 for b <= 128, 32 for b = 256 or 512, 64 for
+ *                  b = 1024): d_in must be a multiple of E and d_in / E at most 1024 (E = 16)
+ *                  or 512 (E = 32, 64), i.e. d_in <= 16384, 16384 and 32768; otherwise
+ *                  QAMW_ERR_UNSUPPORTED.
  *   d_codebook, bits, d_index   K = 2^bits codebook and its index; 1 <= bits <= 12.
  *   d_sigma_in     d_in/2 fp32 per-pair scales to use, or NULL to calibrate (eq. 1):
  *                  sigma_k = fl32(mean |z_k| / sqrt(pi/2)), mean in double over the non-zero

@@ -85,6 +85,7 @@ def _dec(lib, **kw):
     (dict(index=None), ARG), (dict(codes=FAKE + 2), ARG), (dict(cb=FAKE + 4), ARG), (dict(w=FAKE + 1), ARG),
     (dict(sig_in=None, sig_out=FAKE, ws=None), WS), (dict(sig_in=None, sig_out=FAKE, ws=FAKE, ws_bytes=64), WS),
     (dict(d_in=16384 + 256, ld=16384 + 256, block=64), UNSUP), (dict(d_in=16384 + 256, ld=16640, block=256), UNSUP),
+    (dict(d_in=24, ld=24, block=8), UNSUP), (dict(d_in=8, ld=8, block=8), UNSUP),
 ])
 def test_encode_rejects(lib, kw, code):
     assert _enc(lib, **kw) == code
@@ -94,6 +95,7 @@ def test_encode_rejects(lib, kw, code):
     (dict(d_in=255), ARG), (dict(block=12), ARG), (dict(ld=255), ARG), (dict(ld=128), ARG), (dict(dt=3), ARG),
     (dict(bits=14), UNSUP), (dict(bits=0), ARG), (dict(codes=None), ARG), (dict(out=FAKE + 2), ARG),
     (dict(out=FAKE + 4, dt=q.F32), ARG), (dict(sigma=None), ARG), (dict(d_out=-3), ARG),
+    (dict(d_in=40, ld=40, block=8), UNSUP),
 ])
 def test_decode_rejects(lib, kw, code):
     assert _dec(lib, **kw) == code

@@ -325,6 +325,38 @@ __device__ __forceinline__ void load_raw_buf(const void* w, int64_t ld, int d_in
     }
 }
 
+// The same through 2- or 4-byte loads, for rows that are not 16-byte aligned.
+template <int E, bool BF>
+__device__ __forceinline__ void load_raw_buf_unaligned(const void* w, int64_t ld, int d_in, int d_out, int row,
+                                                       int tid, RawW<E, BF>& r) {
+    constexpr int ESZ = BF ? 2 : 4;
+    const bool ok = row < d_out;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(reinterpret_cast<const char*>(w) + (size_t)(ok ? row : 0) * (size_t)ld * ESZ), (short)0,
+        ok ? d_in * ESZ : 0, 0x00020000);
+    const uint32_t off = (uint32_t)tid * (uint32_t)(E * ESZ);
+    if constexpr (BF) {
+#pragma unroll
+        for (int m = 0; m < E / 2; ++m) {
+            const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(rs, off + 4u * m, 0, 0);
+            const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(rs, off + 4u * m + 2u, 0, 0);
+            r.u[m] = lo | (hi << 16);
+        }
+    } else {
+#pragma unroll
+        for (int m = 0; m < E; ++m) r.u[m] = __builtin_amdgcn_raw_buffer_load_b32(rs, off + 4u * m, 0, 0);
+    }
+}
+
+template <int E, bool BF, bool VEC>
+__device__ __forceinline__ void load_row_raw(const void* w, int64_t ld, int d_in, int d_out, int row, int tid,
+                                             RawW<E, BF>& r) {
+    if constexpr (VEC)
+        load_raw_buf<E, BF>(w, ld, d_in, d_out, row, tid, r);
+    else
+        load_raw_buf_unaligned<E, BF>(w, ld, d_in, d_out, row, tid, r);
+}
+
 // Encoder.  A workgroup runs R rows at a time (R groups of T lanes, T = lanes per row) over one
 // LDS image of the codebook and its search index; group g takes rows base + g for base = R *
 // blockIdx.x, R * (blockIdx.x + gridDim.x), ...  Every group runs every pass (a row past the end
@@ -332,6 +364,9 @@ __device__ __forceinline__ void load_raw_buf(const void* w, int64_t ld, int d_in
 // Per pass: front end (scale, norm, transform), pairs, lockstep search in batches of four pairs
 // per lane, indices to LDS, then the group packs its row into 16-byte words.
 constexpr int kSearchBatch = 4;
+// Threads per workgroup the encoder aims for (R rows of T lanes): 768 keeps the kernel within
+// 170 VGPRs (three wavefronts per SIMD) without spills.
+constexpr int kEncodeMaxThreads = 768;
 
 // LDS bytes per row group of the encoder: the indices (u16, zero-padded to a multiple of 32) and
 // the packed words, which cover whole 32-index chunks and at least the row stride.
@@ -343,7 +378,7 @@ __host__ __device__ inline size_t encode_group_bytes(int n_pairs, int bits) {
     return idx_stride * 2 + stage;
 }
 
-template <int L, int MAXT, bool BF>
+template <int L, int MAXT, bool BF, bool VEC>
 __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a, int T, int R) {
     using Lo = Layout<L>;
     constexpr int E = Lo::E, NP = E / 2;
@@ -373,16 +408,14 @@ __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a, int T, int R) {
 
     const int units = a.d_in / E;
     const bool active = tid < units;
-    const bool vec = (((uintptr_t)a.w & 15) == 0) && (((a.ld * (BF ? 2 : 4)) & 15) == 0);
     const int rstride = gridDim.x * R;
     int base = blockIdx.x * R;
 
+    // Every VMEM access of the row loop is unconditional (out-of-range lanes and rows use offsets
+    // or descriptors outside their buffers: loads return 0, stores are dropped), so the wait for
+    // the prefetched row can leave the previous row's stores in flight.
     RawW<E, BF> nxt;
-    if (vec) {
-        load_raw_buf<E, BF>(a.w, a.ld, a.d_in, a.d_out, base + grp, tid, nxt);
-    } else if (active && base + grp < a.d_out) {
-        load_raw<E, BF>(a.w, false, (int64_t)(base + grp) * a.ld + (int64_t)tid * E, nxt);
-    }
+    load_row_raw<E, BF, VEC>(a.w, a.ld, a.d_in, a.d_out, base + grp, tid, nxt);
     search_lds_fill(sl, a.cb, K, index, threadIdx.x, blockDim.x);
 
     int32_t flags = 0;
@@ -401,17 +434,15 @@ __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a, int T, int R) {
     const double inv_sqrt_b = 1.0 / __builtin_sqrt((double)Lo::b);
     const int bits = a.bits;
     const int nwords = (int)(a.stride / 4);
+    const __amdgpu_buffer_rsrc_t nrs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)a.norm, (short)0, a.d_out * 2, 0x00020000);
     __syncthreads();
 
     for (; base < a.d_out; base += rstride) {
         const int row = base + grp;
         const bool rv = row < a.d_out;
         const RawW<E, BF> cur = nxt;
-        if (vec) {   // keep the next row in flight
-            load_raw_buf<E, BF>(a.w, a.ld, a.d_in, a.d_out, row + rstride, tid, nxt);
-        } else if (active && row + rstride < a.d_out) {
-            load_raw<E, BF>(a.w, false, (int64_t)(row + rstride) * a.ld + (int64_t)tid * E, nxt);
-        }
+        load_row_raw<E, BF, VEC>(a.w, a.ld, a.d_in, a.d_out, row + rstride, tid, nxt);   // next row in flight
         double x[E];
         int32_t rf = 0;
         const double r2 = front_end<L, BF>(cur, active && rv, tid, cf, x, red, xb, nwaves, rf);
@@ -442,14 +473,14 @@ __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a, int T, int R) {
                     idxrow_l[(h * kSearchBatch + i) * (Lo::two_phase ? Lo::lanes : 1)] = nonzero ? (uint16_t)bi[i] : (uint16_t)0;
             }
         }
-        if (tid == 0 && rv) {
+        {   // the norm, stored by lane 0 of the group
             uint16_t nh = 0;
             if (nonzero) {
                 __half hv = __float2half_rn((float)r);
                 nh = __half_as_ushort(hv);
-                if ((nh & 0x7FFF) == 0x7C00) rf |= 4;
+                if (tid == 0 && (nh & 0x7FFF) == 0x7C00) rf |= 4;
             }
-            a.norm[row] = nh;
+            __builtin_amdgcn_raw_buffer_store_b16(nh, nrs, tid == 0 ? (uint32_t)row * 2u : 0x7FFFFFF0u, 0, 0);
         }
         if (rv) flags |= rf;
         __syncthreads();
@@ -478,12 +509,17 @@ __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a, int T, int R) {
         }
         for (int wd = nchunks * bits + tid; wd < nwords; wd += T) stage[wd] = 0;   // row padding
         __syncthreads();
-        // 16-byte stores of the staged row
+        // 16-byte stores of the staged row: thread t stores chunks t, t + T, ...  A row has at most
+        // ceil(3 d_in / 64) chunks (12 bits per pair) and T >= d_in / E lanes, so NCH = ceil(3E/64)
+        // stores per thread cover it; the ones past the row are dropped.
         const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(a.codes + (size_t)(rv ? row : 0) * a.stride), (short)0, rv ? (int)a.stride : 0, 0x00020000);
-        for (int w4 = tid; 4 * w4 < nwords; w4 += T) {
-            const u32x4 q = *reinterpret_cast<const u32x4*>(stage + 4 * w4);
-            __builtin_amdgcn_raw_buffer_store_b128(q, crs, (uint32_t)w4 * 16u, 0, 0);
+        constexpr int NCH = (3 * E + 63) / 64;
+#pragma unroll
+        for (int u = 0; u < NCH; ++u) {
+            const int c = tid + u * T;
+            const u32x4 q = *reinterpret_cast<const u32x4*>(stage + 4 * min(c, nwords / 4 - 1));
+            __builtin_amdgcn_raw_buffer_store_b128(q, crs, 4 * c < nwords ? (uint32_t)c * 16u : 0x7FFFFFF0u, 0, 0);
         }
     }
     flag_status(a.status, flags);
@@ -511,14 +547,14 @@ size_t calib_smem(int R, int nwaves) {
     return (size_t)R * kMaxWaves * sizeof(double) + (xb > comb ? xb : comb);
 }
 
-template <int L, bool BF>
-hipError_t encode_LB(const EncodeArgs& a, hipStream_t st) {
+template <int L, bool BF, bool VEC>
+hipError_t encode_LBV(const EncodeArgs& a, hipStream_t st) {
     using Lo = Layout<L>;
-    constexpr int kMax = L <= 7 ? 1024 : 512;
+    constexpr int kMax = L <= 7 ? kEncodeMaxThreads : 512;
     const int T = ((a.d_in / Lo::E) + kWave - 1) / kWave * kWave;
-    if (T > kMax) return hipErrorInvalidConfiguration;
+    if (T > 1024 || (T > 512 && L > 7)) return hipErrorInvalidConfiguration;
     const int K = 1 << a.bits;
-    int R = kMax / T;
+    int R = T >= kMax ? 1 : kMax / T;
     if (R > 4) R = 4;
     if (R > a.d_out) R = a.d_out > 0 ? a.d_out : 1;
     while (R > 1 && encode_smem<L>(K, R, R * T / kWave, a.d_in) > kLdsBytes) --R;
@@ -533,15 +569,26 @@ hipError_t encode_LB(const EncodeArgs& a, hipStream_t st) {
     if (grid > need) grid = need;
     if (grid < 1) return hipSuccess;
     if (threads <= 512) {
-        allow_lds(k_encode<L, 512, BF>, smem);
-        hipLaunchKernelGGL((k_encode<L, 512, BF>), dim3(grid), dim3(threads), smem, st, a, T, R);
+        allow_lds(k_encode<L, 512, BF, VEC>, smem);
+        hipLaunchKernelGGL((k_encode<L, 512, BF, VEC>), dim3(grid), dim3(threads), smem, st, a, T, R);
     } else if constexpr (L <= 7) {
-        allow_lds(k_encode<L, 1024, BF>, smem);
-        hipLaunchKernelGGL((k_encode<L, 1024, BF>), dim3(grid), dim3(threads), smem, st, a, T, R);
+        if (threads <= 768) {
+            allow_lds(k_encode<L, 768, BF, VEC>, smem);
+            hipLaunchKernelGGL((k_encode<L, 768, BF, VEC>), dim3(grid), dim3(threads), smem, st, a, T, R);
+        } else {
+            allow_lds(k_encode<L, 1024, BF, VEC>, smem);
+            hipLaunchKernelGGL((k_encode<L, 1024, BF, VEC>), dim3(grid), dim3(threads), smem, st, a, T, R);
+        }
     } else {
         return hipErrorInvalidConfiguration;
     }
     return hipGetLastError();
+}
+
+template <int L, bool BF>
+hipError_t encode_LB(const EncodeArgs& a, hipStream_t st) {
+    const bool vec = (((uintptr_t)a.w & 15) == 0) && (((a.ld * (BF ? 2 : 4)) & 15) == 0);
+    return vec ? encode_LBV<L, BF, true>(a, st) : encode_LBV<L, BF, false>(a, st);
 }
 
 template <int L, bool BF>

@@ -27,8 +27,9 @@ int check_shape(int32_t d_in, int32_t block) {
     if (b < 2 || b > 1024 || !is_pow2(b) || d_in % b) return QAMW_ERR_ARG;
     int L = log2i(b);
     int E = lane_elems(L);
-    // one lane per E columns, one workgroup per row: at most 1024 lanes (512 when E >= 32)
-    if (E <= 0 || d_in / E > (E >= 32 ? 512 : 1024)) return QAMW_ERR_UNSUPPORTED;
+    // one lane per E columns (whole lanes only), one workgroup per row: at most 1024 lanes (512
+    // when E >= 32)
+    if (E <= 0 || d_in % E || d_in / E > (E >= 32 ? 512 : 1024)) return QAMW_ERR_UNSUPPORTED;
     return L;
 }
 
