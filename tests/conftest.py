@@ -29,3 +29,13 @@ def synth():
     import synth_inputs
     synth_inputs.build()
     return synth_inputs
+
+
+@pytest.fixture(scope="session")
+def q():
+    """The HIP library through its binding (GPU tests only)."""
+    import torch
+    import weight_quantization_codec_amd as qamw
+    qamw.load()
+    assert torch.cuda.is_available()
+    return qamw

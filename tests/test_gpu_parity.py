@@ -19,14 +19,6 @@ pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 
-@pytest.fixture(scope="module")
-def q():
-    import weight_quantization_codec_amd as q
-    q.load()
-    assert torch.cuda.is_available()
-    return q
-
-
 def golden_cb(name):
     z = np.load(os.path.join(GOLDEN, name + ".npz"))
     return z["codebook"], z["trace"], z["meta"]

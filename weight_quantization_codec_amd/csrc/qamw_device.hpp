@@ -23,6 +23,7 @@ constexpr int kIndexFine = 2048;                          // W: fine bins per ax
 constexpr int kIndexFineMax = 2048;
 constexpr int kIndexGMax = 64;                            // cells per axis, at most
 constexpr int kIndexCellCap = 64;                         // longer lists: cell searched exhaustively
+constexpr int kIndexListPad = kIndexCellCap + 8;          // LDS entries after the lists (over-reads)
 constexpr int kIndexMaxEntries = 24576;                   // candidate-list budget (u16 entries)
 constexpr int kIndexHeaderBytes = 256;
 constexpr int kIndexFineOff = 256;                        // u8[W]   fine bin -> cell
@@ -54,19 +55,21 @@ __host__ __device__ constexpr size_t align16(size_t v) { return (v + 15) & ~(siz
 // LDS image of the codebook and its index used by the search.
 struct SearchLds {
     float2* cb;
+    uint32_t cb_lds;   // LDS byte address of cb (the lists hold cb_lds + 8 j)
     uint16_t* order;   // codewords by decreasing norm
     uint8_t* fine;
     uint16_t* offs;
-    uint16_t* ent;     // candidate lists: byte offsets j * 8 into cb
+    uint16_t* ent;     // candidate lists: LDS byte addresses cb_lds + 8 j of the codewords
     float R, inv_w;
     int W, G, K;
 };
 
-// The candidate lists in LDS hold byte offsets j * 8 of the codewords (K <= 4096 keeps them in
-// 16 bits) and are followed by kIndexCellCap zero entries, so a list can be read past its end.
+// The candidate lists in LDS hold the LDS byte addresses of their codewords (the image starts
+// low in LDS and K <= 4096, so they fit in 16 bits) and are followed by kIndexListPad entries
+// naming codeword 0, so a list can be read past its end.
 __host__ __device__ inline size_t search_lds_bytes(int K, int G) {
     return align16((size_t)K * 8) + align16((size_t)K * 2) + align16(kIndexFine) + align16((size_t)(G * G + 1) * 2) +
-           align16((size_t)(index_lds_entries(K) + kIndexCellCap) * 2);
+           align16((size_t)(index_lds_entries(K) + kIndexListPad) * 2);
 }
 
 template <int L>
@@ -155,6 +158,7 @@ __device__ inline SearchLds search_lds_carve(char* smem, int K, const IndexHeade
     SearchLds s;
     char* p = smem;
     s.cb = reinterpret_cast<float2*>(p);
+    s.cb_lds = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)p);   // LDS offset
     p += align16((size_t)K * 8);
     s.order = reinterpret_cast<uint16_t*>(p);
     p += align16((size_t)K * 2);
@@ -190,7 +194,8 @@ __device__ inline void search_lds_fill(const SearchLds& s, const float* __restri
         uint32_t o = offs[c];
         s.offs[c] = (uint16_t)(o < (uint32_t)ne ? o : (uint32_t)ne);
     }
-    for (int e = tid; e < ne + kIndexCellCap; e += nthreads) s.ent[e] = e < ne ? (uint16_t)(ent[e] << 3) : (uint16_t)0;
+    for (int e = tid; e < ne + kIndexListPad; e += nthreads)
+        s.ent[e] = (uint16_t)(s.cb_lds + (e < ne ? 8u * ent[e] : 0u));
 }
 
 // True when any active lane of the wavefront has a non-zero value.
@@ -203,7 +208,7 @@ __device__ __forceinline__ int nearest_exterior(float px, float py, const Search
     const float qx = fminf(fmaxf(px, -lim_in), lim_in), qy = fminf(fmaxf(py, -lim_in), lim_in);
     const int bx = min((int)((qx + s.R) * s.inv_w), s.W - 1), by = min((int)((qy + s.R) * s.inv_w), s.W - 1);
     const int cell = s.fine[by] * s.G + s.fine[bx];
-    const int a = (s.offs[cell + 1] > s.offs[cell]) ? (s.ent[s.offs[cell]] >> 3) : 0;
+    const int a = (s.offs[cell + 1] > s.offs[cell]) ? (int)((s.ent[s.offs[cell]] - s.cb_lds) >> 3) : 0;
     const float da = dist_f32(px, py, s.cb[a]);
     const double pn = __builtin_sqrt((double)px * px + (double)py * py);
     const double lim = pn - __builtin_sqrt((double)da * (1.0 + 1e-5));
@@ -245,7 +250,7 @@ __device__ __forceinline__ int nearest_lds(float px, float py, const SearchLds& 
             float bd = __builtin_inff();
             int bj = 0;
             for (int o = o0; o < o1; ++o) {
-                const int j = s.ent[o] >> 3;
+                const int j = (int)((s.ent[o] - s.cb_lds) >> 3);
                 eval_cw(px, py, s.cb[j], j, bd, bj);
             }
             return bj;
@@ -254,9 +259,11 @@ __device__ __forceinline__ int nearest_lds(float px, float py, const SearchLds& 
     return nearest_slow(px, py, s);
 }
 
-// Codeword at byte offset `off` of the LDS codebook.
-__device__ __forceinline__ float2 cw_at(const SearchLds& s, uint32_t off) {
-    return *reinterpret_cast<const float2*>(reinterpret_cast<const char*>(s.cb) + off);
+// Codeword at LDS byte address `addr`.
+typedef float lds_f2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float2 cw_at(uint32_t addr) {
+    const lds_f2 v = *(const __attribute__((address_space(3))) lds_f2*)(addr);
+    return make_float2(v.x, v.y);
 }
 
 // NP points searched in lockstep.  Step t evaluates entry o_i + t of every point's list.  The
@@ -279,7 +286,7 @@ __device__ __forceinline__ void nearest_lds_batch(const float (&px)[NP], const f
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
         bd[i] = __builtin_inff();
-        bo[i] = 0;
+        bo[i] = s.cb_lds;
         int o0 = 0, o1 = 0;   // empty: points outside the grid take the slow path
         if (fabsf(px[i]) < s.R && fabsf(py[i]) < s.R) {
             const int bx = min((int)((px[i] + s.R) * s.inv_w), s.W - 1);
@@ -297,23 +304,23 @@ __device__ __forceinline__ void nearest_lds_batch(const float (&px)[NP], const f
         steps = max(steps, o1 - o0);
     }
     for (int t = 0; wave_any((uint32_t)(t < steps)); ++t) {
-        uint32_t off[NP];
+        uint32_t ad[NP];
 #pragma unroll
-        for (int i = 0; i < NP; ++i) off[i] = lp[i][t];
+        for (int i = 0; i < NP; ++i) ad[i] = lp[i][t];
         float2 c[NP];
 #pragma unroll
-        for (int i = 0; i < NP; ++i) c[i] = cw_at(s, off[i]);
+        for (int i = 0; i < NP; ++i) c[i] = cw_at(ad[i]);
 #pragma unroll
         for (int i = 0; i < NP; ++i) {
             const float d = dist_f32(px[i], py[i], c[i]);
             if (d < bd[i]) {
                 bd[i] = d;
-                bo[i] = off[i];
+                bo[i] = ad[i];
             }
         }
     }
 #pragma unroll
-    for (int i = 0; i < NP; ++i) out[i] = (int)(bo[i] >> 3);
+    for (int i = 0; i < NP; ++i) out[i] = (int)((bo[i] - s.cb_lds) >> 3);
     if (wave_any(slow)) {
 #pragma unroll 1
         for (int i = 0; i < NP; ++i) {
