@@ -388,7 +388,7 @@ __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a, int T, int R) {
     const int tid = threadIdx.x - grp * T, nwaves = T / kWave;
     const char* index = reinterpret_cast<const char*>(a.index);
     const IndexHeader ih = *reinterpret_cast<const IndexHeader*>(index);
-    const SearchLds sl = search_lds_carve(smem, K, ih);
+    const SearchLds sl = search_lds_carve(smem, K, ih, index);
     double* red_all = reinterpret_cast<double*>(smem + search_lds_bytes(K, ih.G));
     double* red = red_all + grp * kMaxWaves;
     double* xb_all = red_all + R * kMaxWaves;
@@ -398,7 +398,9 @@ __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a, int T, int R) {
     // words (the row stride, a multiple of 16 bytes)
     const int idx_stride = (n_pairs + 31) & ~31;
     const int grp_bytes = (int)encode_group_bytes(n_pairs, a.bits);
-    char* gbuf = reinterpret_cast<char*>(xb_all + (Lo::two_phase ? (R * T / kWave) * Lo::xbuf : 0)) + grp * grp_bytes;
+    // the group buffers share LDS with the exchange buffers: they are used between the end of the
+    // front end (a workgroup barrier) and the end of the pass (another barrier)
+    char* gbuf = reinterpret_cast<char*>(xb_all) + grp * grp_bytes;
     uint16_t* idxrow = reinterpret_cast<uint16_t*>(gbuf);
     uint32_t* stage = reinterpret_cast<uint32_t*>(gbuf + idx_stride * 2);
     for (int k = n_pairs + tid; k < idx_stride; k += T) idxrow[k] = 0;   // never written again
@@ -521,20 +523,21 @@ __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a, int T, int R) {
             const u32x4 q = *reinterpret_cast<const u32x4*>(stage + 4 * min(c, nwords / 4 - 1));
             __builtin_amdgcn_raw_buffer_store_b128(q, crs, 4 * c < nwords ? (uint32_t)c * 16u : 0x7FFFFFF0u, 0, 0);
         }
+        __syncthreads();   // the staged words are read before the next pass reuses the LDS
     }
     flag_status(a.status, flags);
 }
 
-// LDS of the encoder: search image, R * kMaxWaves norm partials, one exchange buffer per
-// wavefront, and R rows of indices.
+// LDS of the encoder: search image, R * kMaxWaves norm partials, and one region holding either
+// the exchange buffers (one per wavefront) or the R groups' indices and packed words.
 template <int L>
 size_t encode_smem(int K, int R, int nwaves_total, int d_in) {
     using Lo = Layout<L>;
     int bits = 0;
     while ((1 << bits) < K) ++bits;
-    return search_lds_bytes(K, index_grid_size(bits)) + (size_t)R * kMaxWaves * sizeof(double) +
-           (Lo::two_phase ? (size_t)nwaves_total * Lo::xbuf * sizeof(double) : 0) +
-           (size_t)R * encode_group_bytes(d_in / 2, bits);
+    const size_t xb = Lo::two_phase ? (size_t)nwaves_total * Lo::xbuf * sizeof(double) : 0;
+    const size_t grp = (size_t)R * encode_group_bytes(d_in / 2, bits);
+    return search_lds_bytes(K, index_grid_size(bits)) + (size_t)R * kMaxWaves * sizeof(double) + (xb > grp ? xb : grp);
 }
 
 // R * kMaxWaves norm partials, then the exchange buffers (at least d_in/2 doubles: they also
@@ -655,8 +658,8 @@ size_t encode_lds_bytes(int L, int bits, int d_in) {
     if (E <= 0) return 0;
     const int nwaves = ((d_in / E) + kWave - 1) / kWave;
     const size_t xb = (L > 4) ? (size_t)nwaves * (kWave * (E / 2) + kWave) * sizeof(double) : 0;
-    return search_lds_bytes(1 << bits, index_grid_size(bits)) + kMaxWaves * sizeof(double) + xb +
-           encode_group_bytes(d_in / 2, bits);
+    const size_t grp = encode_group_bytes(d_in / 2, bits);
+    return search_lds_bytes(1 << bits, index_grid_size(bits)) + kMaxWaves * sizeof(double) + (xb > grp ? xb : grp);
 }
 
 int calib_groups(int n_rows) { return n_rows < kCalibMaxGroups ? n_rows : kCalibMaxGroups; }

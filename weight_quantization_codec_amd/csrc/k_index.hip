@@ -1,10 +1,11 @@
 // Search index for the nearest-codeword step (paper section 3.6: each normalized pair maps to
 // its Euclidean-nearest codebook entry), built on the GPU once per codebook.
 //
-// Grid.  A G x G grid over [-Rg, Rg]^2, Rg = 1.5 max_j max(|c_jx|, |c_jy|), whose cell edges sit
+// Grid.  A G x G grid over [-Rg, Rg]^2, Rg = 2.5 max_j max(|c_jx|, |c_jy|), whose cell edges sit
 // at quantiles of the codeword coordinates (both axes share one set of edges): a point is
 // located by a uniform fine bin (W bins over [-Rg, Rg]) and a table fine bin -> cell, so that
-// every cell holds about one codeword wherever the codebook is dense or sparse.
+// cells are equally fine, relative to the codeword spacing, wherever the codebook is dense or
+// sparse (G = 2.12 sqrt(K): a few cells per codeword, short candidate lists).
 //
 // Candidates.  Codeword j is listed for cell Q when its Voronoi region, widened to absorb fp32
 // distance rounding, meets Q widened by 1e-3 of a fine bin (the lookup's own rounding):
@@ -16,7 +17,9 @@
 // codeword outside the list can neither beat nor tie the listed ones in fp32: the fp32 argmin
 // over the list, ties to the lowest index (lists are in increasing index order), equals the
 // argmin over all K codewords.  Points outside the grid use a scan in decreasing |c| that stops
-// once |p| - |c| exceeds the distance to a known codeword (plus a 1e-5 margin).
+// once |p| - |c| exceeds the distance to a known codeword (plus a 1e-5 margin); with Rg at 2.5
+// times the codebook's extent such points do not occur for calibrated data (a Gaussian
+// coordinate beyond 9 sigma), so that path only has to be correct, not fast.
 #include <cmath>
 
 #include "qamw_device.hpp"
@@ -128,7 +131,7 @@ __global__ __launch_bounds__(1024) void k_ix_grid(const float* __restrict__ cb, 
         if (tid < s) red[tid] = fmaxf(red[tid], red[tid + s]);
         __syncthreads();
     }
-    float R = 1.5f * red[0];
+    float R = 2.5f * red[0];
     if (!(R >= 1e-3f) || !(R < 1e30f)) R = 1.0f;
     const float inv_w = (float)W / (2.0f * R);
     for (int j = tid; j < 2 * K; j += blockDim.x) {
@@ -272,8 +275,12 @@ __global__ __launch_bounds__(256) void k_ix_order(const float* __restrict__ cb, 
 }  // namespace
 
 int index_grid_size(int bits) {
-    // about one codeword per cell
-    int G = (int)std::lround(1.07 * std::sqrt((double)(1 << bits)));
+    // G = 2.12 sqrt(K): about 4.5 cells per codeword, so a point's list holds 2.5 codewords on
+    // average and at most about 7 (Gaussian-trained codebooks); K = 4096 uses G = 64 to keep the
+    // LDS image (codebook, offsets, lists) below about 90 KiB.
+    const int K = 1 << bits;
+    if (K >= 4096) return 64;
+    int G = (int)std::lround(2.12 * std::sqrt((double)K));
     return G < 4 ? 4 : (G > kIndexGMax ? kIndexGMax : G);
 }
 
@@ -300,7 +307,7 @@ namespace {
 __global__ __launch_bounds__(256) void k_nearest(const float* __restrict__ pts, int64_t n, const float* __restrict__ cb,
                                                  int K, const char* __restrict__ index, int32_t* __restrict__ out) {
     extern __shared__ __align__(16) char smem[];
-    SearchLds s = search_lds_carve(smem, K, *reinterpret_cast<const IndexHeader*>(index));
+    SearchLds s = search_lds_carve(smem, K, *reinterpret_cast<const IndexHeader*>(index), index);
     search_lds_fill(s, cb, K, index, threadIdx.x, blockDim.x);
     __syncthreads();
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {

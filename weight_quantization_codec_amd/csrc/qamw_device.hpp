@@ -21,17 +21,17 @@ constexpr int kWave = 64;
 // Search-index layout (bytes from the start of the index buffer written by qamw_codebook_index).
 constexpr int kIndexFine = 2048;                          // W: fine bins per axis
 constexpr int kIndexFineMax = 2048;
-constexpr int kIndexGMax = 64;                            // cells per axis, at most
+constexpr int kIndexGMax = 128;                           // cells per axis, at most
 constexpr int kIndexCellCap = 64;                         // longer lists: cell searched exhaustively
 constexpr int kIndexListPad = kIndexCellCap + 8;          // LDS entries after the lists (over-reads)
-constexpr int kIndexMaxEntries = 24576;                   // candidate-list budget (u16 entries)
+constexpr int kIndexMaxEntries = 40960;                   // candidate-list capacity (u16 entries)
 constexpr int kIndexHeaderBytes = 256;
-constexpr int kIndexFineOff = 256;                        // u8[W]   fine bin -> cell
-constexpr int kIndexEdgeOff = kIndexFineOff + 2048;       // u16[G+1] first fine bin of each cell
-constexpr int kIndexOvfOff = kIndexEdgeOff + 256;         // u8[G*G] overflow flags
-constexpr int kIndexOrderOff = kIndexOvfOff + 4096;       // u16[K]  codewords by decreasing norm
-constexpr int kIndexOffsOff = kIndexOrderOff + 8192;      // u32[G*G+1] list offsets
-constexpr int kIndexEntOff = kIndexOffsOff + 16384 + 256; // u16[]    candidate lists
+constexpr int kIndexFineOff = 256;                                    // u8[W]      fine bin -> cell
+constexpr int kIndexEdgeOff = kIndexFineOff + kIndexFine;             // u16[G+1]   first fine bin of each cell
+constexpr int kIndexOvfOff = kIndexEdgeOff + 512;                     // u8[G*G]    overflow flags
+constexpr int kIndexOrderOff = kIndexOvfOff + kIndexGMax * kIndexGMax; // u16[K]     codewords by decreasing norm
+constexpr int kIndexOffsOff = kIndexOrderOff + 8192;                  // u32[G*G+1] list offsets
+constexpr int kIndexEntOff = kIndexOffsOff + 4 * kIndexGMax * kIndexGMax + 256;   // u16[] candidate lists
 
 struct IndexHeader {
     int32_t K;
@@ -44,10 +44,12 @@ struct IndexHeader {
     int32_t overflow; // cells searched exhaustively
 };
 
-// Candidate-list entries kept in LDS for a 2^bits codebook: enough for Gaussian-trained
-// codebooks (about 5 per cell); a codebook needing more gets exhaustive cells instead.
+// Candidate-list entries kept in LDS for a K-entry codebook.  With G = 2.12 sqrt(K) cells per
+// axis a Gaussian-trained codebook lists about 11.5 K entries (2.5 per point on average);
+// K = 4096 uses a coarser grid (G = 64, about 5 K entries) to stay within LDS.  A codebook that
+// needs more gets exhaustive cells instead (at the far end of the grid's scan order).
 __host__ __device__ constexpr int index_lds_entries(int K) {
-    return (6 * K < kIndexMaxEntries) ? (6 * K < 64 ? 64 : 6 * K) : kIndexMaxEntries;
+    return K >= 4096 ? 22528 : (12 * K < 64 ? 64 : 12 * K);
 }
 
 __host__ __device__ constexpr size_t align16(size_t v) { return (v + 15) & ~(size_t)15; }
@@ -56,7 +58,7 @@ __host__ __device__ constexpr size_t align16(size_t v) { return (v + 15) & ~(siz
 struct SearchLds {
     float2* cb;
     uint32_t cb_lds;   // LDS byte address of cb (the lists hold cb_lds + 8 j)
-    uint16_t* order;   // codewords by decreasing norm
+    const uint16_t* order;   // codewords by decreasing norm (global memory: exterior points only)
     uint8_t* fine;
     uint16_t* offs;
     uint16_t* ent;     // candidate lists: LDS byte addresses cb_lds + 8 j of the codewords
@@ -68,7 +70,7 @@ struct SearchLds {
 // low in LDS and K <= 4096, so they fit in 16 bits) and are followed by kIndexListPad entries
 // naming codeword 0, so a list can be read past its end.
 __host__ __device__ inline size_t search_lds_bytes(int K, int G) {
-    return align16((size_t)K * 8) + align16((size_t)K * 2) + align16(kIndexFine) + align16((size_t)(G * G + 1) * 2) +
+    return align16((size_t)K * 8) + align16(kIndexFine) + align16((size_t)(G * G + 1) * 2) +
            align16((size_t)(index_lds_entries(K) + kIndexListPad) * 2);
 }
 
@@ -154,14 +156,13 @@ __device__ __forceinline__ void eval_cw(float px, float py, float2 c, int j, flo
     }
 }
 
-__device__ inline SearchLds search_lds_carve(char* smem, int K, const IndexHeader& ih) {
+__device__ inline SearchLds search_lds_carve(char* smem, int K, const IndexHeader& ih, const char* index) {
     SearchLds s;
     char* p = smem;
     s.cb = reinterpret_cast<float2*>(p);
     s.cb_lds = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)p);   // LDS offset
     p += align16((size_t)K * 8);
-    s.order = reinterpret_cast<uint16_t*>(p);
-    p += align16((size_t)K * 2);
+    s.order = reinterpret_cast<const uint16_t*>(index + kIndexOrderOff);
     s.fine = reinterpret_cast<uint8_t*>(p);
     p += align16(kIndexFine);
     s.offs = reinterpret_cast<uint16_t*>(p);
@@ -183,11 +184,7 @@ __device__ inline void search_lds_fill(const SearchLds& s, const float* __restri
     const uint16_t* ent = reinterpret_cast<const uint16_t*>(index + kIndexEntOff);
     const uint8_t* fine = reinterpret_cast<const uint8_t*>(index + kIndexFineOff);
     const int ne = min(ih.n_entries, index_lds_entries(K));   // the builder keeps n_entries within this
-    const uint16_t* order = reinterpret_cast<const uint16_t*>(index + kIndexOrderOff);
-    for (int j = tid; j < K; j += nthreads) {
-        s.cb[j] = reinterpret_cast<const float2*>(cb)[j];
-        s.order[j] = order[j];
-    }
+    for (int j = tid; j < K; j += nthreads) s.cb[j] = reinterpret_cast<const float2*>(cb)[j];
     for (int b = tid; b < s.W; b += nthreads) s.fine[b] = fine[b];
     const int cells = s.G * s.G;
     for (int c = tid; c <= cells; c += nthreads) {
@@ -262,7 +259,7 @@ __device__ __forceinline__ int nearest_lds(float px, float py, const SearchLds& 
 // Codeword at LDS byte address `addr`.
 typedef float lds_f2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float2 cw_at(uint32_t addr) {
-    const lds_f2 v = *(const __attribute__((address_space(3))) lds_f2*)(addr);
+    const lds_f2 v = *(const __attribute__((address_space(3))) lds_f2*)(size_t)addr;
     return make_float2(v.x, v.y);
 }
 
