@@ -256,24 +256,25 @@ __global__ __launch_bounds__(MAXT) void k_calibrate(CalibArgs a, int T, int R) {
     }
 }
 
-// sigma_k from the per-group sums.  A block owns 64 pairs; each pair's groups are split into 16
-// contiguous runs, one per thread, every thread adds its run in increasing group order, and the
-// 16 run sums are added in run order, so the result does not depend on scheduling.  The count of
-// non-zero rows is reduced by the whole block.
-constexpr int kFinishParts = 16;
+// sigma_k from the per-group sums.  A block of 1024 threads owns kFinishPairs pairs; each pair's
+// groups are split into kFinishParts contiguous runs, one per thread, every thread adds its run in
+// increasing group order, and the run sums are added in run order, so the result does not depend
+// on scheduling.  The count of non-zero rows is reduced by the whole block.
+constexpr int kFinishParts = 32;
+constexpr int kFinishPairs = 1024 / kFinishParts;
 __global__ __launch_bounds__(1024) void k_calibrate_finish(const double* __restrict__ partial,
                                                            const int32_t* __restrict__ nzs, int n_groups, int n_pairs,
                                                            int d_in, float* __restrict__ sigma) {
-    __shared__ double part[kFinishParts][64];
+    __shared__ double part[kFinishParts][kFinishPairs];
     __shared__ int64_t nzw[1024 / kWave];
-    const int kl = threadIdx.x & 63, q = threadIdx.x >> 6;
-    const int k = blockIdx.x * 64 + kl;
+    const int kl = threadIdx.x % kFinishPairs, q = threadIdx.x / kFinishPairs;
+    const int k = blockIdx.x * kFinishPairs + kl;
     // rows counted by the groups (each thread at most one group per pass)
     int64_t nn = 0;
     for (int g = threadIdx.x; g < n_groups; g += blockDim.x) nn += nzs[g];
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) nn += __shfl_xor(nn, off, kWave);
-    if (kl == 0) nzw[q] = nn;
+    if ((threadIdx.x & (kWave - 1)) == 0) nzw[threadIdx.x / kWave] = nn;
     double s = 0.0;
     if (k < n_pairs) {
         const int per = (n_groups + kFinishParts - 1) / kFinishParts;
@@ -620,7 +621,7 @@ hipError_t calibrate_LB(const CalibArgs& a, float* sigma, hipStream_t st) {
         }
     }
     int n_pairs = a.d_in / 2;
-    hipLaunchKernelGGL(k_calibrate_finish, dim3((n_pairs + 63) / 64), dim3(64 * kFinishParts), 0, st, a.partial, a.nz,
+    hipLaunchKernelGGL(k_calibrate_finish, dim3((n_pairs + kFinishPairs - 1) / kFinishPairs), dim3(1024), 0, st, a.partial, a.nz,
                        groups, n_pairs, a.d_in, sigma);
     return hipGetLastError();
 }
