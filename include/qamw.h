@@ -93,6 +93,9 @@ int qamw_codebook_train(const float* d_points, int64_t n_points, int32_t bits, i
  * codebook's extent; each cell lists, in increasing order, every codeword that can be the
  * nearest (or tied nearest) to a point of the cell, with a margin that covers fp32 rounding,
  * so searching a cell's list returns exactly what a search over all K codewords returns.
+ * The index also holds a copy of the codebook, laid out with the grid as the encoder loads it
+ * into LDS; qamw_encode searches that copy, so d_codebook passed to qamw_encode must be the
+ * codebook the index was built from.
  *   d_index  device buffer of at least qamw_index_bytes(bits) bytes; it stays valid for this
  *            codebook until the codebook changes.  Limits: 1 <= bits <= 12. */
 int qamw_codebook_index(const float* d_codebook, int32_t bits, void* d_index, size_t index_bytes,

@@ -419,7 +419,7 @@ __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a, int T, int R) {
     // the prefetched row can leave the previous row's stores in flight.
     RawW<E, BF> nxt;
     load_row_raw<E, BF, VEC>(a.w, a.ld, a.d_in, a.d_out, base + grp, tid, nxt);
-    search_lds_fill(sl, a.cb, K, index, threadIdx.x, blockDim.x);
+    search_lds_fill(sl, index, K, threadIdx.x, blockDim.x);
 
     int32_t flags = 0;
     float cf[E];   // s_j * eps_j, exact in fp32

@@ -272,6 +272,37 @@ __global__ __launch_bounds__(256) void k_ix_order(const float* __restrict__ cb, 
     order[rank] = (uint16_t)j;
 }
 
+// 6. The LDS image (layout of search_image_layout): codebook, fine-bin table, list offsets as
+// u16 (clamped to the entries kept), lists as byte offsets 8 j, then zeros.
+__global__ __launch_bounds__(256) void k_ix_image(const float* __restrict__ cb, int K, char* __restrict__ index) {
+    const IndexHeader& ih = *reinterpret_cast<const IndexHeader*>(index);
+    const SearchImageLayout l = search_image_layout(K, ih.G);
+    char* img = index + kIndexImgOff;
+    const uint32_t* offs = reinterpret_cast<const uint32_t*>(index + kIndexOffsOff);
+    const uint16_t* ent = reinterpret_cast<const uint16_t*>(index + kIndexEntOff);
+    const uint8_t* fine = reinterpret_cast<const uint8_t*>(index + kIndexFineOff);
+    const uint32_t ne = (uint32_t)min(ih.n_entries, index_lds_entries(K));
+    const int cells = ih.G * ih.G;
+    const int stride = gridDim.x * blockDim.x;
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < (int)(l.bytes / 2); i += stride) {
+        const size_t byte = (size_t)i * 2;   // one u16 of the image per step
+        uint16_t v = 0;
+        if (byte < l.fine) {
+            v = reinterpret_cast<const uint16_t*>(cb)[i];
+        } else if (byte < l.offs) {
+            const size_t b = byte - l.fine;
+            if (b + 1 < (size_t)kIndexFine) v = (uint16_t)(fine[b] | (fine[b + 1] << 8));
+        } else if (byte < l.ent) {
+            const size_t c = (byte - l.offs) / 2;
+            if (c <= (size_t)cells) v = (uint16_t)min(offs[c], ne);
+        } else {
+            const size_t e = (byte - l.ent) / 2;
+            if (e < ne) v = (uint16_t)(8u * ent[e]);
+        }
+        reinterpret_cast<uint16_t*>(img)[i] = v;
+    }
+}
+
 }  // namespace
 
 int index_grid_size(int bits) {
@@ -285,7 +316,7 @@ int index_grid_size(int bits) {
 }
 
 size_t index_bytes_for(int bits) {
-    return (size_t)kIndexEntOff + (size_t)kIndexMaxEntries * sizeof(uint16_t);
+    return kIndexImgOff + search_lds_bytes(1 << bits, index_grid_size(bits));
 }
 
 hipError_t launch_index_build(const float* cb, int bits, void* index, hipStream_t st) {
@@ -299,6 +330,7 @@ hipError_t launch_index_build(const float* cb, int bits, void* index, hipStream_
     hipLaunchKernelGGL(k_ix_scan, dim3(1), dim3(64), 0, st, ix, index_lds_entries(K));
     hipLaunchKernelGGL(k_ix_cells, dim3(G * G), dim3(256), smem, st, cb, K, ix, 1);
     hipLaunchKernelGGL(k_ix_order, dim3((K + 255) / 256), dim3(256), 0, st, cb, K, ix);
+    hipLaunchKernelGGL(k_ix_image, dim3(64), dim3(256), 0, st, cb, K, ix);
     return hipGetLastError();
 }
 
@@ -308,7 +340,7 @@ __global__ __launch_bounds__(256) void k_nearest(const float* __restrict__ pts, 
                                                  int K, const char* __restrict__ index, int32_t* __restrict__ out) {
     extern __shared__ __align__(16) char smem[];
     SearchLds s = search_lds_carve(smem, K, *reinterpret_cast<const IndexHeader*>(index), index);
-    search_lds_fill(s, cb, K, index, threadIdx.x, blockDim.x);
+    search_lds_fill(s, index, K, threadIdx.x, blockDim.x);
     __syncthreads();
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
         float2 p = reinterpret_cast<const float2*>(pts)[i];

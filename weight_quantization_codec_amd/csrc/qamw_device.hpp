@@ -74,6 +74,23 @@ __host__ __device__ inline size_t search_lds_bytes(int K, int G) {
            align16((size_t)(index_lds_entries(K) + kIndexListPad) * 2);
 }
 
+// Byte offsets of the sections of the LDS image: codebook, fine-bin table, list offsets (u16),
+// lists.  The search index holds a ready-made copy of this image (lists as byte offsets 8 j)
+// at kIndexImgOff, so a workgroup fills its LDS with a plain 16-byte copy.
+struct SearchImageLayout {
+    size_t cb, fine, offs, ent, bytes;
+};
+__host__ __device__ inline SearchImageLayout search_image_layout(int K, int G) {
+    SearchImageLayout l;
+    l.cb = 0;
+    l.fine = l.cb + align16((size_t)K * 8);
+    l.offs = l.fine + align16(kIndexFine);
+    l.ent = l.offs + align16((size_t)(G * G + 1) * 2);
+    l.bytes = search_lds_bytes(K, G);
+    return l;
+}
+constexpr size_t kIndexImgOff = ((size_t)kIndexEntOff + (size_t)kIndexMaxEntries * 2 + 255) / 256 * 256;
+
 template <int L>
 struct Layout {
     static constexpr int b = 1 << L;
@@ -157,17 +174,14 @@ __device__ __forceinline__ void eval_cw(float px, float py, float2 c, int j, flo
 }
 
 __device__ inline SearchLds search_lds_carve(char* smem, int K, const IndexHeader& ih, const char* index) {
+    const SearchImageLayout l = search_image_layout(K, ih.G);
     SearchLds s;
-    char* p = smem;
-    s.cb = reinterpret_cast<float2*>(p);
-    s.cb_lds = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)p);   // LDS offset
-    p += align16((size_t)K * 8);
+    s.cb = reinterpret_cast<float2*>(smem + l.cb);
+    s.cb_lds = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)smem);   // LDS offset
     s.order = reinterpret_cast<const uint16_t*>(index + kIndexOrderOff);
-    s.fine = reinterpret_cast<uint8_t*>(p);
-    p += align16(kIndexFine);
-    s.offs = reinterpret_cast<uint16_t*>(p);
-    p += align16((size_t)(ih.G * ih.G + 1) * 2);
-    s.ent = reinterpret_cast<uint16_t*>(p);
+    s.fine = reinterpret_cast<uint8_t*>(smem + l.fine);
+    s.offs = reinterpret_cast<uint16_t*>(smem + l.offs);
+    s.ent = reinterpret_cast<uint16_t*>(smem + l.ent);
     s.R = ih.R;
     s.inv_w = ih.inv_w;
     s.W = ih.W;
@@ -176,23 +190,31 @@ __device__ inline SearchLds search_lds_carve(char* smem, int K, const IndexHeade
     return s;
 }
 
-// Copy the codebook and the index into LDS (the caller synchronizes afterwards).
-__device__ inline void search_lds_fill(const SearchLds& s, const float* __restrict__ cb, int K,
-                                       const char* __restrict__ index, int tid, int nthreads) {
+// Copy the index's LDS image into LDS (16-byte copies, four in flight per thread).  The image's
+// lists hold byte offsets 8 j; when the image does not start at LDS address 0 they are rebased
+// after a barrier.  The caller synchronizes afterwards.
+__device__ inline void search_lds_fill(const SearchLds& s, const char* __restrict__ index, int K, int tid,
+                                       int nthreads) {
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
     const IndexHeader& ih = *reinterpret_cast<const IndexHeader*>(index);
-    const uint32_t* offs = reinterpret_cast<const uint32_t*>(index + kIndexOffsOff);
-    const uint16_t* ent = reinterpret_cast<const uint16_t*>(index + kIndexEntOff);
-    const uint8_t* fine = reinterpret_cast<const uint8_t*>(index + kIndexFineOff);
-    const int ne = min(ih.n_entries, index_lds_entries(K));   // the builder keeps n_entries within this
-    for (int j = tid; j < K; j += nthreads) s.cb[j] = reinterpret_cast<const float2*>(cb)[j];
-    for (int b = tid; b < s.W; b += nthreads) s.fine[b] = fine[b];
-    const int cells = s.G * s.G;
-    for (int c = tid; c <= cells; c += nthreads) {
-        uint32_t o = offs[c];
-        s.offs[c] = (uint16_t)(o < (uint32_t)ne ? o : (uint32_t)ne);
+    const SearchImageLayout l = search_image_layout(K, ih.G);
+    const int n16 = (int)(l.bytes / 16);
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(index + kIndexImgOff);
+    u32x4_t* dst = reinterpret_cast<u32x4_t*>(s.cb);
+    int i = tid;
+    for (; i + 3 * nthreads < n16; i += 4 * nthreads) {
+        const u32x4_t v0 = src[i], v1 = src[i + nthreads], v2 = src[i + 2 * nthreads], v3 = src[i + 3 * nthreads];
+        dst[i] = v0;
+        dst[i + nthreads] = v1;
+        dst[i + 2 * nthreads] = v2;
+        dst[i + 3 * nthreads] = v3;
     }
-    for (int e = tid; e < ne + kIndexListPad; e += nthreads)
-        s.ent[e] = (uint16_t)(s.cb_lds + (e < ne ? 8u * ent[e] : 0u));
+    for (; i < n16; i += nthreads) dst[i] = src[i];
+    if (s.cb_lds != 0) {
+        __syncthreads();
+        const int ne = min(ih.n_entries, index_lds_entries(K)) + kIndexListPad;
+        for (int e = tid; e < ne; e += nthreads) s.ent[e] = (uint16_t)(s.ent[e] + s.cb_lds);
+    }
 }
 
 // True when any active lane of the wavefront has a non-zero value.
