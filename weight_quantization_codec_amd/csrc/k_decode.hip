@@ -33,6 +33,8 @@ __device__ __forceinline__ int dcol_B(int tid, int m) {
 }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -46,6 +48,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // streamed; on gfx950 this raises the sustained rate of the mixed code-read / output-write
 // traffic from about 4.5 to about 6 TB/s (measured with 1 KiB-contiguous 16-byte stores).
 constexpr int kStoreNT = 2;
+
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const uint8_t* codes, size_t stride, int row) {
     return __builtin_amdgcn_make_buffer_rsrc((void*)(codes + (size_t)row * stride), (short)0, (int)stride,
@@ -82,6 +85,57 @@ struct DecWave {
     __device__ static constexpr int pad(int k) { return k + 4 * (k >> 5); }
 };
 
+// The dwords that hold NP consecutive fields of BITS bits, whatever the bit phase of the first.
+template <int NP, int BITS>
+struct LaneCodes {
+    static constexpr int NA = (NP * BITS + 31) / 32;   // dwords of the fields once aligned
+    static constexpr int ND = NA + 1;                  // dwords to load
+};
+
+// N consecutive dwords from byte offset off of a buffer (dword-aligned; dwords past the
+// descriptor's size read as 0, each dword checked on its own).
+template <int N>
+__device__ __forceinline__ void load_dwords(__amdgpu_buffer_rsrc_t rs, uint32_t off, uint32_t* d) {
+#pragma unroll
+    for (int c = 0; c + 4 <= N; c += 4) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 4 * c, 0, 0);
+        d[c] = v[0];
+        d[c + 1] = v[1];
+        d[c + 2] = v[2];
+        d[c + 3] = v[3];
+    }
+    constexpr int c = N / 4 * 4;
+    if constexpr (N - c == 3) {
+        const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(rs, off + 4 * c, 0, 0);
+        d[c] = v[0];
+        d[c + 1] = v[1];
+        d[c + 2] = v[2];
+    } else if constexpr (N - c == 2) {
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rs, off + 4 * c, 0, 0);
+        d[c] = v[0];
+        d[c + 1] = v[1];
+    } else if constexpr (N - c == 1) {
+        d[c] = __builtin_amdgcn_raw_buffer_load_b32(rs, off + 4 * c, 0, 0);
+    }
+}
+
+// The NP fields of a lane from its loaded dwords; s0 = bit phase of the first field.
+template <int NP, int BITS>
+__device__ __forceinline__ void unpack_lane(const uint32_t (&dw)[LaneCodes<NP, BITS>::ND], uint32_t s0,
+                                            int (&idx)[NP]) {
+    constexpr int NA = LaneCodes<NP, BITS>::NA;
+    uint32_t al[NA];
+#pragma unroll
+    for (int t = 0; t < NA; ++t) al[t] = __builtin_amdgcn_alignbit(dw[t + 1], dw[t], s0);
+    constexpr uint32_t mask = (1u << BITS) - 1u;
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+        const int off = i * BITS, w = off >> 5, sh = off & 31;
+        const uint32_t v = (sh + BITS <= 32) ? (al[w] >> sh) : __builtin_amdgcn_alignbit(al[w + 1], al[w], sh);
+        idx[i] = (int)(v & mask);
+    }
+}
+
 template <int L, int BITS>
 __device__ __forceinline__ void unpack_staged(const uint32_t* wb, int lane, int bits, int (&idx)[Layout<L>::E / 2]) {
     constexpr int NP = Layout<L>::E / 2;
@@ -114,16 +168,22 @@ __device__ __forceinline__ void unpack_staged(const uint32_t* wb, int lane, int 
 }
 
 // A workgroup decodes R rows at a time (R groups of T lanes, T = lanes per row) and walks rows
-// strided over the grid with the next row's codes in flight.  Every lane runs the same
-// instruction stream: idle lanes load and store through buffer descriptors with offsets beyond
-// their bounds (loads then return 0, stores are dropped), and rows with a zero norm select +0
-// after the arithmetic, so the compiler never has to wait for this row's stores.
+// strided over the grid with the next row's codes in flight.  Memory accesses never branch:
+// idle lanes and rows past the end load and store through offsets or descriptors outside their
+// buffers (loads return 0, stores are dropped), so the wait for the prefetched row can leave the
+// previous row's stores in flight.  A row with a zero norm takes a branch that is uniform over
+// its group and writes +0.
+//
+// With a compile-time field width each lane loads the dwords holding its own fields straight
+// into registers; otherwise the group stages the row's codes in LDS.  The output leaves through
+// the wave's LDS buffer: 16-byte stores, each instruction writing 1 KiB of consecutive bytes.
 template <int L, int BITS, int MAXT, bool OBF>
 __global__ __launch_bounds__(MAXT) void k_decode(DecodeArgs a, int T, int R) {
     using Lo = Layout<L>;
     using DW = DecWave<L>;
     constexpr int E = Lo::E, NP = E / 2;
     constexpr int ESZ = OBF ? 2 : 4;
+    constexpr bool kLaneLoads = BITS > 0;
     extern __shared__ __align__(16) char smem[];
     const int bits = BITS > 0 ? BITS : a.bits;
     const int K = 1 << bits;
@@ -140,8 +200,13 @@ __global__ __launch_bounds__(MAXT) void k_decode(DecodeArgs a, int T, int R) {
     const bool active = tid < a.d_in / E;
     const int rstride = gridDim.x * R;
 
-    // this wave's code span: E*bits dwords from dword wave_in_row*E*bits of the row
+    // this wave's code span: E*bits dwords from dword wave_in_row*E*bits of the row; this lane's
+    // fields start at bit bp0 of the span
     const int span_dw = E * bits;
+    const uint32_t bp0 = (uint32_t)(lane * NP) * (uint32_t)bits;
+    const uint32_t s0 = bp0 & 31u;
+    constexpr int ND = kLaneLoads ? LaneCodes<NP, (BITS > 0 ? BITS : 1)>::ND : 4 * DW::nload;
+    uint32_t lane_off = active ? (uint32_t)(wave_in_row * span_dw * 4) + (bp0 >> 5) * 4u : 0x7FFFFF00u;
     uint32_t coff[DW::nload];
 #pragma unroll
     for (int c = 0; c < DW::nload; ++c) {
@@ -149,24 +214,35 @@ __global__ __launch_bounds__(MAXT) void k_decode(DecodeArgs a, int T, int R) {
         coff[c] = d < span_dw ? (uint32_t)((wave_in_row * span_dw + d) * 4) : 0x7FFFFFF0u;
     }
 
-    // Row loads never branch: a row past the end gets a descriptor covering no bytes (the loads
-    // return 0), so the loop body is straight-line code and the wait for the prefetched row can
-    // leave the previous row's stores in flight.
     const __amdgpu_buffer_rsrc_t nrs =
         __builtin_amdgcn_make_buffer_rsrc((void*)a.norm, (short)0, a.d_out * 2, 0x00020000);
-    auto load_row = [&](int r, u32x4 (&dst)[DW::nload], uint16_t& nh) {
+    auto load_row = [&](int r, uint32_t (&dst)[ND]) {
         const bool ok = r < a.d_out;
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(a.codes + (size_t)(ok ? r : 0) * a.stride), (short)0, ok ? (int)a.stride : 0, 0x00020000);
-        nh = __builtin_amdgcn_raw_buffer_load_b16(nrs, (uint32_t)r * 2u, 0, 0);
+        if constexpr (kLaneLoads) {
+            load_dwords<ND>(rs, lane_off, dst);
+        } else {
 #pragma unroll
-        for (int c = 0; c < DW::nload; ++c) dst[c] = __builtin_amdgcn_raw_buffer_load_b128(rs, coff[c], 0, 0);
+            for (int c = 0; c < DW::nload; ++c) {
+                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, coff[c], 0, 0);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) dst[4 * c + k] = v[k];
+            }
+        }
+    };
+    // Row norms come in batches of 64: lane l holds the norm of the group's row r0 + l * rstride
+    // (0 past the end), and pass n of the batch reads lane n.  A batch is loaded (and waited for)
+    // once per 64 passes, so no pass waits on a norm load issued in that pass.
+    auto load_norms = [&](int r0) {
+        return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(
+            nrs, ((uint32_t)r0 + (uint32_t)lane * (uint32_t)rstride) * 2u, 0, 0);
     };
 
     int row = blockIdx.x * R + grp;
-    u32x4 nxt[DW::nload];
-    uint16_t nh_next;
-    load_row(row, nxt, nh_next);
+    uint32_t nxt[ND];
+    load_row(row, nxt);
+    uint32_t nbatch = load_norms(row);
 
     // ---- once per workgroup: codebook table, sigma of this lane's pairs, eps_j / s_j of its columns
     {   // table entry j = (c_x + c_y, c_x - c_y), exact in double; two codewords per 16-byte load
@@ -248,14 +324,14 @@ __global__ __launch_bounds__(MAXT) void k_decode(DecodeArgs a, int T, int R) {
     }
 #pragma unroll
     for (int m = 0; m < E; ++m) pin_reg(cf[m]);
-    // output: chunk c of this wave covers dwords [256 c, 256 c + 256) of the wave's span
+    const double inv_sqrt_b = 1.0 / __builtin_sqrt((double)Lo::b);
+    // Output, staged: chunk c of this wave covers dwords [256 c, 256 c + 256) of the wave's span;
+    // element m of this lane goes to dword pad(kb + o(m)) of the wave buffer, kb per lane and o(m)
+    // a compile-time offset.  kb's place within its 32-dword group plus o(m)'s never crosses a
+    // group, so pad(kb + o) = pad(kb) + o + 4*(o/32): one base register.
     constexpr int out_dw = kWave * E * ESZ / 4;
     constexpr int nchunk = out_dw / 256;
     const uint32_t wave_byte0 = (uint32_t)(wave_in_row * out_dw * 4);
-    const double inv_sqrt_b = 1.0 / __builtin_sqrt((double)Lo::b);
-    // Staged output: element m of this lane goes to dword pad(kb + o(m)) of the wave buffer, kb
-    // per lane and o(m) a compile-time offset.  kb's place within its 32-dword group plus o(m)'s
-    // never crosses a group, so pad(kb + o) = pad(kb) + o + 4*(o/32): one base register.
     uint32_t* stg;
     {
         const unsigned ul = (unsigned)lane;
@@ -270,60 +346,108 @@ __global__ __launch_bounds__(MAXT) void k_decode(DecodeArgs a, int T, int R) {
     }
     __syncthreads();
 
+    int npass = 0;
     for (; row < a.d_out; row += rstride) {
-        const uint16_t nh = nh_next;
-        u32x4 cur[DW::nload];
-#pragma unroll
-        for (int c = 0; c < DW::nload; ++c) cur[c] = nxt[c];
-        load_row(row + rstride, nxt, nh_next);   // keep the next row in flight
-        const float rn = __half2float(__ushort_as_half(nh));
-        const bool zero_row = rn == 0.0f;
-        // codes -> LDS -> fields of this lane
-#pragma unroll
-        for (int c = 0; c < DW::nload; ++c) *reinterpret_cast<u32x4*>(wb + 4 * (lane + c * kWave)) = cur[c];
-        wave_lds_sync();
-        double x[E];
-        {
-            int idx[NP];
-            unpack_staged<L, BITS>(wb, lane, bits, idx);
-            const double g = (double)rn * inv_sqrt_b;
-#pragma unroll
-            for (int i = 0; i < NP; ++i) {
-                double2 t = tab[idx[i]];
-                double sc = (double)sg[i] * g;
-                x[2 * i] = t.x * sc;
-                x[2 * i + 1] = t.y * sc;
-            }
+        if (npass == kWave) {
+            nbatch = load_norms(row);
+            pin_reg(nbatch);   // waited for here, not at the reads of later passes
+            npass = 0;
         }
-        wave_lds_sync();
-        if constexpr (Lo::two_phase) {
-#pragma unroll
-            for (int r = 1; r < Lo::e; ++r) butterfly<E>(x, r);
-            exchange_AB<L>(x, xb, lane);
-#pragma unroll
-            for (int r = 1; r < Lo::e; ++r)
-                if (L - Lo::e + r >= Lo::e) butterfly<E>(x, r);
+        const uint16_t nh = (uint16_t)__builtin_amdgcn_readlane(nbatch, npass);
+        ++npass;
+        const float rn = __half2float(__ushort_as_half(nh));
+        // this lane's fields, then the next row's codes into the same registers
+        int idx[NP];
+        if constexpr (kLaneLoads) {
+            unpack_lane<NP, (BITS > 0 ? BITS : 1)>(nxt, s0, idx);
         } else {
 #pragma unroll
-            for (int r = 1; r < L; ++r) butterfly<E>(x, r);
+            for (int c = 0; c < DW::nload; ++c)
+                *reinterpret_cast<u32x4*>(wb + 4 * (lane + c * kWave)) =
+                    u32x4{nxt[4 * c], nxt[4 * c + 1], nxt[4 * c + 2], nxt[4 * c + 3]};
+            wave_lds_sync();
+            unpack_staged<L, BITS>(wb, lane, bits, idx);
+            wave_lds_sync();
         }
-        // scale, round, and stage the output in wave order
-        const uint32_t keep = zero_row ? 0u : ~0u;   // a zero row decodes to +0
+        load_row(row + rstride, nxt);   // keep the next row in flight
+        uint32_t ow[E * ESZ / 4];       // output dwords of this lane, in m order
+        if (rn != 0.0f) {
+            double x[E];
+            const double g = (double)rn * inv_sqrt_b;
+            // all NP table reads in flight at once, then one wait
+            double2 t[NP];
+#pragma unroll
+            for (int i = 0; i < NP; ++i) t[i] = tab[idx[i]];
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < NP; ++i) {
+                const double sc = (double)sg[i] * g;
+                x[2 * i] = t[i].x * sc;
+                x[2 * i + 1] = t[i].y * sc;
+            }
+            // Stage 0 is in the table; the other stages never mix the halves (element bit 0 = 0
+            // or 1), so each half is exchanged while the other one is transformed: the LDS
+            // latency of one half hides behind the arithmetic of the other.
+            float f[E];   // x * eps / s, rounded to fp32
+            if constexpr (Lo::two_phase) {
+                const Exchange<L> ex(xb, lane);
+#pragma unroll
+                for (int r = 1; r < Lo::e; ++r) butterfly_half<E>(x, r, 0);
+                ex.write(x, 0);
+#pragma unroll
+                for (int r = 1; r < Lo::e; ++r) butterfly_half<E>(x, r, 1);
+                wave_lds_sync();
+                ex.read(x, 0);
+                wave_lds_sync();   // half 0 read before half 1 overwrites the buffer
+                ex.write(x, 1);
+#pragma unroll
+                for (int r = 1; r < Lo::e; ++r)
+                    if (L - Lo::e + r >= Lo::e) butterfly_half<E>(x, r, 0);
+#pragma unroll
+                for (int m = 0; m < E; m += 2) f[m] = (float)(x[m] * cf[m]);
+                wave_lds_sync();
+                ex.read(x, 1);
+                wave_lds_sync();
+#pragma unroll
+                for (int r = 1; r < Lo::e; ++r)
+                    if (L - Lo::e + r >= Lo::e) butterfly_half<E>(x, r, 1);
+#pragma unroll
+                for (int m = 1; m < E; m += 2) f[m] = (float)(x[m] * cf[m]);
+            } else {
+#pragma unroll
+                for (int r = 1; r < L; ++r) butterfly<E>(x, r);
+#pragma unroll
+                for (int m = 0; m < E; ++m) f[m] = (float)(x[m] * cf[m]);
+            }
+            // round to the output type
+#pragma unroll
+            for (int m = 0; m < E; m += 2) {
+                if constexpr (OBF) {
+                    ow[m / 2] = pack_bf16x2(f[m], f[m + 1]);
+                } else {
+                    ow[m] = __float_as_uint(f[m]);
+                    ow[m + 1] = __float_as_uint(f[m + 1]);
+                }
+            }
+        } else {   // a zero row decodes to +0
+#pragma unroll
+            for (int k = 0; k < E * ESZ / 4; ++k) ow[k] = 0u;
+        }
+        const bool rv = row < a.d_out;
+        const __amdgpu_buffer_rsrc_t ors = out_rsrc(a.out, a.ld, ESZ, rv ? a.d_in : 0, rv ? row : 0);
+        // stage in wave order, then 16-byte stores
 #pragma unroll
         for (int m = 0; m < E; m += 2) {
-            const float v0 = (float)(x[m] * cf[m]);
-            const float v1 = (float)(x[m + 1] * cf[m + 1]);
             if constexpr (OBF) {
                 const int o = Lo::two_phase ? (m >> 1) * Lo::lanes : m / 2;
-                stg[o + 4 * (o >> 5)] = pack_bf16x2(v0, v1) & keep;
+                stg[o + 4 * (o >> 5)] = ow[m / 2];
             } else {
                 const int o = Lo::two_phase ? (m >> 1) * 2 * Lo::lanes : m;
-                stg[o + 4 * (o >> 5)] = __float_as_uint(v0) & keep;
-                stg[o + 1 + 4 * ((o + 1) >> 5)] = __float_as_uint(v1) & keep;
+                stg[o + 4 * (o >> 5)] = ow[m];
+                stg[o + 1 + 4 * ((o + 1) >> 5)] = ow[m + 1];
             }
         }
         wave_lds_sync();
-        const __amdgpu_buffer_rsrc_t ors = out_rsrc(a.out, a.ld, ESZ, a.d_in, row);
 #pragma unroll
         for (int c = 0; c < nchunk; ++c) {
             const u32x4 v = *reinterpret_cast<const u32x4*>(wb + DW::pad(256 * c + 4 * lane));
@@ -337,7 +461,7 @@ __global__ __launch_bounds__(MAXT) void k_decode(DecodeArgs a, int T, int R) {
                 __builtin_amdgcn_raw_buffer_store_b32(v[3], ors, off + 12, 0, kStoreNT);
             }
         }
-        wave_lds_sync();
+        wave_lds_sync();   // the wave buffer is rewritten by the next pass
     }
 }
 

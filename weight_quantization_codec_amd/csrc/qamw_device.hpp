@@ -132,28 +132,57 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Phase A -> phase B for one wavefront.  `xb` is the wavefront's exchange buffer
-// (Layout<L>::xbuf doubles).  lane = lane id in the wavefront.
+// Butterflies on index bit rbit over the elements whose bit 0 is h (rbit >= 1 keeps the two
+// halves apart).
+template <int E>
+__device__ __forceinline__ void butterfly_half(double (&x)[E], int rbit, int h) {
+#pragma unroll
+    for (int m = 0; m < E; ++m) {
+        if ((m & 1) == h && !(m & (1 << rbit))) {
+            double a = x[m], c = x[m | (1 << rbit)];
+            x[m] = a + c;
+            x[m | (1 << rbit)] = a - c;
+        }
+    }
+}
+
+// Phase A -> phase B for one wavefront, one half (the elements with bit 0 = h) at a time.
+// `xb` is the wavefront's exchange buffer (Layout<L>::xbuf doubles, one half).
 // Compact index c of a (block-local) element sits at c + c/H (one pad double per H).  The lanes
 // of a block divide H, so both address streams are one per-lane base plus compile-time offsets:
 //   write: element q*E + 2i + h -> c = base + q*H + i,        c/H = base/H + q
 //   read : element h | (q<<1) | (i<<(L-e+1)) -> c = base + q + i*lanes, c/H = base/H + i*lanes/H
 template <int L>
-__device__ __forceinline__ void exchange_AB(double (&x)[Layout<L>::E], double* xb, int lane) {
+struct Exchange {
     using Lo = Layout<L>;
-    constexpr int H = Lo::half, NL = Lo::lanes;
+    static constexpr int H = Lo::half, NL = Lo::lanes;
     static_assert(H % NL == 0, "lanes of a block must divide E/2");
-    const unsigned beta = (unsigned)lane / NL, q = (unsigned)lane % NL;
-    const unsigned base = beta * (Lo::b / 2);
-    double* wr = xb + (base + base / H + q * (H + 1));
-    double* rd = xb + (base + base / H + q);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    double* wr;
+    double* rd;
+    __device__ Exchange(double* xb, int lane) {
+        const unsigned beta = (unsigned)lane / NL, q = (unsigned)lane % NL;
+        const unsigned base = beta * (Lo::b / 2);
+        wr = xb + (base + base / H + q * (H + 1));
+        rd = xb + (base + base / H + q);
+    }
+    __device__ __forceinline__ void write(const double (&x)[Lo::E], int h) const {
 #pragma unroll
         for (int i = 0; i < H; ++i) wr[i] = x[2 * i + h];
-        wave_lds_sync();
+    }
+    __device__ __forceinline__ void read(double (&x)[Lo::E], int h) const {
 #pragma unroll
         for (int i = 0; i < H; ++i) x[2 * i + h] = rd[i * NL + (i * NL) / H];
+    }
+};
+
+template <int L>
+__device__ __forceinline__ void exchange_AB(double (&x)[Layout<L>::E], double* xb, int lane) {
+    const Exchange<L> ex(xb, lane);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        ex.write(x, h);
+        wave_lds_sync();
+        ex.read(x, h);
         wave_lds_sync();
     }
 }
