@@ -157,12 +157,29 @@ __device__ __forceinline__ double front_end(const RawW<Layout<L>::E, BF>& raw, b
     ss = wave_sum(ss);
     if ((tid & (kWave - 1)) == 0) red[tid / kWave] = ss;
     if constexpr (Lo::two_phase) {
+        // The stages commute: stage 0 (element bit 0) runs last, in phase B, so the two halves
+        // (bit 0 = 0 or 1) stay apart until then and each half is exchanged while the other one
+        // is transformed.
+        const Exchange<L> ex(xb, tid & (kWave - 1));
 #pragma unroll
-        for (int r = 0; r < Lo::e; ++r) butterfly<E>(x, r);
-        exchange_AB<L>(x, xb, tid & (kWave - 1));
+        for (int r = 1; r < Lo::e; ++r) butterfly_half<E>(x, r, 0);
+        ex.write(x, 0);
+#pragma unroll
+        for (int r = 1; r < Lo::e; ++r) butterfly_half<E>(x, r, 1);
+        wave_lds_sync();
+        ex.read(x, 0);
+        wave_lds_sync();   // half 0 read before half 1 overwrites the buffer
+        ex.write(x, 1);
 #pragma unroll
         for (int r = 1; r < Lo::e; ++r)
-            if (L - Lo::e + r >= Lo::e) butterfly<E>(x, r);
+            if (L - Lo::e + r >= Lo::e) butterfly_half<E>(x, r, 0);
+        wave_lds_sync();
+        ex.read(x, 1);
+        wave_lds_sync();
+#pragma unroll
+        for (int r = 1; r < Lo::e; ++r)
+            if (L - Lo::e + r >= Lo::e) butterfly_half<E>(x, r, 1);
+        butterfly<E>(x, 0);
     } else {
 #pragma unroll
         for (int r = 0; r < L; ++r) butterfly<E>(x, r);
@@ -369,14 +386,14 @@ constexpr int kSearchBatch = 4;
 // 170 VGPRs (three wavefronts per SIMD) without spills.
 constexpr int kEncodeMaxThreads = 768;
 
-// LDS bytes per row group of the encoder: the indices (u16, zero-padded to a multiple of 32) and
-// the packed words, which cover whole 32-index chunks and at least the row stride.
-__host__ __device__ inline size_t encode_group_bytes(int n_pairs, int bits) {
-    const size_t idx_stride = (size_t)((n_pairs + 31) & ~31);
-    const size_t stride = (((size_t)n_pairs * bits + 7) / 8 + 15) / 16 * 16;
-    const size_t chunk_words = idx_stride * bits / 8;
-    const size_t stage = ((stride > chunk_words ? stride : chunk_words) + 15) / 16 * 16;
-    return idx_stride * 2 + stage;
+// LDS bytes per wavefront of the encoder.  A wavefront's lanes cover 32 E consecutive pairs of
+// the row, so it packs and stores its own part of the row: its buffer holds the exchange during
+// the front end and then the wavefront's 32 E indices (u16) and their packed words (4 E bits
+// bytes, a multiple of 16).
+__host__ __device__ inline size_t encode_wave_bytes(int E, bool two_phase, int bits) {
+    const size_t xch = two_phase ? (size_t)(kWave * (E / 2) + kWave) * sizeof(double) : 0;
+    const size_t pack = (size_t)64 * E + (size_t)4 * E * bits;
+    return xch > pack ? xch : pack;
 }
 
 template <int L, int MAXT, bool BF, bool VEC>
@@ -390,25 +407,20 @@ __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a, int T, int R) {
     const char* index = reinterpret_cast<const char*>(a.index);
     const IndexHeader ih = *reinterpret_cast<const IndexHeader*>(index);
     const SearchLds sl = search_lds_carve(smem, K, ih, index);
+    // norm partials, double-buffered by pass parity ([2][R][kMaxWaves]): a wavefront may reach
+    // the next pass's front end while others still read this pass's partials
     double* red_all = reinterpret_cast<double*>(smem + search_lds_bytes(K, ih.G));
-    double* red = red_all + grp * kMaxWaves;
-    double* xb_all = red_all + R * kMaxWaves;
-    double* xb = xb_all + (threadIdx.x / kWave) * Lo::xbuf;
+    const int wave_bytes = (int)encode_wave_bytes(E, Lo::two_phase, a.bits);
+    char* wbuf = reinterpret_cast<char*>(red_all + 2 * R * kMaxWaves) + (threadIdx.x / kWave) * wave_bytes;
+    double* xb = reinterpret_cast<double*>(wbuf);
     const int n_pairs = a.d_in / 2;
-    // per group: the row's indices (u16, padded with zeros to a multiple of 32), then its packed
-    // words (the row stride, a multiple of 16 bytes)
-    const int idx_stride = (n_pairs + 31) & ~31;
-    const int grp_bytes = (int)encode_group_bytes(n_pairs, a.bits);
-    // the group buffers share LDS with the exchange buffers: they are used between the end of the
-    // front end (a workgroup barrier) and the end of the pass (another barrier)
-    char* gbuf = reinterpret_cast<char*>(xb_all) + grp * grp_bytes;
-    uint16_t* idxrow = reinterpret_cast<uint16_t*>(gbuf);
-    uint32_t* stage = reinterpret_cast<uint32_t*>(gbuf + idx_stride * 2);
-    for (int k = n_pairs + tid; k < idx_stride; k += T) idxrow[k] = 0;   // never written again
+    const int lane = threadIdx.x & (kWave - 1);
+    // this wavefront's indices and packed words (after the front end, in its exchange buffer)
+    uint16_t* widx = reinterpret_cast<uint16_t*>(wbuf);
+    uint32_t* wstage = reinterpret_cast<uint32_t*>(wbuf + 64 * E);
     // this lane's pairs k = col_B(tid, 2i)/2 are base + i * (lanes per block): one base address
-    uint16_t* idxrow_l = idxrow + (Lo::two_phase ? ((unsigned)tid / Lo::lanes) * (Lo::b / 2) + (unsigned)tid % Lo::lanes
-                                                 : (unsigned)tid * NP);
-
+    uint16_t* idx_l = widx + (Lo::two_phase ? ((unsigned)lane / Lo::lanes) * (Lo::b / 2) + (unsigned)lane % Lo::lanes
+                                            : (unsigned)lane * NP);
     const int units = a.d_in / E;
     const bool active = tid < units;
     const int rstride = gridDim.x * R;
@@ -436,18 +448,19 @@ __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a, int T, int R) {
     }
     const double inv_sqrt_b = 1.0 / __builtin_sqrt((double)Lo::b);
     const int bits = a.bits;
-    const int nwords = (int)(a.stride / 4);
     const __amdgpu_buffer_rsrc_t nrs =
         __builtin_amdgcn_make_buffer_rsrc((void*)a.norm, (short)0, a.d_out * 2, 0x00020000);
     __syncthreads();
 
-    for (; base < a.d_out; base += rstride) {
+    const uint32_t wave_byte0 = (uint32_t)(tid / kWave) * (uint32_t)(4 * E * a.bits);   // the wavefront's part of the row
+    for (int pass = 0; base < a.d_out; base += rstride, ++pass) {
         const int row = base + grp;
         const bool rv = row < a.d_out;
         const RawW<E, BF> cur = nxt;
         load_row_raw<E, BF, VEC>(a.w, a.ld, a.d_in, a.d_out, row + rstride, tid, nxt);   // next row in flight
         double x[E];
         int32_t rf = 0;
+        double* red = red_all + ((pass & 1) * R + grp) * kMaxWaves;
         const double r2 = front_end<L, BF>(cur, active && rv, tid, cf, x, red, xb, nwaves, rf);
         const double r = __builtin_sqrt(r2);
         const bool nonzero = r > 0.0 && __builtin_isfinite(r);
@@ -473,8 +486,11 @@ __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a, int T, int R) {
                 if (nonzero) nearest_lds_batch<kSearchBatch>(bx, by, sl, bi);
 #pragma unroll
                 for (int i = 0; i < kSearchBatch; ++i)
-                    idxrow_l[(h * kSearchBatch + i) * (Lo::two_phase ? Lo::lanes : 1)] = nonzero ? (uint16_t)bi[i] : (uint16_t)0;
+                    idx_l[(h * kSearchBatch + i) * (Lo::two_phase ? Lo::lanes : 1)] = nonzero ? (uint16_t)bi[i] : (uint16_t)0;
             }
+        } else {   // pairs past the row: zero indices, so the row's padding bits are zero
+#pragma unroll
+            for (int i = 0; i < NP; ++i) idx_l[i * (Lo::two_phase ? Lo::lanes : 1)] = 0;
         }
         {   // the norm, stored by lane 0 of the group
             uint16_t nh = 0;
@@ -486,17 +502,17 @@ __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a, int T, int R) {
             __builtin_amdgcn_raw_buffer_store_b16(nh, nrs, tid == 0 ? (uint32_t)row * 2u : 0x7FFFFFF0u, 0, 0);
         }
         if (rv) flags |= rf;
-        __syncthreads();
-        // pack: 32 consecutive indices fill exactly `bits` words; thread t packs chunk t (the shift
-        // sequence is the same for every chunk, so the branches are uniform) into the staging words
-        const int nchunks = idx_stride / 32;
-        for (int c = tid; c < nchunks; c += T) {
+        wave_lds_sync();
+        // pack: 32 consecutive indices fill exactly `bits` words; lane c packs chunk c of the
+        // wavefront's E chunks (the shift sequence is the same for every chunk, so the branches
+        // are uniform)
+        for (int c = lane; c < E; c += kWave) {
             uint64_t acc = 0;
             int nb = 0;
-            uint32_t* wp = stage + c * bits;
+            uint32_t* wp = wstage + c * bits;
 #pragma unroll
             for (int k8 = 0; k8 < 4; ++k8) {
-                const uint4 q = *reinterpret_cast<const uint4*>(idxrow + 32 * c + 8 * k8);
+                const uint4 q = *reinterpret_cast<const uint4*>(widx + 32 * c + 8 * k8);
                 const uint32_t v[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
@@ -510,21 +526,20 @@ __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a, int T, int R) {
                 }
             }
         }
-        for (int wd = nchunks * bits + tid; wd < nwords; wd += T) stage[wd] = 0;   // row padding
-        __syncthreads();
-        // 16-byte stores of the staged row: thread t stores chunks t, t + T, ...  A row has at most
-        // ceil(3 d_in / 64) chunks (12 bits per pair) and T >= d_in / E lanes, so NCH = ceil(3E/64)
-        // stores per thread cover it; the ones past the row are dropped.
+        wave_lds_sync();
+        // 16-byte stores of the wavefront's 4 E bits bytes: E bits / 4 chunks, lane c storing
+        // chunks c, c + 64, ...; chunks past the row stride are dropped by the descriptor
         const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(a.codes + (size_t)(rv ? row : 0) * a.stride), (short)0, rv ? (int)a.stride : 0, 0x00020000);
-        constexpr int NCH = (3 * E + 63) / 64;
+        const int nchunks = E * bits / 4;
+        constexpr int NCH = (E * 4 + kWave - 1) / kWave;   // bits <= 16
 #pragma unroll
         for (int u = 0; u < NCH; ++u) {
-            const int c = tid + u * T;
-            const u32x4 q = *reinterpret_cast<const u32x4*>(stage + 4 * min(c, nwords / 4 - 1));
-            __builtin_amdgcn_raw_buffer_store_b128(q, crs, 4 * c < nwords ? (uint32_t)c * 16u : 0x7FFFFFF0u, 0, 0);
+            const int c = lane + u * kWave;
+            const u32x4 q = *reinterpret_cast<const u32x4*>(wstage + 4 * min(c, nchunks - 1));
+            __builtin_amdgcn_raw_buffer_store_b128(q, crs, c < nchunks ? wave_byte0 + (uint32_t)c * 16u : 0x7FFFFFF0u, 0, 0);
         }
-        __syncthreads();   // the staged words are read before the next pass reuses the LDS
+        wave_lds_sync();   // the staged words are read before the next front end reuses the buffer
     }
     flag_status(a.status, flags);
 }
@@ -534,11 +549,11 @@ __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a, int T, int R) {
 template <int L>
 size_t encode_smem(int K, int R, int nwaves_total, int d_in) {
     using Lo = Layout<L>;
+    (void)d_in;
     int bits = 0;
     while ((1 << bits) < K) ++bits;
-    const size_t xb = Lo::two_phase ? (size_t)nwaves_total * Lo::xbuf * sizeof(double) : 0;
-    const size_t grp = (size_t)R * encode_group_bytes(d_in / 2, bits);
-    return search_lds_bytes(K, index_grid_size(bits)) + (size_t)R * kMaxWaves * sizeof(double) + (xb > grp ? xb : grp);
+    return search_lds_bytes(K, index_grid_size(bits)) + (size_t)2 * R * kMaxWaves * sizeof(double) +
+           (size_t)nwaves_total * encode_wave_bytes(Lo::E, Lo::two_phase, bits);
 }
 
 // R * kMaxWaves norm partials, then the exchange buffers (at least d_in/2 doubles: they also
@@ -658,9 +673,8 @@ size_t encode_lds_bytes(int L, int bits, int d_in) {
     const int E = lane_elems(L);
     if (E <= 0) return 0;
     const int nwaves = ((d_in / E) + kWave - 1) / kWave;
-    const size_t xb = (L > 4) ? (size_t)nwaves * (kWave * (E / 2) + kWave) * sizeof(double) : 0;
-    const size_t grp = encode_group_bytes(d_in / 2, bits);
-    return search_lds_bytes(1 << bits, index_grid_size(bits)) + kMaxWaves * sizeof(double) + (xb > grp ? xb : grp);
+    return search_lds_bytes(1 << bits, index_grid_size(bits)) + 2 * kMaxWaves * sizeof(double) +
+           (size_t)nwaves * encode_wave_bytes(E, L > 4, bits);
 }
 
 int calib_groups(int n_rows) { return n_rows < kCalibMaxGroups ? n_rows : kCalibMaxGroups; }
