@@ -121,10 +121,11 @@ __device__ __forceinline__ void load_raw(const void* w, bool vec, int64_t off, R
     }
 }
 
-// a_j = w_j * s_j * eps_j in double (exact), accumulating sum a_j^2.
+// a_j = w_j * s_j * eps_j in double (exact), accumulating sum a_j^2.  A non-finite a_j makes the
+// row's sum of squares non-finite (|a_j| < 2^256, so a_j^2 cannot overflow), so the row norm
+// alone tells whether the row has a non-finite weight.
 template <int E, bool BF>
-__device__ __forceinline__ void scale_raw(const RawW<E, BF>& r, const float (&cf)[E], double (&x)[E], double& ss,
-                                          int32_t& flags) {
+__device__ __forceinline__ void scale_raw(const RawW<E, BF>& r, const float (&cf)[E], double (&x)[E], double& ss) {
 #pragma unroll
     for (int m = 0; m < E; ++m) {
         float f;
@@ -133,7 +134,6 @@ __device__ __forceinline__ void scale_raw(const RawW<E, BF>& r, const float (&cf
         else
             f = __uint_as_float(r.u[m]);
         double a = (double)f * (double)cf[m];   // exact: two 24-bit significands
-        if (!__builtin_isfinite(a)) flags |= 1;
         x[m] = a;
         ss += a * a;
     }
@@ -144,12 +144,12 @@ __device__ __forceinline__ void scale_raw(const RawW<E, BF>& r, const float (&cf
 template <int L, bool BF>
 __device__ __forceinline__ double front_end(const RawW<Layout<L>::E, BF>& raw, bool active, int tid,
                                             const float (&cf)[Layout<L>::E], double (&x)[Layout<L>::E],
-                                            double* red, double* xb, int nwaves, int32_t& flags) {
+                                            double* red, double* xb, int nwaves) {
     using Lo = Layout<L>;
     constexpr int E = Lo::E;
     double ss = 0.0;
     if (active) {
-        scale_raw<E, BF>(raw, cf, x, ss, flags);
+        scale_raw<E, BF>(raw, cf, x, ss);
     } else {
 #pragma unroll
         for (int m = 0; m < E; ++m) x[m] = 0.0;
@@ -221,7 +221,6 @@ __global__ __launch_bounds__(MAXT) void k_calibrate(CalibArgs a, int T, int R) {
 #pragma unroll
     for (int i = 0; i < NP; ++i) acc[i] = 0.0;
     int nz = 0;
-    int32_t flags = 0;
     for (; base < a.n_rows; base += rstride) {
         const int row = base + grp;
         const bool rv = row < a.n_rows;
@@ -229,7 +228,7 @@ __global__ __launch_bounds__(MAXT) void k_calibrate(CalibArgs a, int T, int R) {
         if (active && row + rstride < a.n_rows)
             load_raw<E, BF>(a.w, vec, (int64_t)(row + rstride) * a.ld + (int64_t)tid * E, nxt);
         double x[E];
-        double r2 = front_end<L, BF>(cur, active && rv, tid, cf, x, red, xb, nwaves, flags);
+        double r2 = front_end<L, BF>(cur, active && rv, tid, cf, x, red, xb, nwaves);
         double r = __builtin_sqrt(r2);
         if (rv && r > 0.0 && __builtin_isfinite(r)) {
             ++nz;
@@ -380,11 +379,8 @@ __device__ __forceinline__ void load_row_raw(const void* w, int64_t ld, int d_in
 // blockIdx.x, R * (blockIdx.x + gridDim.x), ...  Every group runs every pass (a row past the end
 // is all zero and writes nothing), so the workgroup barriers are reached by all threads.
 // Per pass: front end (scale, norm, transform), pairs, lockstep search in batches of four pairs
-// per lane, indices to LDS, then the group packs its row into 16-byte words.
+// per lane, indices to LDS, then each wavefront packs and stores its part of the row.
 constexpr int kSearchBatch = 4;
-// Threads per workgroup the encoder aims for (R rows of T lanes): 768 keeps the kernel within
-// 170 VGPRs (three wavefronts per SIMD) without spills.
-constexpr int kEncodeMaxThreads = 768;
 
 // LDS bytes per wavefront of the encoder.  A wavefront's lanes cover 32 E consecutive pairs of
 // the row, so it packs and stores its own part of the row: its buffer holds the exchange during
@@ -396,7 +392,7 @@ __host__ __device__ inline size_t encode_wave_bytes(int E, bool two_phase, int b
     return xch > pack ? xch : pack;
 }
 
-template <int L, int MAXT, bool BF, bool VEC>
+template <int L, int MAXT, bool BF, bool VEC, bool ISG_LDS>
 __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a, int T, int R) {
     using Lo = Layout<L>;
     constexpr int E = Lo::E, NP = E / 2;
@@ -440,11 +436,23 @@ __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a, int T, int R) {
     if (active && bad_scale && blockIdx.x == 0) flags |= 2;   // reported once
 #pragma unroll
     for (int m = 0; m < E; ++m) pin_reg(cf[m]);
-    double isg[NP];
+    // 1 / sigma_k of the lane's pairs: in registers, or (ISG_LDS, which frees 16 VGPRs) in LDS,
+    // the same for every group (it depends on the lane's columns only), as double2 [NP/2][T] so
+    // that a wavefront's reads are consecutive
+    double2 isg_reg[NP / 2];
+    double2* isg_lds = reinterpret_cast<double2*>(reinterpret_cast<char*>(red_all + 2 * R * kMaxWaves) +
+                                                  (size_t)(blockDim.x / kWave) * wave_bytes);
 #pragma unroll
-    for (int i = 0; i < NP; ++i) {
-        isg[i] = 1.0 / (double)a.sigma[min(col_B<L>(tid, 2 * i) / 2, n_pairs - 1)];
-        pin_reg(isg[i]);
+    for (int i = 0; i < NP / 2; ++i) {
+        const double i0 = 1.0 / (double)a.sigma[min(col_B<L>(tid, 4 * i) / 2, n_pairs - 1)];
+        const double i1 = 1.0 / (double)a.sigma[min(col_B<L>(tid, 4 * i + 2) / 2, n_pairs - 1)];
+        if constexpr (ISG_LDS) {
+            if (grp == 0) isg_lds[i * T + tid] = make_double2(i0, i1);
+        } else {
+            isg_reg[i] = make_double2(i0, i1);
+            pin_reg(isg_reg[i].x);
+            pin_reg(isg_reg[i].y);
+        }
     }
     const double inv_sqrt_b = 1.0 / __builtin_sqrt((double)Lo::b);
     const int bits = a.bits;
@@ -461,7 +469,7 @@ __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a, int T, int R) {
         double x[E];
         int32_t rf = 0;
         double* red = red_all + ((pass & 1) * R + grp) * kMaxWaves;
-        const double r2 = front_end<L, BF>(cur, active && rv, tid, cf, x, red, xb, nwaves, rf);
+        const double r2 = front_end<L, BF>(cur, active && rv, tid, cf, x, red, xb, nwaves);
         const double r = __builtin_sqrt(r2);
         const bool nonzero = r > 0.0 && __builtin_isfinite(r);
         if (rv && !__builtin_isfinite(r)) rf |= 1;
@@ -469,10 +477,13 @@ __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a, int T, int R) {
             float px[NP], py[NP];
             const double hr = inv_sqrt_b / r;
 #pragma unroll
-            for (int i = 0; i < NP; ++i) {
-                const double g = isg[i] * hr;
-                px[i] = (float)(x[2 * i] * g);
-                py[i] = (float)(x[2 * i + 1] * g);
+            for (int i = 0; i < NP; i += 2) {
+                const double2 isg = ISG_LDS ? isg_lds[(i / 2) * T + tid] : isg_reg[i / 2];
+                const double g0 = isg.x * hr, g1 = isg.y * hr;
+                px[i] = (float)(x[2 * i] * g0);
+                py[i] = (float)(x[2 * i + 1] * g0);
+                px[i + 1] = (float)(x[2 * i + 2] * g1);
+                py[i + 1] = (float)(x[2 * i + 3] * g1);
             }
 #pragma unroll
             for (int h = 0; h < NP / kSearchBatch; ++h) {
@@ -547,13 +558,13 @@ __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a, int T, int R) {
 // LDS of the encoder: search image, R * kMaxWaves norm partials, and one region holding either
 // the exchange buffers (one per wavefront) or the R groups' indices and packed words.
 template <int L>
-size_t encode_smem(int K, int R, int nwaves_total, int d_in) {
+size_t encode_smem(int K, int R, int nwaves_total, bool isg_lds) {
     using Lo = Layout<L>;
-    (void)d_in;
     int bits = 0;
     while ((1 << bits) < K) ++bits;
+    const size_t isg = isg_lds ? (size_t)(nwaves_total / R) * kWave * (Lo::E / 2) * sizeof(double) : 0;
     return search_lds_bytes(K, index_grid_size(bits)) + (size_t)2 * R * kMaxWaves * sizeof(double) +
-           (size_t)nwaves_total * encode_wave_bytes(Lo::E, Lo::two_phase, bits);
+           (size_t)nwaves_total * encode_wave_bytes(Lo::E, Lo::two_phase, bits) + isg;
 }
 
 // R * kMaxWaves norm partials, then the exchange buffers (at least d_in/2 doubles: they also
@@ -569,34 +580,53 @@ size_t calib_smem(int R, int nwaves) {
 template <int L, bool BF, bool VEC>
 hipError_t encode_LBV(const EncodeArgs& a, hipStream_t st) {
     using Lo = Layout<L>;
-    constexpr int kMax = L <= 7 ? kEncodeMaxThreads : 512;
     const int T = ((a.d_in / Lo::E) + kWave - 1) / kWave * kWave;
     if (T > 1024 || (T > 512 && L > 7)) return hipErrorInvalidConfiguration;
     const int K = 1 << a.bits;
+    auto grid_for = [&](int R, int threads, size_t smem) {
+        int per_cu = (int)(kLdsBytes / smem);
+        if (per_cu * (threads / kWave) > 32) per_cu = 32 / (threads / kWave);
+        if (per_cu < 1) per_cu = 1;
+        const int need = (a.d_out + R - 1) / R;
+        return 256 * per_cu < need ? 256 * per_cu : need;
+    };
+    if constexpr (L <= 7) {
+        // up to 1024 threads with 1 / sigma in LDS (128 VGPRs, four wavefronts per SIMD)
+        int R = 1024 / T;
+        if (R > 4) R = 4;
+        if (R > a.d_out) R = a.d_out > 0 ? a.d_out : 1;
+        while (R > 1 && encode_smem<L>(K, R, R * T / kWave, true) > kLdsBytes) --R;
+        const int threads = R * T;
+        const size_t smem = encode_smem<L>(K, R, threads / kWave, true);
+        if (smem <= kLdsBytes) {
+            const int grid = grid_for(R, threads, smem);
+            if (grid < 1) return hipSuccess;
+            allow_lds(k_encode<L, 1024, BF, VEC, true>, smem);
+            hipLaunchKernelGGL((k_encode<L, 1024, BF, VEC, true>), dim3(grid), dim3(threads), smem, st, a, T, R);
+            return hipGetLastError();
+        }
+    }
+    // 1 / sigma in registers
+    constexpr int kMax = L <= 7 ? 768 : 512;
     int R = T >= kMax ? 1 : kMax / T;
     if (R > 4) R = 4;
     if (R > a.d_out) R = a.d_out > 0 ? a.d_out : 1;
-    while (R > 1 && encode_smem<L>(K, R, R * T / kWave, a.d_in) > kLdsBytes) --R;
+    while (R > 1 && encode_smem<L>(K, R, R * T / kWave, false) > kLdsBytes) --R;
     const int threads = R * T;
-    const size_t smem = encode_smem<L>(K, R, threads / kWave, a.d_in);
+    const size_t smem = encode_smem<L>(K, R, threads / kWave, false);
     if (smem > kLdsBytes) return hipErrorInvalidConfiguration;
-    int per_cu = (int)(kLdsBytes / smem);
-    if (per_cu * (threads / kWave) > 32) per_cu = 32 / (threads / kWave);
-    if (per_cu < 1) per_cu = 1;
-    int grid = 256 * per_cu;
-    const int need = (a.d_out + R - 1) / R;
-    if (grid > need) grid = need;
+    const int grid = grid_for(R, threads, smem);
     if (grid < 1) return hipSuccess;
     if (threads <= 512) {
-        allow_lds(k_encode<L, 512, BF, VEC>, smem);
-        hipLaunchKernelGGL((k_encode<L, 512, BF, VEC>), dim3(grid), dim3(threads), smem, st, a, T, R);
+        allow_lds(k_encode<L, 512, BF, VEC, false>, smem);
+        hipLaunchKernelGGL((k_encode<L, 512, BF, VEC, false>), dim3(grid), dim3(threads), smem, st, a, T, R);
     } else if constexpr (L <= 7) {
         if (threads <= 768) {
-            allow_lds(k_encode<L, 768, BF, VEC>, smem);
-            hipLaunchKernelGGL((k_encode<L, 768, BF, VEC>), dim3(grid), dim3(threads), smem, st, a, T, R);
+            allow_lds(k_encode<L, 768, BF, VEC, false>, smem);
+            hipLaunchKernelGGL((k_encode<L, 768, BF, VEC, false>), dim3(grid), dim3(threads), smem, st, a, T, R);
         } else {
-            allow_lds(k_encode<L, 1024, BF, VEC>, smem);
-            hipLaunchKernelGGL((k_encode<L, 1024, BF, VEC>), dim3(grid), dim3(threads), smem, st, a, T, R);
+            allow_lds(k_encode<L, 1024, BF, VEC, false>, smem);
+            hipLaunchKernelGGL((k_encode<L, 1024, BF, VEC, false>), dim3(grid), dim3(threads), smem, st, a, T, R);
         }
     } else {
         return hipErrorInvalidConfiguration;
