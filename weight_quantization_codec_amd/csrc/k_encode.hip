@@ -23,10 +23,26 @@ namespace {
 constexpr int kMaxWaves = 16;
 constexpr int kCalibMaxGroups = 256;
 
+// Sum over the wavefront in a fixed order, the same value returned to every lane.  DPP moves
+// (32-bit halves of the double) within rows of 16 lanes, then the row broadcasts into lane 63:
+// no LDS traffic and a short dependent chain.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_term(double x) {
+    // lanes of rows outside ROW_MASK get 0 (the `old` operand)
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)__double2loint(x), CTRL, ROW_MASK, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)__double2hiint(x), CTRL, ROW_MASK, 0xF, false);
+    return __hiloint2double(hi, lo);
+}
 __device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
-    return v;
+    v += dpp_term<0xB1, 0xF>(v);    // quad_perm [1,0,3,2]: pairs
+    v += dpp_term<0x4E, 0xF>(v);    // quad_perm [2,3,0,1]: quads
+    v += dpp_term<0x141, 0xF>(v);   // row_half_mirror: 8 lanes
+    v += dpp_term<0x140, 0xF>(v);   // row_mirror: rows of 16
+    v += dpp_term<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+    v += dpp_term<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3: lane 63 holds the total
+    const int lo = __builtin_amdgcn_readlane((int)__double2loint(v), kWave - 1);
+    const int hi = __builtin_amdgcn_readlane((int)__double2hiint(v), kWave - 1);
+    return __hiloint2double(hi, lo);
 }
 
 // s_j * eps_j of the E consecutive columns tid*E .. tid*E + E - 1 of a lane (phase A), exact in
