@@ -156,8 +156,10 @@ __device__ __forceinline__ void scale_raw(const RawW<E, BF>& r, const float (&cf
 }
 
 // Front end for one row given its raw weights: x <- unnormalized transform (phase B layout);
-// returns sum a^2 over the whole row (fixed shuffle tree, then wavefronts in order).
-template <int L, bool BF>
+// returns sum a^2 over the whole row (fixed shuffle tree, then wavefronts in order).  With SPLIT
+// the LDS transpose runs for lanes 0-31 and then for lanes 32-63 (a block's lanes never straddle
+// the two), so the wavefront's exchange buffer covers 32 lanes: half the LDS.
+template <int L, bool BF, bool SPLIT = false>
 __device__ __forceinline__ double front_end(const RawW<Layout<L>::E, BF>& raw, bool active, int tid,
                                             const float (&cf)[Layout<L>::E], double (&x)[Layout<L>::E],
                                             double* red, double* xb, int nwaves) {
@@ -176,22 +178,52 @@ __device__ __forceinline__ double front_end(const RawW<Layout<L>::E, BF>& raw, b
         // The stages commute: stage 0 (element bit 0) runs last, in phase B, so the two halves
         // (bit 0 = 0 or 1) stay apart until then and each half is exchanged while the other one
         // is transformed.
-        const Exchange<L> ex(xb, tid & (kWave - 1));
+        if constexpr (SPLIT) {
+            static_assert(32 % Lo::lanes == 0, "a block's lanes sit in one half of the wavefront");
+            const int lane = tid & (kWave - 1);
+            const Exchange<L> ex(xb, lane & 31);
+            const bool hi = lane >= 32;
 #pragma unroll
-        for (int r = 1; r < Lo::e; ++r) butterfly_half<E>(x, r, 0);
-        ex.write(x, 0);
+            for (int r = 1; r < Lo::e; ++r) butterfly_half<E>(x, r, 0);
+            if (!hi) ex.write(x, 0);
 #pragma unroll
-        for (int r = 1; r < Lo::e; ++r) butterfly_half<E>(x, r, 1);
-        wave_lds_sync();
-        ex.read(x, 0);
-        wave_lds_sync();   // half 0 read before half 1 overwrites the buffer
-        ex.write(x, 1);
+            for (int r = 1; r < Lo::e; ++r) butterfly_half<E>(x, r, 1);
+            wave_lds_sync();
+            if (!hi) ex.read(x, 0);
+            wave_lds_sync();
+            if (hi) ex.write(x, 0);
+            wave_lds_sync();
+            if (hi) ex.read(x, 0);
+            wave_lds_sync();
+            if (!hi) ex.write(x, 1);
 #pragma unroll
-        for (int r = 1; r < Lo::e; ++r)
-            if (L - Lo::e + r >= Lo::e) butterfly_half<E>(x, r, 0);
-        wave_lds_sync();
-        ex.read(x, 1);
-        wave_lds_sync();
+            for (int r = 1; r < Lo::e; ++r)
+                if (L - Lo::e + r >= Lo::e) butterfly_half<E>(x, r, 0);
+            wave_lds_sync();
+            if (!hi) ex.read(x, 1);
+            wave_lds_sync();
+            if (hi) ex.write(x, 1);
+            wave_lds_sync();
+            if (hi) ex.read(x, 1);
+            wave_lds_sync();
+        } else {
+            const Exchange<L> ex(xb, tid & (kWave - 1));
+#pragma unroll
+            for (int r = 1; r < Lo::e; ++r) butterfly_half<E>(x, r, 0);
+            ex.write(x, 0);
+#pragma unroll
+            for (int r = 1; r < Lo::e; ++r) butterfly_half<E>(x, r, 1);
+            wave_lds_sync();
+            ex.read(x, 0);
+            wave_lds_sync();   // half 0 read before half 1 overwrites the buffer
+            ex.write(x, 1);
+#pragma unroll
+            for (int r = 1; r < Lo::e; ++r)
+                if (L - Lo::e + r >= Lo::e) butterfly_half<E>(x, r, 0);
+            wave_lds_sync();
+            ex.read(x, 1);
+            wave_lds_sync();
+        }
 #pragma unroll
         for (int r = 1; r < Lo::e; ++r)
             if (L - Lo::e + r >= Lo::e) butterfly_half<E>(x, r, 1);
@@ -403,7 +435,7 @@ constexpr int kSearchBatch = 4;
 // the front end and then the wavefront's 32 E indices (u16) and their packed words (4 E bits
 // bytes, a multiple of 16).
 __host__ __device__ inline size_t encode_wave_bytes(int E, bool two_phase, int bits) {
-    const size_t xch = two_phase ? (size_t)(kWave * (E / 2) + kWave) * sizeof(double) : 0;
+    const size_t xch = two_phase ? (size_t)(32 * (E / 2) + 32) * sizeof(double) : 0;   // the split transpose
     const size_t pack = (size_t)64 * E + (size_t)4 * E * bits;
     return xch > pack ? xch : pack;
 }
@@ -485,7 +517,7 @@ __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a, int T, int R) {
         double x[E];
         int32_t rf = 0;
         double* red = red_all + ((pass & 1) * R + grp) * kMaxWaves;
-        const double r2 = front_end<L, BF>(cur, active && rv, tid, cf, x, red, xb, nwaves);
+        const double r2 = front_end<L, BF, true>(cur, active && rv, tid, cf, x, red, xb, nwaves);
         const double r = __builtin_sqrt(r2);
         const bool nonzero = r > 0.0 && __builtin_isfinite(r);
         if (rv && !__builtin_isfinite(r)) rf |= 1;
