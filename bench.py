@@ -11,6 +11,11 @@ copies of the buffers (>= 1 GiB) that the 256 MiB last-level cache cannot serve 
 The codebook training and the search-index build depend on the codebook only; they run and
 are timed once in the same run and reported beside the step.
 
+After the step, unless --no-stack: a 40-layer 13B-shaped stack (per layer q, k, v, o 5120x5120,
+gate and up 13824x5120, down 5120x13824; 12.7 G weights, bf16 Student-t(4) x 0.015 drawn on the
+GPU) is encoded and then decoded to BF16 in HBM, all 280 matrices back to back, for the
+sustained rates.
+
 Prints one JSON line.  --gpus N with N > 1 is not supported (single-GPU build).
 """
 import argparse
@@ -39,6 +44,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--rot-gib", type=float, default=1.25, help="bytes of rotated buffers")
+    ap.add_argument("--no-stack", action="store_true",
+                    help="skip the 40-layer 13B-shaped stack (sustained encode and decode)")
     return ap.parse_args()
 
 
@@ -210,6 +217,12 @@ def main():
         "roofline": roof_enc, "roofline_decode": roof_dec,
     }
 
+    # ---------------------------------------------------------------- 40-layer stack (sustained rates)
+    if not args.no_stack:
+        del sets
+        torch.cuda.empty_cache()
+        result["stack40"] = stack_run(torch, q, cb, index, bits, block, stream)
+
     # ---------------------------------------------------------------- CPU oracle baseline (whole workload)
     if not args.no_cpu:
         import oracle
@@ -226,6 +239,78 @@ def main():
                                   "sample": "whole 4096x4096 round trip (calibrate 1024 rows, encode, decode), "
                                             "%.1f s" % t_cpu}
     print(json.dumps(result), flush=True)
+
+
+def stack_run(torch, q, cb, index, bits, block, stream):
+    """Encode, then decode, the 280 matrices of a 40-layer 13B-shaped stack back to back."""
+    dev = cb.device
+    shapes = [(5120, 5120)] * 4 + [(13824, 5120)] * 2 + [(5120, 13824)]
+    n_layers = 40
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0x51414D5700000005)
+    mats = []
+    for layer in range(n_layers):
+        for (d_out, d_in) in shapes:
+            # Student-t(4) x 0.015: a normal over the root of a chi-square(4) / 4, drawn in fp32
+            g = torch.randn((d_out, d_in), generator=gen, device=dev)
+            c = torch.zeros_like(g)
+            for _ in range(4):
+                c.add_(torch.randn((d_out, d_in), generator=gen, device=dev).square_())
+            w = (g * 0.015 / torch.sqrt(c * 0.25)).to(torch.bfloat16)
+            del g, c
+            s = torch.randn((d_in,), generator=gen, device=dev).abs().sqrt() + 0.1
+            sign = torch.randint(-2**31, 2**31 - 1, ((d_in + 31) // 32,), generator=gen, device=dev,
+                                 dtype=torch.int32)
+            stride = q.row_stride(d_in, bits)
+            mats.append({"w": w, "s": s, "sign": sign, "d_in": d_in,
+                         "codes": torch.empty((d_out, stride), dtype=torch.uint8, device=dev),
+                         "norm": torch.empty((d_out,), dtype=torch.int16, device=dev),
+                         "sigma": torch.empty((d_in // 2,), dtype=torch.float32, device=dev),
+                         "out": torch.empty((d_out, d_in), dtype=torch.bfloat16, device=dev)})
+    ws = torch.empty((max(q.encode_workspace(m["w"].shape[0], m["d_in"], bits) for m in mats),), dtype=torch.uint8,
+                     device=dev)
+    status = torch.zeros((1,), dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+
+    def enc_all():
+        for m in mats:
+            q.encode(m["w"], cb, bits, index, scale=m["s"], sign_bits=m["sign"], block=block, status=status,
+                     workspace=ws, out={"codes": m["codes"], "norm": m["norm"], "sigma": m["sigma"]})
+
+    def dec_all():
+        for m in mats:
+            q.decode(m["codes"], m["norm"], m["sigma"], cb, bits, m["d_in"], scale=m["s"], sign_bits=m["sign"],
+                     block=block, out=m["out"])
+
+    def best_ms(fn, reps=3):
+        best = None
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            t = a.elapsed_time(b)
+            best = t if best is None else min(best, t)
+        return best
+
+    enc_all()
+    dec_all()
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0, "data-fault flags raised in the stack: %d" % int(status.item())
+    enc_ms = best_ms(enc_all)
+    dec_ms = best_ms(dec_all)
+    n_w = sum(m["w"].numel() for m in mats)
+    dec_bytes = sum(m["codes"].numel() + m["norm"].numel() * 2 + m["out"].numel() * 2 for m in mats)
+    res = {"matrices": len(mats), "weights": n_w, "encode_ms": round(enc_ms, 3),
+           "encode_Mweights_per_s": round(n_w / (enc_ms * 1e-3) / 1e6, 1), "decode_ms": round(dec_ms, 3),
+           "decode_GB_per_s": round(dec_bytes / (dec_ms * 1e-3) / 1e9, 1),
+           "decode_frac": round(dec_bytes / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+           "resident_GB": round((n_w * 2 + sum(m["codes"].numel() for m in mats) + n_w * 2) / 1e9, 1),
+           "data": "synthetic, drawn on the GPU; K=2048 codebook and b=128 of the step"}
+    del mats
+    torch.cuda.empty_cache()
+    return res
 
 
 if __name__ == "__main__":
