@@ -562,28 +562,17 @@ __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a, int T, int R) {
         }
         if (rv) flags |= rf;
         wave_lds_sync();
-        // pack: 32 consecutive indices fill exactly `bits` words; lane c packs chunk c of the
-        // wavefront's E chunks (the shift sequence is the same for every chunk, so the branches
-        // are uniform)
-        for (int c = lane; c < E; c += kWave) {
-            uint64_t acc = 0;
-            int nb = 0;
-            uint32_t* wp = wstage + c * bits;
-#pragma unroll
-            for (int k8 = 0; k8 < 4; ++k8) {
-                const uint4 q = *reinterpret_cast<const uint4*>(widx + 32 * c + 8 * k8);
-                const uint32_t v[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    acc |= (uint64_t)((v[u >> 1] >> (16 * (u & 1))) & 0xFFFFu) << nb;
-                    nb += bits;
-                    if (nb >= 32) {
-                        *wp++ = (uint32_t)acc;
-                        acc >>= 32;
-                        nb -= 32;
-                    }
-                }
+        // pack (LSB first): lane c builds words c, c + 64, ... of the wavefront's E * bits words,
+        // each from the few indices that overlap it, so all lanes share the work
+        for (int wd = lane; wd < E * bits; wd += kWave) {
+            const int b0 = 32 * wd;   // first bit of the word
+            uint32_t word = 0;
+            for (int i = b0 / bits; i * bits < b0 + 32; ++i) {   // at most 32 / bits + 2 indices
+                const uint32_t v = widx[i];
+                const int sh = i * bits - b0;                     // negative for an index begun earlier
+                word |= sh >= 0 ? (v << sh) : (v >> -sh);
             }
+            wstage[wd] = word;
         }
         wave_lds_sync();
         // 16-byte stores of the wavefront's 4 E bits bytes: E bits / 4 chunks, lane c storing
