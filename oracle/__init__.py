@@ -58,6 +58,11 @@ def _bind(lib):
                           ctypes.c_int),
         "oracle_decode": ([vp, vp, i64, i32, vp, vp, i32, vp, vp, i32, vp, vp, vp], ctypes.c_int),
         "oracle_lloyd": ([vp, i64, i32, i32, vp, vp, vp, vp], ctypes.c_int),
+        "oracle_rayleigh_lloyd_max": ([i32, vp, vp], ctypes.c_int),
+        "oracle_polar_index": ([f32, f32, i32, i32, vp], i32),
+        "oracle_polar_table": ([i32, i32, vp, vp], None),
+        "oracle_encode_polar": ([vp, i32, i64, i32, i64, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp],
+                                ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -198,6 +203,50 @@ class Oracle:
                                    self._p(e), self._p(st))
         assert rc == 0
         return cb, e[:iters], int(st[0])
+
+
+    # -- polar baseline (section 3.5) -----------------------------------------
+    def rayleigh_lloyd_max(self, ba):
+        na = 1 << ba
+        levels = np.empty((na,), dtype=np.float64)
+        thr = np.zeros((max(na - 1, 1),), dtype=np.float64)
+        rc = self.lib.oracle_rayleigh_lloyd_max(ba, self._p(levels), self._p(thr))
+        assert rc == 0
+        return levels, thr[: na - 1]
+
+    def polar_index(self, p, ba, bp, thresholds):
+        p = np.ascontiguousarray(p, dtype=np.float32).reshape(-1, 2)
+        thr = np.ascontiguousarray(thresholds, dtype=np.float64)
+        if thr.size == 0:
+            thr = np.zeros((1,), dtype=np.float64)
+        return np.array([self.lib.oracle_polar_index(float(x), float(y), ba, bp, self._p(thr)) for x, y in p],
+                        dtype=np.int32)
+
+    def polar_table(self, ba, bp, levels):
+        cb = np.empty((1 << (ba + bp), 2), dtype=np.float32)
+        levels = np.ascontiguousarray(levels, dtype=np.float64)
+        self.lib.oracle_polar_table(ba, bp, self._p(levels), self._p(cb))
+        return cb
+
+    def encode_polar(self, w, s, sign_bits, block, ba, bp, thresholds, sigma, want_idx=True, want_p=False):
+        w, bf = self._w(w)
+        n, d_in = w.shape
+        bits = ba + bp
+        stride = self.row_stride(d_in, bits)
+        norm = np.empty((n,), dtype=np.uint16)
+        codes = np.empty((n, stride), dtype=np.uint8)
+        idx = np.empty((n, d_in // 2), dtype=np.int32) if want_idx else None
+        p = np.empty((n, d_in), dtype=np.float32) if want_p else None
+        st = np.zeros((1,), dtype=np.int32)
+        thr = np.ascontiguousarray(thresholds, dtype=np.float64)
+        if thr.size == 0:
+            thr = np.zeros((1,), dtype=np.float64)
+        sigma = np.ascontiguousarray(sigma, dtype=np.float32)
+        rc = self.lib.oracle_encode_polar(self._p(w), bf, n, d_in, d_in, self._p(s), self._p(sign_bits), block, ba,
+                                          bp, self._p(thr), self._p(sigma), self._p(norm), self._p(codes),
+                                          self._p(idx), self._p(p), self._p(st))
+        assert rc == 0
+        return {"norm": norm, "codes": codes, "idx": idx, "p": p, "status": int(st[0])}
 
 
 _default: Optional[Oracle] = None

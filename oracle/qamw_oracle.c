@@ -34,6 +34,19 @@
  *   R7 Lloyd on a sample of points: first K points as the start, empty cells
  *      keep their centroid, sums kept as 64-bit integers of x*2^32 so that
  *      the result does not depend on summation order.
+ *   R8 polar baseline (section 3.5): the magnitude quantizer is the Na-level
+ *      Lloyd-Max quantizer of the unit Rayleigh density r exp(-r^2/2), started
+ *      from the conditional means of Na equal-probability intervals and
+ *      iterated (thresholds at the midpoints of adjacent levels, levels at the
+ *      conditional means of their intervals, integrals in closed form) until
+ *      no level moves by more than 1e-15 of itself, at most 10000 times.  A
+ *      pair's magnitude index is the number of thresholds t with
+ *      fl64(px^2 + py^2) > fl64(t^2) (the squares of the float pair are exact
+ *      in double; ties go to the lower level).  Its phase index is
+ *      floor(atan2(py, px) * Np / (2 pi) + 1/2) mod Np, the bin centred on
+ *      2 pi j / Np.  The pair's B = Ba + Bp bit index is ia + Na * ip, and the
+ *      decoder is the QAM-W decoder with the table
+ *      c[ia + Na ip] = fl32(a_ia cos(2 pi ip / Np)), fl32(a_ia sin(2 pi ip / Np)).
  */
 #include "qamw_oracle.h"
 
@@ -305,11 +318,82 @@ void oracle_unpack_row(const uint8_t* in, int32_t n_pairs, int32_t bits, int32_t
     }
 }
 
-/* Section 3.1, steps 1-6, for every row passed in. */
-int oracle_encode(const void* w, int32_t w_bf16, int64_t n_rows, int32_t d_in, int64_t ld,
-                  const float* s, const uint32_t* sign_bits, int32_t block, const float* cb,
-                  int32_t bits, const float* sigma, uint16_t* norm16, uint8_t* codes,
-                  int32_t* idx_out, float* p_out, int32_t* status)
+/* ------------------------------------------------------------------------
+ * Section 3.5: the polar baseline (reading R8). */
+
+/* Integrals of the unit Rayleigh density over [a, b] (b may be infinite):
+ * mass = exp(-a^2/2) - exp(-b^2/2);
+ * first moment = a exp(-a^2/2) - b exp(-b^2/2) + sqrt(pi/2) (erf(b/sqrt2) - erf(a/sqrt2)). */
+static double rayleigh_mass(double a, double b)
+{
+    return exp(-0.5 * a * a) - (isinf(b) ? 0.0 : exp(-0.5 * b * b));
+}
+static double rayleigh_moment(double a, double b)
+{
+    double hi = isinf(b) ? 0.0 : b * exp(-0.5 * b * b);
+    double eb = isinf(b) ? 1.0 : erf(b / sqrt(2.0));
+    return a * exp(-0.5 * a * a) - hi + sqrt(0.5 * ORACLE_PI) * (eb - erf(a / sqrt(2.0)));
+}
+
+int oracle_rayleigh_lloyd_max(int32_t ba, double* levels, double* thresholds)
+{
+    if (ba < 0 || ba > 8) return -1;
+    int32_t na = 1 << ba;
+    /* start: conditional means of na equal-probability intervals, edges at the
+     * quantiles sqrt(-2 ln(1 - i/na)) */
+    for (int i = 0; i < na; ++i) {
+        double a = sqrt(-2.0 * log(1.0 - (double)i / na));
+        double b = (i + 1 == na) ? INFINITY : sqrt(-2.0 * log(1.0 - (double)(i + 1) / na));
+        levels[i] = rayleigh_moment(a, b) / rayleigh_mass(a, b);
+    }
+    for (int it = 0; it < 10000; ++it) {
+        for (int i = 0; i + 1 < na; ++i) thresholds[i] = 0.5 * (levels[i] + levels[i + 1]);
+        int moved = 0;
+        for (int i = 0; i < na; ++i) {
+            double a = (i == 0) ? 0.0 : thresholds[i - 1];
+            double b = (i + 1 == na) ? INFINITY : thresholds[i];
+            double v = rayleigh_moment(a, b) / rayleigh_mass(a, b);
+            if (fabs(v - levels[i]) > 1e-15 * levels[i]) moved = 1;
+            levels[i] = v;
+        }
+        if (!moved) break;
+    }
+    for (int i = 0; i + 1 < na; ++i) thresholds[i] = 0.5 * (levels[i] + levels[i + 1]);
+    return 0;
+}
+
+int32_t oracle_polar_index(float px, float py, int32_t ba, int32_t bp, const double* thresholds)
+{
+    int32_t na = 1 << ba, np_ = 1 << bp;
+    double r2 = (double)px * px + (double)py * py;
+    int32_t ia = 0;
+    for (int i = 0; i + 1 < na; ++i)
+        if (r2 > thresholds[i] * thresholds[i]) ia = i + 1;
+    double th = atan2((double)py, (double)px);
+    int32_t ip = (int32_t)floor(th * np_ / (2.0 * ORACLE_PI) + 0.5);
+    ip = ((ip % np_) + np_) % np_;
+    return ia + na * ip;
+}
+
+void oracle_polar_table(int32_t ba, int32_t bp, const double* levels, float* cb)
+{
+    int32_t na = 1 << ba, np_ = 1 << bp;
+    for (int ip = 0; ip < np_; ++ip) {
+        double th = 2.0 * ORACLE_PI * ip / np_;
+        for (int ia = 0; ia < na; ++ia) {
+            cb[2 * (ia + na * ip)] = (float)(levels[ia] * cos(th));
+            cb[2 * (ia + na * ip) + 1] = (float)(levels[ia] * sin(th));
+        }
+    }
+}
+
+/* Section 3.1, steps 1-6, for every row passed in; step 5 is the nearest
+ * codeword of cb (QAM-W, section 3.6) or, when thresholds is given, the polar
+ * index (section 3.5, reading R8) with bits = ba + bp. */
+static int encode_rows(const void* w, int32_t w_bf16, int64_t n_rows, int32_t d_in, int64_t ld,
+                       const float* s, const uint32_t* sign_bits, int32_t block, const float* cb,
+                       int32_t bits, const double* thresholds, int32_t ba, const float* sigma,
+                       uint16_t* norm16, uint8_t* codes, int32_t* idx_out, float* p_out, int32_t* status)
 {
     if (check_block(d_in, block) || ld < d_in || n_rows < 0 || bits < 1 || bits > 16) return -1;
     int32_t K = 1 << bits, n_pairs = d_in / 2;
@@ -335,7 +419,8 @@ int oracle_encode(const void* w, int32_t w_bf16, int64_t n_rows, int32_t d_in, i
                     p_out[i * d_in + 2 * k] = px;
                     p_out[i * d_in + 2 * k + 1] = py;
                 }
-                idx[k] = oracle_nearest(px, py, cb, K, NULL); /* step 5 */
+                idx[k] = thresholds ? oracle_polar_index(px, py, ba, bits - ba, thresholds) /* step 5 */
+                                    : oracle_nearest(px, py, cb, K, NULL);
             }
             nh = oracle_f16_from_f32((float)r); /* section 3.2: 16-bit row norm */
             if ((nh & 0x7fffu) == 0x7c00u) f |= ORACLE_FLAG_NORM_RANGE;
@@ -354,6 +439,25 @@ int oracle_encode(const void* w, int32_t w_bf16, int64_t n_rows, int32_t d_in, i
     free(H);
     if (status) *status |= flags;
     return 0;
+}
+
+int oracle_encode(const void* w, int32_t w_bf16, int64_t n_rows, int32_t d_in, int64_t ld,
+                  const float* s, const uint32_t* sign_bits, int32_t block, const float* cb,
+                  int32_t bits, const float* sigma, uint16_t* norm16, uint8_t* codes,
+                  int32_t* idx_out, float* p_out, int32_t* status)
+{
+    return encode_rows(w, w_bf16, n_rows, d_in, ld, s, sign_bits, block, cb, bits, NULL, 0, sigma, norm16,
+                       codes, idx_out, p_out, status);
+}
+
+int oracle_encode_polar(const void* w, int32_t w_bf16, int64_t n_rows, int32_t d_in, int64_t ld,
+                        const float* s, const uint32_t* sign_bits, int32_t block, int32_t ba, int32_t bp,
+                        const double* thresholds, const float* sigma, uint16_t* norm16, uint8_t* codes,
+                        int32_t* idx_out, float* p_out, int32_t* status)
+{
+    if (ba < 1 || bp < 1 || ba + bp > 16) return -1;
+    return encode_rows(w, w_bf16, n_rows, d_in, ld, s, sign_bits, block, NULL, ba + bp, thresholds, ba, sigma,
+                       norm16, codes, idx_out, p_out, status);
 }
 
 /* Section 3.2: unpack, look up, rescale by sigma_k, reassemble pairs, apply

@@ -58,6 +58,14 @@ int oracle_decode(const uint8_t* codes, const uint16_t* norm16, int64_t n_rows, 
                   double* out_f64);
 int oracle_lloyd(const float* pts, int64_t n, int32_t bits, int32_t iters, const float* init,
                  float* cb, int64_t* e_trace, int32_t* status);
+/* section 3.5, the polar baseline (reading R8) */
+int oracle_rayleigh_lloyd_max(int32_t ba, double* levels, double* thresholds);
+int32_t oracle_polar_index(float px, float py, int32_t ba, int32_t bp, const double* thresholds);
+void oracle_polar_table(int32_t ba, int32_t bp, const double* levels, float* cb);
+int oracle_encode_polar(const void* w, int32_t w_bf16, int64_t n_rows, int32_t d_in, int64_t ld,
+                        const float* s, const uint32_t* sign_bits, int32_t block, int32_t ba, int32_t bp,
+                        const double* thresholds, const float* sigma, uint16_t* norm16, uint8_t* codes,
+                        int32_t* idx_out, float* p_out, int32_t* status);
 
 #ifdef __cplusplus
 }

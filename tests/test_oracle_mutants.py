@@ -1,5 +1,5 @@
 """Planted mistakes: each variant of the oracle below carries one plausible bug, and the pins in
-test_oracle_pins.py must catch every one of them.  Variants are compiled from a patched copy of the
+test_oracle_pins.py (test_oracle_polar.py for the polar baseline) must catch every one of them.  Variants are compiled from a patched copy of the
 oracle source in a temporary directory; the oracle itself is never modified."""
 import os
 import subprocess
@@ -38,11 +38,23 @@ MUTANTS = [
     ("block cap 512", "while (b < 1024 && d_in % (2 * b) == 0)", "while (b < 512 && d_in % (2 * b) == 0)"),
     ("bpw norm bits", "return bits / 2.0 + 16.0 / d_in;", "return bits / 2.0 + 32.0 / d_in;"),
     ("stored norm not rounded via float", "nh = oracle_f16_from_f32((float)r);", "nh = oracle_f16_from_f32((float)(r * 1.001));"),
+    # polar baseline (section 3.5): caught by test_oracle_polar.py
+    ("Rayleigh moment without the erf term", "- hi + sqrt(0.5 * ORACLE_PI) * (eb - erf(a / sqrt(2.0)));", "- hi;",
+     "test_oracle_polar.py"),
+    ("phase index truncated", "floor(th * np_ / (2.0 * ORACLE_PI) + 0.5)", "floor(th * np_ / (2.0 * ORACLE_PI))",
+     "test_oracle_polar.py"),
+    ("magnitude compared unsquared", "if (r2 > thresholds[i] * thresholds[i]) ia = i + 1;",
+     "if (r2 > thresholds[i]) ia = i + 1;", "test_oracle_polar.py"),
+    ("polar index layout swapped", "return ia + na * ip;", "return ip + np_ * ia;", "test_oracle_polar.py"),
+    ("polar table angle off by half a bin", "double th = 2.0 * ORACLE_PI * ip / np_;",
+     "double th = 2.0 * ORACLE_PI * (ip + 0.5) / np_;", "test_oracle_polar.py"),
 ]
 
 
-@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
-def test_pins_catch_planted_mistake(tmp_path, name, old, new):
+@pytest.mark.parametrize("mutant", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_planted_mistake(tmp_path, mutant):
+    name, old, new = mutant[:3]
+    pins = mutant[3] if len(mutant) > 3 else "test_oracle_pins.py"
     import oracle
     src = open(SRC).read()
     assert src.count(old) == 1, "mutation anchor must be unique: %r" % old
@@ -52,6 +64,6 @@ def test_pins_catch_planted_mistake(tmp_path, name, old, new):
     oracle.compile_to(str(variant), lib)
     env = dict(os.environ, ORACLE_LIB=lib, OMP_NUM_THREADS="4")
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                        os.path.join(ROOT, "tests", pins)],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, "planted mistake '%s' passed every pin:\n%s" % (name, r.stdout[-2000:])
