@@ -44,7 +44,10 @@
  *      fl64(px^2 + py^2) > fl64(t^2) (the squares of the float pair are exact
  *      in double; ties go to the lower level).  Its phase index is
  *      floor(atan2(py, px) * Np / (2 pi) + 1/2) mod Np, the bin centred on
- *      2 pi j / Np.  The pair's B = Ba + Bp bit index is ia + Na * ip, and the
+ *      2 pi j / Np; a pair at the origin (either sign of zero) has phase
+ *      index 0, since the sign of a zero out of the transform depends on the
+ *      order of its additions, which the method leaves open.  The pair's
+ *      B = Ba + Bp bit index is ia + Na * ip, and the
  *      decoder is the QAM-W decoder with the table
  *      c[ia + Na ip] = fl32(a_ia cos(2 pi ip / Np)), fl32(a_ia sin(2 pi ip / Np)).
  */
@@ -369,9 +372,12 @@ int32_t oracle_polar_index(float px, float py, int32_t ba, int32_t bp, const dou
     int32_t ia = 0;
     for (int i = 0; i + 1 < na; ++i)
         if (r2 > thresholds[i] * thresholds[i]) ia = i + 1;
-    double th = atan2((double)py, (double)px);
-    int32_t ip = (int32_t)floor(th * np_ / (2.0 * ORACLE_PI) + 0.5);
-    ip = ((ip % np_) + np_) % np_;
+    int32_t ip = 0;
+    if (r2 > 0.0) {
+        double th = atan2((double)py, (double)px);
+        ip = (int32_t)floor(th * np_ / (2.0 * ORACLE_PI) + 0.5);
+        ip = ((ip % np_) + np_) % np_;
+    }
     return ia + na * ip;
 }
 

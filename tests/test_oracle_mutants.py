@@ -46,6 +46,8 @@ MUTANTS = [
     ("magnitude compared unsquared", "if (r2 > thresholds[i] * thresholds[i]) ia = i + 1;",
      "if (r2 > thresholds[i]) ia = i + 1;", "test_oracle_polar.py"),
     ("polar index layout swapped", "return ia + na * ip;", "return ip + np_ * ia;", "test_oracle_polar.py"),
+    ("zero pair phase from atan2 of signed zeros", "    if (r2 > 0.0) {\n        double th", "    if (1) {\n        double th",
+     "test_oracle_polar.py"),
     ("polar table angle off by half a bin", "double th = 2.0 * ORACLE_PI * ip / np_;",
      "double th = 2.0 * ORACLE_PI * (ip + 0.5) / np_;", "test_oracle_polar.py"),
 ]

@@ -63,7 +63,8 @@ def test_levels_match_lloyd_on_samples(orc, ba):
 def test_polar_index_is_nearest_level_and_nearest_phase(orc, ba, bp):
     rng = np.random.default_rng(ba * 16 + bp)
     p = (rng.standard_normal((4000, 2)) * 1.3).astype(np.float32)
-    p[:8] = [[0, 0], [1, 0], [0, 1], [-1, 0], [0, -1], [1e-30, -1e-30], [5, 5], [-3, 1e-6]]
+    p[:11] = [[0, 0], [1, 0], [0, 1], [-1, 0], [0, -1], [1e-30, -1e-30], [5, 5], [-3, 1e-6],
+              [-0.0, 0.0], [-0.0, -0.0], [0.0, -0.0]]   # a zero pair has phase 0 whatever its signs
     levels, thr = orc.rayleigh_lloyd_max(ba)
     idx = orc.polar_index(p, ba, bp, thr)
     na, n_ph = 1 << ba, 1 << bp
