@@ -45,7 +45,8 @@ enum {
     QAMW_FLAG_NONFINITE = 1,   /* w_ij * s_j or the row norm is not finite                    */
     QAMW_FLAG_BAD_SCALE = 2,   /* some s_j <= 0 or NaN                                        */
     QAMW_FLAG_NORM_RANGE = 4,  /* the row norm overflows f16                                  */
-    QAMW_FLAG_POINT_RANGE = 8  /* a training point is non-finite or out of the fixed-point range */
+    QAMW_FLAG_POINT_RANGE = 8, /* a training point is non-finite or out of the fixed-point range */
+    QAMW_FLAG_BAD_THRESHOLDS = 16 /* polar thresholds not finite, >= 0 and non-decreasing        */
 };
 
 /* Bytes per row of the packed index stream: ceil((d_in/2) * bits / 8) rounded up to 16.
@@ -152,6 +153,47 @@ int qamw_decode(const uint8_t* d_codes, const uint16_t* d_norm_f16, const float*
                 const float* d_codebook, int32_t bits, const float* d_scale,
                 const uint32_t* d_sign_bits, int32_t d_out, int32_t d_in, int32_t block,
                 void* d_out_w, qamw_dtype out_dtype, int64_t ld_out, void* stream);
+
+/* Section 3.5 (the polar baseline QAM-W is compared with): a pair is coded as a magnitude level
+ * times a phase.  The magnitude quantizer is the Na = 2^ba level Lloyd-Max quantizer of the unit
+ * Rayleigh density r exp(-r^2/2) (the modulus of a circular standard Gaussian pair, the
+ * distribution the rotated, sigma-scaled pairs follow by section 3.4): started from the
+ * conditional means of Na equal-probability cells, thresholds at midpoints of adjacent levels and
+ * levels at the conditional means of their cells, in fp64, until no level moves by more than
+ * 1e-15 of itself or for 10000 rounds.  The phase has Np = 2^bp uniform bins centred on
+ * 2 pi j / Np.  Writes, on the stream:
+ *   d_levels      Na doubles, increasing;
+ *   d_thresholds  Na - 1 doubles, t_i = (a_i + a_i+1) / 2;
+ *   d_codebook    Na * Np interleaved fp32 pairs, entry ia + Na ip =
+ *                 (fl32(a_ia cos(2 pi ip / Np)), fl32(a_ia sin(2 pi ip / Np))): the table that
+ *                 qamw_decode reads with bits = ba + bp.
+ * Limits: 1 <= ba <= 8, bp >= 1, ba + bp <= 12 (QAMW_ERR_UNSUPPORTED above, QAMW_ERR_ARG for
+ * ba or bp < 1 or ba + bp > 16).  Device pointers, 8-byte aligned, owned by the caller. */
+int qamw_polar_codebook(int32_t ba, int32_t bp, double* d_levels, double* d_thresholds, float* d_codebook,
+                        void* stream);
+
+/* Section 3.5: polar indices of n 2D points (fp32, interleaved) into d_idx (int32): the index
+ * ia + Na ip that qamw_encode_polar gives a scaled pair (rule below), with the thresholds of
+ * qamw_polar_codebook.  Limits as qamw_polar_codebook; d_status (may be NULL) receives
+ * QAMW_FLAG_BAD_THRESHOLDS. */
+int qamw_polar_index(const float* d_points, int64_t n, int32_t ba, int32_t bp, const double* d_thresholds,
+                     int32_t* d_idx, int32_t* d_status, void* stream);
+
+/* Section 3.5: the encoder of qamw_encode (same front end, calibration, norms, packing,
+ * arguments and limits) with the polar quantizer in place of the nearest-codeword search.  With
+ * p the scaled pair:
+ *   ia = #{i : fl64(t_i^2) < fl64(px^2 + py^2)}                 (the nearest level)
+ *   ip = floor(atan2(py, px) Np / (2 pi) + 1/2) mod Np          (the nearest bin centre),
+ *        0 for a pair at the origin, decided up to rounding at a bin edge
+ *   index = ia + Na ip, packed with bits = ba + bp.
+ * d_thresholds: Na - 1 device doubles, finite, >= 0 and non-decreasing (as qamw_polar_codebook
+ * writes them); otherwise QAMW_FLAG_BAD_THRESHOLDS is set and the indices are unspecified.
+ * Decode with qamw_decode, the table of qamw_polar_codebook and bits = ba + bp. */
+int qamw_encode_polar(const void* d_w, qamw_dtype w_dtype, int32_t d_out, int32_t d_in, int64_t ld_w,
+                      const float* d_scale, const uint32_t* d_sign_bits, int32_t block, int32_t ba, int32_t bp,
+                      const double* d_thresholds, const float* d_sigma_in, float* d_sigma_out,
+                      uint16_t* d_norm_f16, uint8_t* d_codes, int32_t* d_status, void* d_ws, size_t ws_bytes,
+                      void* stream);
 
 /* Human-readable text for a return code. */
 const char* qamw_status_string(int code);

@@ -22,7 +22,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = q.header_symbols()
-    assert len(names) == 11
+    assert len(names) == 14
     out = subprocess.run(["nm", "-D", "--defined-only", q.LIB_PATH], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
     for n in names:
@@ -135,3 +135,34 @@ def test_product_path_does_not_use_the_oracle():
             if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
                 text = open(os.path.join(root, f)).read()
                 assert "oracle" not in text.lower(), f
+
+
+def _encp(lib, **kw):
+    a = dict(w=FAKE, dt=q.BF16, d_out=16, d_in=256, ld=256, scale=None, sign=None, block=64, ba=5, bp=6, thr=FAKE,
+             sig_in=FAKE, sig_out=None, norm=FAKE, codes=FAKE, status=None, ws=None, ws_bytes=0)
+    a.update(kw)
+    return lib.qamw_encode_polar(a["w"], a["dt"], a["d_out"], a["d_in"], a["ld"], a["scale"], a["sign"], a["block"],
+                                 a["ba"], a["bp"], a["thr"], a["sig_in"], a["sig_out"], a["norm"], a["codes"],
+                                 a["status"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ba=0), ARG), (dict(bp=0), ARG), (dict(ba=9, bp=1), UNSUP), (dict(ba=6, bp=7), UNSUP),
+    (dict(ba=8, bp=9), ARG), (dict(thr=None), ARG), (dict(thr=FAKE + 4), ARG), (dict(d_in=255, ld=255), ARG),
+    (dict(w=None), ARG), (dict(codes=FAKE + 2), ARG), (dict(sig_in=None, sig_out=FAKE, ws=None), WS),
+    (dict(d_in=24, ld=24, block=8), UNSUP),
+])
+def test_encode_polar_rejects(lib, kw, code):
+    assert _encp(lib, **kw) == code
+
+
+def test_polar_codebook_and_index_reject(lib):
+    assert lib.qamw_polar_codebook(0, 4, FAKE, FAKE, FAKE, None) == ARG
+    assert lib.qamw_polar_codebook(9, 1, FAKE, FAKE, FAKE, None) == UNSUP
+    assert lib.qamw_polar_codebook(4, 9, FAKE, FAKE, FAKE, None) == UNSUP
+    assert lib.qamw_polar_codebook(4, 4, None, FAKE, FAKE, None) == ARG
+    assert lib.qamw_polar_codebook(4, 4, FAKE, FAKE + 4, FAKE, None) == ARG
+    assert lib.qamw_polar_index(FAKE, -1, 4, 4, FAKE, FAKE, None, None) == ARG
+    assert lib.qamw_polar_index(FAKE, 10, 4, 4, None, FAKE, None, None) == ARG
+    assert lib.qamw_polar_index(FAKE + 4, 10, 4, 4, FAKE, FAKE, None, None) == ARG
+    assert lib.qamw_polar_index(None, 0, 4, 4, None, None, None, None) == q.OK

@@ -25,7 +25,7 @@ HEADER_PATH = os.path.join(ROOT, "include", "qamw.h")
 
 F32, BF16 = 0, 1
 OK, ERR_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
-FLAG_NONFINITE, FLAG_BAD_SCALE, FLAG_NORM_RANGE, FLAG_POINT_RANGE = 1, 2, 4, 8
+FLAG_NONFINITE, FLAG_BAD_SCALE, FLAG_NORM_RANGE, FLAG_POINT_RANGE, FLAG_BAD_THRESHOLDS = 1, 2, 4, 8, 16
 
 
 class QamwError(RuntimeError):
@@ -59,6 +59,10 @@ def load(path: Optional[str] = None):
         "qamw_encode": ([vp, ctypes.c_int, i32, i32, i64, vp, vp, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp],
                         ctypes.c_int),
         "qamw_decode": ([vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, vp, ctypes.c_int, i64, vp], ctypes.c_int),
+        "qamw_polar_codebook": ([i32, i32, vp, vp, vp, vp], ctypes.c_int),
+        "qamw_polar_index": ([vp, i64, i32, i32, vp, vp, vp, vp], ctypes.c_int),
+        "qamw_encode_polar": ([vp, ctypes.c_int, i32, i32, i64, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz,
+                               vp], ctypes.c_int),
         "qamw_status_string": ([ctypes.c_int], ctypes.c_char_p),
     }
     for name, (args, res) in sig.items():
@@ -169,12 +173,7 @@ def nearest(points: torch.Tensor, codebook: torch.Tensor, bits: int, index: torc
     return out
 
 
-def encode(w: torch.Tensor, codebook: torch.Tensor, bits: int, index: torch.Tensor,
-           scale: Optional[torch.Tensor] = None, sign_bits: Optional[torch.Tensor] = None, block: int = 0,
-           sigma: Optional[torch.Tensor] = None, status: Optional[torch.Tensor] = None,
-           workspace: Optional[torch.Tensor] = None, out: Optional[Dict[str, torch.Tensor]] = None
-           ) -> Dict[str, torch.Tensor]:
-    """Encode W (d_out x d_in, bf16 or fp32) -> {codes, norm (int16 bit patterns of f16), sigma}."""
+def _encode_buffers(w, bits, scale, sign_bits, sigma, workspace, out):
     if w.dtype not in (torch.bfloat16, torch.float32) or not w.is_cuda or w.dim() != 2:
         raise ValueError("w must be a 2-D bf16 or fp32 device tensor")
     d_out, d_in = w.shape
@@ -205,11 +204,63 @@ def encode(w: torch.Tensor, codebook: torch.Tensor, bits: int, index: torch.Tens
     ws = workspace
     if ws is None and sigma is None:
         ws = _ws(encode_workspace(d_out, d_in, bits), dev)
+    return d_out, d_in, ld, codes, norm, sig_out, ws
+
+
+def encode(w: torch.Tensor, codebook: torch.Tensor, bits: int, index: torch.Tensor,
+           scale: Optional[torch.Tensor] = None, sign_bits: Optional[torch.Tensor] = None, block: int = 0,
+           sigma: Optional[torch.Tensor] = None, status: Optional[torch.Tensor] = None,
+           workspace: Optional[torch.Tensor] = None, out: Optional[Dict[str, torch.Tensor]] = None
+           ) -> Dict[str, torch.Tensor]:
+    """Encode W (d_out x d_in, bf16 or fp32) -> {codes, norm (int16 bit patterns of f16), sigma}."""
+    d_out, d_in, ld, codes, norm, sig_out, ws = _encode_buffers(w, bits, scale, sign_bits, sigma, workspace, out)
     rc = load().qamw_encode(_ptr(w), BF16 if w.dtype == torch.bfloat16 else F32, d_out, d_in, ld,
                             _ptr(scale), _ptr(sign_bits), block, _ptr(codebook), bits, _ptr(index), _ptr(sigma),
                             _ptr(sig_out), _ptr(norm), _ptr(codes), _ptr(status), _ptr(ws),
                             0 if ws is None else ws.numel(), _stream())
     _check(rc, "qamw_encode")
+    return {"codes": codes, "norm": norm, "sigma": sigma if sigma is not None else sig_out}
+
+
+def polar_codebook(ba: int, bp: int, device=None):
+    """Polar baseline (section 3.5): (levels float64[2^ba], thresholds float64[2^ba - 1],
+    table float32[2^(ba+bp), 2]) on the current (or given) device."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    na = 1 << ba
+    levels = torch.empty((na,), dtype=torch.float64, device=dev)
+    thr = torch.empty((max(na - 1, 1),), dtype=torch.float64, device=dev)
+    table = torch.empty((na << bp, 2), dtype=torch.float32, device=dev)
+    rc = load().qamw_polar_codebook(ba, bp, _ptr(levels), _ptr(thr), _ptr(table), _stream())
+    _check(rc, "qamw_polar_codebook")
+    return levels, thr[: na - 1], table
+
+
+def polar_index(points: torch.Tensor, ba: int, bp: int, thresholds: torch.Tensor,
+                status: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Polar indices (section 3.5) of n fp32 pairs (n x 2)."""
+    _dev(points, torch.float32, "points")
+    _dev(thresholds, torch.float64, "thresholds")
+    n = points.numel() // 2
+    out = torch.empty((n,), dtype=torch.int32, device=points.device)
+    rc = load().qamw_polar_index(_ptr(points), n, ba, bp, _ptr(thresholds), _ptr(out), _ptr(status), _stream())
+    _check(rc, "qamw_polar_index")
+    return out
+
+
+def encode_polar(w: torch.Tensor, ba: int, bp: int, thresholds: torch.Tensor,
+                 scale: Optional[torch.Tensor] = None, sign_bits: Optional[torch.Tensor] = None, block: int = 0,
+                 sigma: Optional[torch.Tensor] = None, status: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None, out: Optional[Dict[str, torch.Tensor]] = None
+                 ) -> Dict[str, torch.Tensor]:
+    """Polar-baseline encode (section 3.5); decode with `decode(..., table, ba + bp, ...)`."""
+    _dev(thresholds, torch.float64, "thresholds")
+    bits = ba + bp
+    d_out, d_in, ld, codes, norm, sig_out, ws = _encode_buffers(w, bits, scale, sign_bits, sigma, workspace, out)
+    rc = load().qamw_encode_polar(_ptr(w), BF16 if w.dtype == torch.bfloat16 else F32, d_out, d_in, ld,
+                                  _ptr(scale), _ptr(sign_bits), block, ba, bp, _ptr(thresholds), _ptr(sigma),
+                                  _ptr(sig_out), _ptr(norm), _ptr(codes), _ptr(status), _ptr(ws),
+                                  0 if ws is None else ws.numel(), _stream())
+    _check(rc, "qamw_encode_polar")
     return {"codes": codes, "norm": norm, "sigma": sigma if sigma is not None else sig_out}
 
 

@@ -438,6 +438,7 @@ __device__ __forceinline__ void load_row_raw(const void* w, int64_t ld, int d_in
 // Per pass: front end (scale, norm, transform), pairs, lockstep search in batches of four pairs
 // per lane, indices to LDS, then each wavefront packs and stores its part of the row.
 constexpr int kSearchBatch = 4;
+constexpr int kPolarBatch = 2;   // pairs per polar batch: 4 spills registers
 
 // LDS bytes per wavefront of the encoder.  A wavefront's lanes cover 32 E consecutive pairs of
 // the row, so it packs and stores its own part of the row: its buffer holds the exchange during
@@ -449,7 +450,7 @@ __host__ __device__ inline size_t encode_wave_bytes(int E, bool two_phase, int b
     return xch > pack ? xch : pack;
 }
 
-template <int L, int MAXT, bool BF, bool VEC, bool ISG_LDS>
+template <int L, int MAXT, bool BF, bool VEC, bool ISG_LDS, bool POLAR>
 __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a, int T, int R) {
     using Lo = Layout<L>;
     constexpr int E = Lo::E, NP = E / 2;
@@ -457,12 +458,22 @@ __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a, int T, int R) {
     const int K = 1 << a.bits;
     const int grp = __builtin_amdgcn_readfirstlane(threadIdx.x / T);
     const int tid = threadIdx.x - grp * T, nwaves = T / kWave;
+    // the quantizer's tables: the QAM-W search image (section 3.6) or the polar tables (3.5)
     const char* index = reinterpret_cast<const char*>(a.index);
-    const IndexHeader ih = *reinterpret_cast<const IndexHeader*>(index);
-    const SearchLds sl = search_lds_carve(smem, K, ih, index);
+    SearchLds sl{};
+    PolarLds pl{};
+    size_t front;
+    if constexpr (POLAR) {
+        pl = polar_lds_carve(smem, a.ba, a.bits - a.ba);
+        front = polar_lds_bytes(a.bits - a.ba);
+    } else {
+        const IndexHeader ih = *reinterpret_cast<const IndexHeader*>(index);
+        sl = search_lds_carve(smem, K, ih, index);
+        front = search_lds_bytes(K, ih.G);
+    }
     // norm partials, double-buffered by pass parity ([2][R][kMaxWaves]): a wavefront may reach
     // the next pass's front end while others still read this pass's partials
-    double* red_all = reinterpret_cast<double*>(smem + search_lds_bytes(K, ih.G));
+    double* red_all = reinterpret_cast<double*>(smem + front);
     const int wave_bytes = (int)encode_wave_bytes(E, Lo::two_phase, a.bits);
     char* wbuf = reinterpret_cast<char*>(red_all + 2 * R * kMaxWaves) + (threadIdx.x / kWave) * wave_bytes;
     double* xb = reinterpret_cast<double*>(wbuf);
@@ -484,9 +495,13 @@ __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a, int T, int R) {
     // the prefetched row can leave the previous row's stores in flight.
     RawW<E, BF> nxt;
     load_row_raw<E, BF, VEC>(a.w, a.ld, a.d_in, a.d_out, base + grp, tid, nxt);
-    search_lds_fill(sl, index, K, threadIdx.x, blockDim.x);
-
     int32_t flags = 0;
+    if constexpr (POLAR) {
+        if (polar_lds_fill(pl, a.thr, threadIdx.x, blockDim.x) && blockIdx.x == 0) flags |= 16;
+    } else {
+        search_lds_fill(sl, index, K, threadIdx.x, blockDim.x);
+    }
+
     float cf[E];   // s_j * eps_j, exact in fp32
     bool bad_scale = false;
     load_cf<E>(a.scale, a.sign, tid, a.d_in, cf, bad_scale);
@@ -551,7 +566,25 @@ __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a, int T, int R) {
                     bx[i] = px[h * kSearchBatch + i];
                     by[i] = py[h * kSearchBatch + i];
                 }
-                if (nonzero) nearest_lds_batch<kSearchBatch>(bx, by, sl, bi);
+                if (nonzero) {
+                    if constexpr (POLAR) {
+#pragma unroll
+                        for (int g = 0; g < kSearchBatch; g += kPolarBatch) {
+                            float gx[kPolarBatch], gy[kPolarBatch];
+                            int gi[kPolarBatch];
+#pragma unroll
+                            for (int i = 0; i < kPolarBatch; ++i) {
+                                gx[i] = bx[g + i];
+                                gy[i] = by[g + i];
+                            }
+                            polar_batch<kPolarBatch>(gx, gy, pl, gi);
+#pragma unroll
+                            for (int i = 0; i < kPolarBatch; ++i) bi[g + i] = gi[i];
+                        }
+                    } else {
+                        nearest_lds_batch<kSearchBatch>(bx, by, sl, bi);
+                    }
+                }
 #pragma unroll
                 for (int i = 0; i < kSearchBatch; ++i)
                     idx_l[(h * kSearchBatch + i) * (Lo::two_phase ? Lo::lanes : 1)] = nonzero ? (uint16_t)bi[i] : (uint16_t)0;
@@ -604,13 +637,16 @@ __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a, int T, int R) {
 // LDS of the encoder: search image, R * kMaxWaves norm partials, and one region holding either
 // the exchange buffers (one per wavefront) or the R groups' indices and packed words.
 template <int L>
-size_t encode_smem(int K, int R, int nwaves_total, bool isg_lds) {
+size_t encode_smem(size_t front, int bits, int R, int nwaves_total, bool isg_lds) {
     using Lo = Layout<L>;
-    int bits = 0;
-    while ((1 << bits) < K) ++bits;
     const size_t isg = isg_lds ? (size_t)(nwaves_total / R) * kWave * (Lo::E / 2) * sizeof(double) : 0;
-    return search_lds_bytes(K, index_grid_size(bits)) + (size_t)2 * R * kMaxWaves * sizeof(double) +
+    return front + (size_t)2 * R * kMaxWaves * sizeof(double) +
            (size_t)nwaves_total * encode_wave_bytes(Lo::E, Lo::two_phase, bits) + isg;
+}
+
+// LDS of the quantizer's tables
+inline size_t encode_front_bytes(const EncodeArgs& a) {
+    return a.thr ? polar_lds_bytes(a.bits - a.ba) : search_lds_bytes(1 << a.bits, index_grid_size(a.bits));
 }
 
 // R * kMaxWaves norm partials, then the exchange buffers (at least d_in/2 doubles: they also
@@ -623,12 +659,19 @@ size_t calib_smem(int R, int nwaves) {
     return (size_t)R * kMaxWaves * sizeof(double) + (xb > comb ? xb : comb);
 }
 
-template <int L, bool BF, bool VEC>
-hipError_t encode_LBV(const EncodeArgs& a, hipStream_t st) {
+template <int L, int MT, bool BF, bool VEC, bool ISG, bool POLAR>
+hipError_t encode_launch(const EncodeArgs& a, int grid, int threads, size_t smem, int T, int R, hipStream_t st) {
+    allow_lds(k_encode<L, MT, BF, VEC, ISG, POLAR>, smem);
+    hipLaunchKernelGGL((k_encode<L, MT, BF, VEC, ISG, POLAR>), dim3(grid), dim3(threads), smem, st, a, T, R);
+    return hipGetLastError();
+}
+
+template <int L, bool BF, bool VEC, bool POLAR>
+hipError_t encode_LBVP(const EncodeArgs& a, hipStream_t st) {
     using Lo = Layout<L>;
     const int T = ((a.d_in / Lo::E) + kWave - 1) / kWave * kWave;
     if (T > 1024 || (T > 512 && L > 7)) return hipErrorInvalidConfiguration;
-    const int K = 1 << a.bits;
+    const size_t front = encode_front_bytes(a);
     auto grid_for = [&](int R, int threads, size_t smem) {
         int per_cu = (int)(kLdsBytes / smem);
         if (per_cu * (threads / kWave) > 32) per_cu = 32 / (threads / kWave);
@@ -641,15 +684,13 @@ hipError_t encode_LBV(const EncodeArgs& a, hipStream_t st) {
         int R = 1024 / T;
         if (R > 4) R = 4;
         if (R > a.d_out) R = a.d_out > 0 ? a.d_out : 1;
-        while (R > 1 && encode_smem<L>(K, R, R * T / kWave, true) > kLdsBytes) --R;
+        while (R > 1 && encode_smem<L>(front, a.bits, R, R * T / kWave, true) > kLdsBytes) --R;
         const int threads = R * T;
-        const size_t smem = encode_smem<L>(K, R, threads / kWave, true);
+        const size_t smem = encode_smem<L>(front, a.bits, R, threads / kWave, true);
         if (smem <= kLdsBytes) {
             const int grid = grid_for(R, threads, smem);
             if (grid < 1) return hipSuccess;
-            allow_lds(k_encode<L, 1024, BF, VEC, true>, smem);
-            hipLaunchKernelGGL((k_encode<L, 1024, BF, VEC, true>), dim3(grid), dim3(threads), smem, st, a, T, R);
-            return hipGetLastError();
+            return encode_launch<L, 1024, BF, VEC, true, POLAR>(a, grid, threads, smem, T, R, st);
         }
     }
     // 1 / sigma in registers
@@ -657,27 +698,23 @@ hipError_t encode_LBV(const EncodeArgs& a, hipStream_t st) {
     int R = T >= kMax ? 1 : kMax / T;
     if (R > 4) R = 4;
     if (R > a.d_out) R = a.d_out > 0 ? a.d_out : 1;
-    while (R > 1 && encode_smem<L>(K, R, R * T / kWave, false) > kLdsBytes) --R;
+    while (R > 1 && encode_smem<L>(front, a.bits, R, R * T / kWave, false) > kLdsBytes) --R;
     const int threads = R * T;
-    const size_t smem = encode_smem<L>(K, R, threads / kWave, false);
+    const size_t smem = encode_smem<L>(front, a.bits, R, threads / kWave, false);
     if (smem > kLdsBytes) return hipErrorInvalidConfiguration;
     const int grid = grid_for(R, threads, smem);
     if (grid < 1) return hipSuccess;
-    if (threads <= 512) {
-        allow_lds(k_encode<L, 512, BF, VEC, false>, smem);
-        hipLaunchKernelGGL((k_encode<L, 512, BF, VEC, false>), dim3(grid), dim3(threads), smem, st, a, T, R);
-    } else if constexpr (L <= 7) {
-        if (threads <= 768) {
-            allow_lds(k_encode<L, 768, BF, VEC, false>, smem);
-            hipLaunchKernelGGL((k_encode<L, 768, BF, VEC, false>), dim3(grid), dim3(threads), smem, st, a, T, R);
-        } else {
-            allow_lds(k_encode<L, 1024, BF, VEC, false>, smem);
-            hipLaunchKernelGGL((k_encode<L, 1024, BF, VEC, false>), dim3(grid), dim3(threads), smem, st, a, T, R);
-        }
-    } else {
-        return hipErrorInvalidConfiguration;
+    if (threads <= 512) return encode_launch<L, 512, BF, VEC, false, POLAR>(a, grid, threads, smem, T, R, st);
+    if constexpr (L <= 7) {
+        if (threads <= 768) return encode_launch<L, 768, BF, VEC, false, POLAR>(a, grid, threads, smem, T, R, st);
+        return encode_launch<L, 1024, BF, VEC, false, POLAR>(a, grid, threads, smem, T, R, st);
     }
-    return hipGetLastError();
+    return hipErrorInvalidConfiguration;
+}
+
+template <int L, bool BF, bool VEC>
+hipError_t encode_LBV(const EncodeArgs& a, hipStream_t st) {
+    return a.thr ? encode_LBVP<L, BF, VEC, true>(a, st) : encode_LBVP<L, BF, VEC, false>(a, st);
 }
 
 template <int L, bool BF>
@@ -745,12 +782,12 @@ int lane_elems(int L) {
     }
 }
 
-size_t encode_lds_bytes(int L, int bits, int d_in) {
+size_t encode_lds_bytes(int L, int bits, int d_in, int polar_bp) {
     const int E = lane_elems(L);
     if (E <= 0) return 0;
     const int nwaves = ((d_in / E) + kWave - 1) / kWave;
-    return search_lds_bytes(1 << bits, index_grid_size(bits)) + 2 * kMaxWaves * sizeof(double) +
-           (size_t)nwaves * encode_wave_bytes(E, L > 4, bits);
+    const size_t front = polar_bp >= 1 ? polar_lds_bytes(polar_bp) : search_lds_bytes(1 << bits, index_grid_size(bits));
+    return front + 2 * kMaxWaves * sizeof(double) + (size_t)nwaves * encode_wave_bytes(E, L > 4, bits);
 }
 
 int calib_groups(int n_rows) { return n_rows < kCalibMaxGroups ? n_rows : kCalibMaxGroups; }

@@ -43,6 +43,87 @@ int hip_rc(hipError_t e) { return e == hipSuccess ? QAMW_OK : QAMW_ERR_HIP; }
 
 }  // namespace
 
+namespace {
+
+// The encoder common to QAM-W and the polar baseline: thr == nullptr selects the QAM-W search
+// (d_codebook, d_index), else the polar quantizer (ba magnitude bits, thresholds thr).
+int encode_common(const void* d_w, qamw_dtype w_dtype, int32_t d_out, int32_t d_in, int64_t ld_w,
+                  const float* d_scale, const uint32_t* d_sign_bits, int32_t block, const float* d_codebook,
+                  int32_t bits, const void* d_index, const double* thr, int32_t ba, const float* d_sigma_in,
+                  float* d_sigma_out, uint16_t* d_norm_f16, uint8_t* d_codes, int32_t* d_status, void* d_ws,
+                  size_t ws_bytes, void* stream) {
+    if (d_out < 0 || (w_dtype != QAMW_F32 && w_dtype != QAMW_BF16)) return QAMW_ERR_ARG;
+    int L = check_shape(d_in, block);
+    if (L < 0) return L;
+    int rc = check_bits(bits);
+    if (rc) return rc;
+    if (ld_w < d_in) return QAMW_ERR_ARG;
+    if (encode_lds_bytes(L, bits, d_in, thr ? bits - ba : -1) > kLdsBytes) return QAMW_ERR_UNSUPPORTED;
+    if (!d_sigma_in && !d_sigma_out) return QAMW_ERR_ARG;
+    if (d_out > 0 && (!d_w || !d_norm_f16 || !d_codes)) return QAMW_ERR_ARG;
+    if (d_out > 0 && !thr && (!d_codebook || !d_index || !aligned(d_codebook, 8) || !aligned(d_index, 16)))
+        return QAMW_ERR_ARG;
+    if (d_out > 0 && thr && !aligned(thr, 8)) return QAMW_ERR_ARG;
+    if (d_out > 0 && (!aligned(d_codes, 4) || !aligned(d_w, w_dtype == QAMW_BF16 ? 2 : 4) || !aligned(d_norm_f16, 2)))
+        return QAMW_ERR_ARG;
+    const bool calibrate = d_sigma_in == nullptr;
+    if (calibrate && (!d_ws || !aligned(d_ws, 16) || ws_bytes < qamw_encode_workspace(d_out, d_in, bits)))
+        return QAMW_ERR_WORKSPACE;
+    hipStream_t st = (hipStream_t)stream;
+    const float* sigma = d_sigma_in;
+    if (calibrate) {
+        CalibArgs c{};
+        c.w = d_w;
+        c.w_bf16 = w_dtype == QAMW_BF16;
+        c.n_rows = d_out < 1024 ? d_out : 1024;
+        c.d_in = d_in;
+        c.ld = ld_w;
+        c.scale = d_scale;
+        c.sign = d_sign_bits;
+        c.n_groups = calib_groups(c.n_rows);
+        const size_t part_bytes = (size_t)(c.n_groups > 0 ? c.n_groups : 1) * (size_t)(d_in / 2) * sizeof(double);
+        c.partial = reinterpret_cast<double*>(d_ws);
+        c.nz = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(d_ws) + (part_bytes + 255) / 256 * 256);
+        hipError_t e = launch_calibrate(c, L, d_sigma_out, st);
+        if (e != hipSuccess) return QAMW_ERR_HIP;
+        sigma = d_sigma_out;
+    } else if (d_sigma_out && d_sigma_out != d_sigma_in) {
+        if (hipMemcpyAsync(d_sigma_out, d_sigma_in, sizeof(float) * (size_t)(d_in / 2), hipMemcpyDeviceToDevice, st) !=
+            hipSuccess)
+            return QAMW_ERR_HIP;
+    }
+    if (d_out == 0) return QAMW_OK;
+    EncodeArgs a{};
+    a.w = d_w;
+    a.w_bf16 = w_dtype == QAMW_BF16;
+    a.d_out = d_out;
+    a.d_in = d_in;
+    a.ld = ld_w;
+    a.scale = d_scale;
+    a.sign = d_sign_bits;
+    a.sigma = sigma;
+    a.cb = d_codebook;
+    a.bits = bits;
+    a.index = d_index;
+    a.thr = thr;
+    a.ba = ba;
+    a.norm = d_norm_f16;
+    a.codes = d_codes;
+    a.stride = qamw_row_stride(d_in, bits);
+    a.status = d_status;
+    return hip_rc(launch_encode(a, L, st));
+}
+
+}  // namespace
+
+namespace {
+int check_polar_bits(int32_t ba, int32_t bp) {
+    if (ba < 1 || bp < 1 || ba + bp > 16) return QAMW_ERR_ARG;
+    if (ba > kPolarMaxBa || ba + bp > 12) return QAMW_ERR_UNSUPPORTED;
+    return QAMW_OK;
+}
+}  // namespace
+
 extern "C" {
 
 size_t qamw_row_stride(int32_t d_in, int32_t bits) {
@@ -109,62 +190,43 @@ int qamw_encode(const void* d_w, qamw_dtype w_dtype, int32_t d_out, int32_t d_in
                 const uint32_t* d_sign_bits, int32_t block, const float* d_codebook, int32_t bits, const void* d_index,
                 const float* d_sigma_in, float* d_sigma_out, uint16_t* d_norm_f16, uint8_t* d_codes,
                 int32_t* d_status, void* d_ws, size_t ws_bytes, void* stream) {
-    if (d_out < 0 || (w_dtype != QAMW_F32 && w_dtype != QAMW_BF16)) return QAMW_ERR_ARG;
-    int L = check_shape(d_in, block);
-    if (L < 0) return L;
-    int rc = check_bits(bits);
+    return encode_common(d_w, w_dtype, d_out, d_in, ld_w, d_scale, d_sign_bits, block, d_codebook, bits, d_index,
+                         nullptr, 0, d_sigma_in, d_sigma_out, d_norm_f16, d_codes, d_status, d_ws, ws_bytes, stream);
+}
+
+int qamw_polar_codebook(int32_t ba, int32_t bp, double* d_levels, double* d_thresholds, float* d_codebook,
+                        void* stream) {
+    int rc = check_polar_bits(ba, bp);
     if (rc) return rc;
-    if (ld_w < d_in) return QAMW_ERR_ARG;
-    if (encode_lds_bytes(L, bits, d_in) > kLdsBytes) return QAMW_ERR_UNSUPPORTED;
-    if (!d_sigma_in && !d_sigma_out) return QAMW_ERR_ARG;
-    if (d_out > 0 && (!d_w || !d_codebook || !d_index || !d_norm_f16 || !d_codes)) return QAMW_ERR_ARG;
-    if (d_out > 0 && (!aligned(d_codes, 4) || !aligned(d_codebook, 8) || !aligned(d_index, 16) ||
-                      !aligned(d_w, w_dtype == QAMW_BF16 ? 2 : 4) || !aligned(d_norm_f16, 2)))
+    if (!d_levels || !d_thresholds || !d_codebook || !aligned(d_levels, 8) || !aligned(d_thresholds, 8) ||
+        !aligned(d_codebook, 8))
         return QAMW_ERR_ARG;
-    const bool calibrate = d_sigma_in == nullptr;
-    if (calibrate && (!d_ws || !aligned(d_ws, 16) || ws_bytes < qamw_encode_workspace(d_out, d_in, bits)))
-        return QAMW_ERR_WORKSPACE;
-    hipStream_t st = (hipStream_t)stream;
-    const float* sigma = d_sigma_in;
-    if (calibrate) {
-        CalibArgs c{};
-        c.w = d_w;
-        c.w_bf16 = w_dtype == QAMW_BF16;
-        c.n_rows = d_out < 1024 ? d_out : 1024;
-        c.d_in = d_in;
-        c.ld = ld_w;
-        c.scale = d_scale;
-        c.sign = d_sign_bits;
-        c.n_groups = calib_groups(c.n_rows);
-        const size_t part_bytes = (size_t)(c.n_groups > 0 ? c.n_groups : 1) * (size_t)(d_in / 2) * sizeof(double);
-        c.partial = reinterpret_cast<double*>(d_ws);
-        c.nz = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(d_ws) + (part_bytes + 255) / 256 * 256);
-        hipError_t e = launch_calibrate(c, L, d_sigma_out, st);
-        if (e != hipSuccess) return QAMW_ERR_HIP;
-        sigma = d_sigma_out;
-    } else if (d_sigma_out && d_sigma_out != d_sigma_in) {
-        if (hipMemcpyAsync(d_sigma_out, d_sigma_in, sizeof(float) * (size_t)(d_in / 2), hipMemcpyDeviceToDevice, st) !=
-            hipSuccess)
-            return QAMW_ERR_HIP;
-    }
-    if (d_out == 0) return QAMW_OK;
-    EncodeArgs a{};
-    a.w = d_w;
-    a.w_bf16 = w_dtype == QAMW_BF16;
-    a.d_out = d_out;
-    a.d_in = d_in;
-    a.ld = ld_w;
-    a.scale = d_scale;
-    a.sign = d_sign_bits;
-    a.sigma = sigma;
-    a.cb = d_codebook;
-    a.bits = bits;
-    a.index = d_index;
-    a.norm = d_norm_f16;
-    a.codes = d_codes;
-    a.stride = qamw_row_stride(d_in, bits);
-    a.status = d_status;
-    return hip_rc(launch_encode(a, L, st));
+    return hip_rc(launch_polar_codebook(ba, bp, d_levels, d_thresholds, d_codebook, (hipStream_t)stream));
+}
+
+int qamw_polar_index(const float* d_points, int64_t n, int32_t ba, int32_t bp, const double* d_thresholds,
+                     int32_t* d_idx, int32_t* d_status, void* stream) {
+    int rc = check_polar_bits(ba, bp);
+    if (rc) return rc;
+    if (n < 0) return QAMW_ERR_ARG;
+    if (n == 0) return QAMW_OK;
+    if (!d_points || !d_thresholds || !d_idx || !aligned(d_points, 8) || !aligned(d_thresholds, 8) ||
+        !aligned(d_idx, 4))
+        return QAMW_ERR_ARG;
+    return hip_rc(launch_polar_index(d_points, n, ba, bp, d_thresholds, d_idx, d_status, (hipStream_t)stream));
+}
+
+int qamw_encode_polar(const void* d_w, qamw_dtype w_dtype, int32_t d_out, int32_t d_in, int64_t ld_w,
+                      const float* d_scale, const uint32_t* d_sign_bits, int32_t block, int32_t ba, int32_t bp,
+                      const double* d_thresholds, const float* d_sigma_in, float* d_sigma_out,
+                      uint16_t* d_norm_f16, uint8_t* d_codes, int32_t* d_status, void* d_ws, size_t ws_bytes,
+                      void* stream) {
+    int rc = check_polar_bits(ba, bp);
+    if (rc) return rc;
+    if (!d_thresholds) return QAMW_ERR_ARG;
+    return encode_common(d_w, w_dtype, d_out, d_in, ld_w, d_scale, d_sign_bits, block, nullptr, ba + bp, nullptr,
+                         d_thresholds, ba, d_sigma_in, d_sigma_out, d_norm_f16, d_codes, d_status, d_ws, ws_bytes,
+                         stream);
 }
 
 int qamw_decode(const uint8_t* d_codes, const uint16_t* d_norm_f16, const float* d_sigma, const float* d_codebook,

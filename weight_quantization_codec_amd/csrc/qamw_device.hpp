@@ -388,6 +388,135 @@ __device__ __forceinline__ void nearest_lds_batch(const float (&px)[NP], const f
     }
 }
 
+// ----------------------------------------------------------------------------- polar baseline
+// Paper section 3.5: the pair is coded as a magnitude level (Na = 2^ba levels) times a phase bin
+// (Np = 2^bp bins centred on 2 pi j / Np); the index is ia + Na * ip.  In LDS:
+//   t2[i]     = fl64(t_i^2) for the Na - 1 magnitude thresholds (non-decreasing);
+//   edge[k]   = (cos, sin) of the phase-bin edge (2k + 1) pi / Np, k = 0 .. Np/4 - 1: the edges
+//               inside the first quadrant.
+constexpr int kPolarMaxBa = 8;
+
+struct PolarLds {
+    double* t2;
+    double2* edge;
+    int ba, bp;
+};
+
+__host__ __device__ inline size_t polar_lds_bytes(int bp) {
+    const int nq = bp >= 2 ? (1 << bp) / 4 : 1;
+    return (size_t)(1 << kPolarMaxBa) * sizeof(double) + (size_t)nq * 2 * sizeof(double);
+}
+
+__device__ inline PolarLds polar_lds_carve(char* smem, int ba, int bp) {
+    PolarLds p;
+    p.t2 = reinterpret_cast<double*>(smem);
+    p.edge = reinterpret_cast<double2*>(smem + (size_t)(1 << kPolarMaxBa) * sizeof(double));
+    p.ba = ba;
+    p.bp = bp;
+    return p;
+}
+
+// Fill the tables (all threads of the workgroup take part; a barrier must follow).  Returns true
+// in some thread when the thresholds are not finite, non-negative and non-decreasing.
+__device__ inline bool polar_lds_fill(const PolarLds& p, const double* __restrict__ thr, int tid, int nthreads) {
+    const int na = 1 << p.ba;
+    bool bad = false;
+    for (int i = tid; i < na - 1; i += nthreads) {
+        const double t = thr[i];
+        p.t2[i] = t * t;
+        bad |= !(t >= 0.0 && t <= __builtin_huge_val());
+        if (i + 1 < na - 1) bad |= !(t <= thr[i + 1]);
+    }
+    if (p.bp >= 2) {
+        const int np = 1 << p.bp, nq = np / 4;
+        for (int k = tid; k < nq; k += nthreads) {
+            const double f = (double)(2 * k + 1) / (double)np;   // exact
+            p.edge[k] = make_double2(cospi(f), sinpi(f));
+        }
+    }
+    return bad;
+}
+
+// Polar indices of NB pairs.  Magnitude: ia = #{i : t2[i] < fl64(x^2 + y^2)} by a branch-free
+// binary search (ba steps; t2 is sorted).  Phase: the pair is rotated by a multiple of pi/2 into
+// the first quadrant (exact), and the bin inside it is the number of edges it lies on or past,
+// decided by the sign of the fp64 cross product with the edge direction (bp - 1 steps of binary
+// search).  This is floor(theta Np / (2 pi) + 1/2) mod Np up to rounding at a bin edge.  A pair
+// at the origin (or NaN) gets phase 0; an infinite component is taken as the direction it points.
+template <int NB>
+__device__ __forceinline__ void polar_batch(const float (&px)[NB], const float (&py)[NB], const PolarLds& p,
+                                            int (&out)[NB]) {
+    const int na = 1 << p.ba;
+    int ia[NB];
+    bool zero[NB], big[NB];
+    {
+        double r2[NB];
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const double x = px[i], y = py[i];
+            r2[i] = x * x + y * y;   // both products exact
+            ia[i] = 0;
+            zero[i] = !(r2[i] > 0.0);   // the origin, or NaN
+            big[i] = __builtin_isinf(r2[i]);
+        }
+        for (int step = na >> 1; step >= 1; step >>= 1) {
+#pragma unroll
+            for (int i = 0; i < NB; ++i)
+                if (p.t2[ia[i] + step - 1] < r2[i]) ia[i] += step;
+        }
+    }
+    // the pair, with an infinite component taken as the direction it points (r2 infinite)
+    float fx[NB], fy[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        fx[i] = px[i];
+        fy[i] = py[i];
+        if (big[i]) {
+            fx[i] = __builtin_isinf(fx[i]) ? __builtin_copysignf(1.0f, fx[i]) : __builtin_copysignf(0.0f, fx[i]);
+            fy[i] = __builtin_isinf(fy[i]) ? __builtin_copysignf(1.0f, fy[i]) : __builtin_copysignf(0.0f, fy[i]);
+        }
+    }
+    int ip[NB];
+    if (p.bp == 1) {   // two bins, centred on 0 and pi: the edge is the y axis (theta = -pi/2 goes to 0)
+#pragma unroll
+        for (int i = 0; i < NB; ++i) ip[i] = (fx[i] > 0.0f || (fx[i] == 0.0f && fy[i] < 0.0f)) ? 0 : 1;
+    } else {
+        const int nq = (1 << p.bp) >> 2;
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const float x = fx[i], y = fy[i];
+            // quadrant q: theta in [q pi/2, (q+1) pi/2) (mod 2 pi); (fx, fy) becomes the pair rotated
+            // by -q pi/2 (exact), and ip starts at q Np/4
+            int q;
+            if (x > 0.0f && y >= 0.0f) {
+                q = 0; fx[i] = x; fy[i] = y;
+            } else if (x <= 0.0f && y > 0.0f) {
+                q = 1; fx[i] = y; fy[i] = -x;
+            } else if (x < 0.0f && y <= 0.0f) {
+                q = 2; fx[i] = -x; fy[i] = -y;
+            } else {
+                q = 3; fx[i] = -y; fy[i] = x;
+            }
+            ip[i] = q * nq;
+        }
+        int m[NB];
+#pragma unroll
+        for (int i = 0; i < NB; ++i) m[i] = 0;
+        for (int step = nq; step >= 1; step >>= 1) {
+#pragma unroll
+            for (int i = 0; i < NB; ++i) {
+                const int k = m[i] + step;
+                const double2 e = p.edge[(k <= nq ? k : nq) - 1];
+                if (k <= nq && e.x * (double)fy[i] - e.y * (double)fx[i] >= 0.0) m[i] = k;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i) ip[i] = (ip[i] + m[i]) & ((1 << p.bp) - 1);
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) out[i] = ia[i] + ((zero[i] ? 0 : ip[i]) << p.ba);
+}
+
 __device__ __forceinline__ float bf16_bits_to_float(uint16_t h) {
     return __uint_as_float((uint32_t)h << 16);
 }

@@ -32,6 +32,8 @@ struct EncodeArgs {
     const float* cb;
     int bits;
     const void* index;
+    const double* thr;         // polar baseline: ba bits of magnitude (thresholds) and bits - ba of phase
+    int ba;
     uint16_t* norm;
     uint8_t* codes;
     size_t stride;
@@ -67,7 +69,9 @@ struct DecodeArgs {
 
 // Elements per lane of the transform layout for block size 2^L.
 int lane_elems(int L);
-size_t encode_lds_bytes(int L, int bits, int d_in);
+// LDS bytes of the encoder for one row group; polar_bp >= 1 for the polar quantizer, else the
+// QAM-W search image.
+size_t encode_lds_bytes(int L, int bits, int d_in, int polar_bp);
 constexpr size_t kLdsBytes = 160 * 1024;   // LDS per CU on gfx950
 int calib_groups(int n_rows);
 size_t calib_workspace(int d_out, int d_in);
@@ -75,6 +79,9 @@ size_t calib_workspace(int d_out, int d_in);
 hipError_t launch_calibrate(const CalibArgs& a, int L, float* sigma_out, hipStream_t st);
 hipError_t launch_encode(const EncodeArgs& a, int L, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, int L, hipStream_t st);
+hipError_t launch_polar_codebook(int ba, int bp, double* levels, double* thr, float* cb, hipStream_t st);
+hipError_t launch_polar_index(const float* pts, int64_t n, int ba, int bp, const double* thr, int32_t* out,
+                              int32_t* status, hipStream_t st);
 
 struct LloydAcc;   // device accumulators, defined in k_lloyd.hip
 size_t lloyd_workspace(int bits);
