@@ -11,6 +11,9 @@ copies of the buffers (>= 1 GiB) that the 256 MiB last-level cache cannot serve 
 The codebook training and the search-index build depend on the codebook only; they run and
 are timed once in the same run and reported beside the step.
 
+Beside the step: the polar baseline of section 3.5 (5 + 6 and 4 + 4 bits) on the same matrix:
+codebook build, encode, encoder kernel alone, decode.
+
 After the step, unless --no-stack: a 40-layer 13B-shaped stack (per layer q, k, v, o 5120x5120,
 gate and up 13824x5120, down 5120x13824; 12.7 G weights, bf16 Student-t(4) x 0.015 drawn on the
 GPU) is encoded and then decoded to BF16 in HBM, all 280 matrices back to back, for the
@@ -217,6 +220,10 @@ def main():
         "roofline": roof_enc, "roofline_decode": roof_dec,
     }
 
+    # ---------------------------------------------------------------- polar baseline (section 3.5)
+    for ba, bp in ((5, 6), (4, 4)):
+        result["polar_%d_%d" % (ba, bp)] = polar_run(torch, q, sets, n_sets, scale, sign, block, ba, bp, timed, stream)
+
     # ---------------------------------------------------------------- 40-layer stack (sustained rates)
     if not args.no_stack:
         del sets
@@ -239,6 +246,53 @@ def main():
                                   "sample": "whole 4096x4096 round trip (calibrate 1024 rows, encode, decode), "
                                             "%.1f s" % t_cpu}
     print(json.dumps(result), flush=True)
+
+
+def polar_run(torch, q, sets, n_sets, scale, sign, block, ba, bp, timed, stream):
+    """The polar baseline on the step's workload: codebook build (once), encode with calibration,
+    the encoder kernel alone (fixed sigma) and the decode of its codes with the product table."""
+    dev = sets[0]["w"].device
+    d_out, d_in = sets[0]["w"].shape
+    n_w = d_out * d_in
+    bits = ba + bp
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    levels, thr, table = q.polar_codebook(ba, bp)
+    b.record(stream)
+    torch.cuda.synchronize()
+    cb_ms = a.elapsed_time(b)
+    stride = q.row_stride(d_in, bits)
+    codes = [torch.empty((d_out, stride), dtype=torch.uint8, device=dev) for _ in range(n_sets)]
+    ws = torch.empty((q.encode_workspace(d_out, d_in, bits),), dtype=torch.uint8, device=dev)
+    status = torch.zeros((1,), dtype=torch.int32, device=dev)
+
+    def enc(i, sigma=None):
+        bset = sets[i % n_sets]
+        q.encode_polar(bset["w"], ba, bp, thr, scale=scale, sign_bits=sign, block=block, sigma=sigma, status=status,
+                       workspace=ws, out={"codes": codes[i % n_sets], "norm": bset["norm"], "sigma": bset["sigma"]})
+
+    def dec(i):
+        bset = sets[i % n_sets]
+        q.decode(codes[i % n_sets], bset["norm"], bset["sigma"], table, bits, d_in, scale=scale, sign_bits=sign,
+                 block=block, out=bset["out"])
+
+    for i in range(n_sets):
+        enc(i)
+        dec(i)
+    n_k = 100
+    enc_ms = timed(enc, n_k)
+    sigma_fixed = sets[0]["sigma"].clone()
+    enc_kernel_ms = timed(lambda i: enc(i, sigma_fixed), n_k)
+    dec_ms = timed(dec, n_k)
+    assert int(status.item()) == 0, "data-fault flags raised: %d" % int(status.item())
+    dec_bytes = n_w * (bits / 16.0 + 2.0 / d_in + 2.0)
+    out = {"ba": ba, "bp": bp, "codebook_ms": round(cb_ms, 4), "encode_ms": round(enc_ms, 5),
+           "encode_Mweights_per_s": round(n_w / (enc_ms * 1e-3) / 1e6, 1),
+           "encode_kernel_ms": round(enc_kernel_ms, 5), "decode_ms": round(dec_ms, 5),
+           "decode_GB_per_s": round(dec_bytes / (dec_ms * 1e-3) / 1e9, 1),
+           "bpw": round(stride * 8 / d_in + 16.0 / d_in, 4)}
+    del codes
+    return out
 
 
 def stack_run(torch, q, cb, index, bits, block, stream):

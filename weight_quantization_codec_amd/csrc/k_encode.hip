@@ -438,7 +438,7 @@ __device__ __forceinline__ void load_row_raw(const void* w, int64_t ld, int d_in
 // Per pass: front end (scale, norm, transform), pairs, lockstep search in batches of four pairs
 // per lane, indices to LDS, then each wavefront packs and stores its part of the row.
 constexpr int kSearchBatch = 4;
-constexpr int kPolarBatch = 2;   // pairs per polar batch: 4 spills registers
+constexpr int kPolarBatch = 1;   // pairs per polar batch: more spill registers
 
 // LDS bytes per wavefront of the encoder.  A wavefront's lanes cover 32 E consecutive pairs of
 // the row, so it packs and stores its own part of the row: its buffer holds the exchange during
@@ -659,10 +659,29 @@ size_t calib_smem(int R, int nwaves) {
     return (size_t)R * kMaxWaves * sizeof(double) + (xb > comb ? xb : comb);
 }
 
+// Launch with one workgroup per resident slot: the occupancy the kernel reaches with this LDS and
+// its register count (rows are strided over the grid, so a second wave of workgroups would only
+// add a tail).
 template <int L, int MT, bool BF, bool VEC, bool ISG, bool POLAR>
-hipError_t encode_launch(const EncodeArgs& a, int grid, int threads, size_t smem, int T, int R, hipStream_t st) {
-    allow_lds(k_encode<L, MT, BF, VEC, ISG, POLAR>, smem);
-    hipLaunchKernelGGL((k_encode<L, MT, BF, VEC, ISG, POLAR>), dim3(grid), dim3(threads), smem, st, a, T, R);
+hipError_t encode_launch(const EncodeArgs& a, int R, int threads, size_t smem, int T, hipStream_t st) {
+    auto kern = k_encode<L, MT, BF, VEC, ISG, POLAR>;
+    allow_lds(kern, smem);
+    // the last answer of the occupancy query, per instantiation and host thread
+    static thread_local int c_threads = -1, c_per_cu = 1;
+    static thread_local size_t c_smem = 0;
+    if (threads != c_threads || smem != c_smem) {
+        int per_cu = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, smem) != hipSuccess || per_cu < 1)
+            per_cu = 1;
+        c_threads = threads;
+        c_smem = smem;
+        c_per_cu = per_cu;
+    }
+    const int per_cu = c_per_cu;
+    const int need = (a.d_out + R - 1) / R;
+    const int grid = 256 * per_cu < need ? 256 * per_cu : need;
+    if (grid < 1) return hipSuccess;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), smem, st, a, T, R);
     return hipGetLastError();
 }
 
@@ -672,13 +691,6 @@ hipError_t encode_LBVP(const EncodeArgs& a, hipStream_t st) {
     const int T = ((a.d_in / Lo::E) + kWave - 1) / kWave * kWave;
     if (T > 1024 || (T > 512 && L > 7)) return hipErrorInvalidConfiguration;
     const size_t front = encode_front_bytes(a);
-    auto grid_for = [&](int R, int threads, size_t smem) {
-        int per_cu = (int)(kLdsBytes / smem);
-        if (per_cu * (threads / kWave) > 32) per_cu = 32 / (threads / kWave);
-        if (per_cu < 1) per_cu = 1;
-        const int need = (a.d_out + R - 1) / R;
-        return 256 * per_cu < need ? 256 * per_cu : need;
-    };
     if constexpr (L <= 7) {
         // up to 1024 threads with 1 / sigma in LDS (128 VGPRs, four wavefronts per SIMD)
         int R = 1024 / T;
@@ -687,11 +699,7 @@ hipError_t encode_LBVP(const EncodeArgs& a, hipStream_t st) {
         while (R > 1 && encode_smem<L>(front, a.bits, R, R * T / kWave, true) > kLdsBytes) --R;
         const int threads = R * T;
         const size_t smem = encode_smem<L>(front, a.bits, R, threads / kWave, true);
-        if (smem <= kLdsBytes) {
-            const int grid = grid_for(R, threads, smem);
-            if (grid < 1) return hipSuccess;
-            return encode_launch<L, 1024, BF, VEC, true, POLAR>(a, grid, threads, smem, T, R, st);
-        }
+        if (smem <= kLdsBytes) return encode_launch<L, 1024, BF, VEC, true, POLAR>(a, R, threads, smem, T, st);
     }
     // 1 / sigma in registers
     constexpr int kMax = L <= 7 ? 768 : 512;
@@ -702,12 +710,10 @@ hipError_t encode_LBVP(const EncodeArgs& a, hipStream_t st) {
     const int threads = R * T;
     const size_t smem = encode_smem<L>(front, a.bits, R, threads / kWave, false);
     if (smem > kLdsBytes) return hipErrorInvalidConfiguration;
-    const int grid = grid_for(R, threads, smem);
-    if (grid < 1) return hipSuccess;
-    if (threads <= 512) return encode_launch<L, 512, BF, VEC, false, POLAR>(a, grid, threads, smem, T, R, st);
+    if (threads <= 512) return encode_launch<L, 512, BF, VEC, false, POLAR>(a, R, threads, smem, T, st);
     if constexpr (L <= 7) {
-        if (threads <= 768) return encode_launch<L, 768, BF, VEC, false, POLAR>(a, grid, threads, smem, T, R, st);
-        return encode_launch<L, 1024, BF, VEC, false, POLAR>(a, grid, threads, smem, T, R, st);
+        if (threads <= 768) return encode_launch<L, 768, BF, VEC, false, POLAR>(a, R, threads, smem, T, st);
+        return encode_launch<L, 1024, BF, VEC, false, POLAR>(a, R, threads, smem, T, st);
     }
     return hipErrorInvalidConfiguration;
 }

@@ -78,7 +78,7 @@ __global__ __launch_bounds__(256) void k_polar_index(const float2* __restrict__ 
                                                      const double* __restrict__ thr, int32_t* __restrict__ out,
                                                      int32_t* __restrict__ status) {
     extern __shared__ __align__(16) char smem[];
-    const PolarLds pl = polar_lds_carve(smem, ba, bp);
+    PolarLds pl = polar_lds_carve(smem, ba, bp);
     const bool bad = polar_lds_fill(pl, thr, threadIdx.x, blockDim.x);
     __syncthreads();
     if (bad && blockIdx.x == 0) flag_status(status, 16);

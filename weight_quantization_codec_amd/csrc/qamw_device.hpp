@@ -390,35 +390,51 @@ __device__ __forceinline__ void nearest_lds_batch(const float (&px)[NP], const f
 
 // ----------------------------------------------------------------------------- polar baseline
 // Paper section 3.5: the pair is coded as a magnitude level (Na = 2^ba levels) times a phase bin
-// (Np = 2^bp bins centred on 2 pi j / Np); the index is ia + Na * ip.  In LDS:
-//   t2[i]     = fl64(t_i^2) for the Na - 1 magnitude thresholds (non-decreasing);
-//   edge[k]   = (cos, sin) of the phase-bin edge (2k + 1) pi / Np, k = 0 .. Np/4 - 1: the edges
-//               inside the first quadrant.
+// (Np = 2^bp bins centred on 2 pi j / Np); the index is ia + Na * ip.  Both parts are found by a
+// guess and an exact check, so the dependent chain is short:
+//   magnitude  ia = #{i : t2[i] < fl64(x^2 + y^2)}.  A grid of kPolarGrid cells over
+//              r in [0, 1.5 t_max) gives a lower bound (the count below the edge of the cell under
+//              the one r falls in), and a scan of t2 upwards finishes it (cells hold at most one
+//              Lloyd-Max threshold for ba <= 8, so the scan takes one or two steps).
+//   phase      the pair is rotated by a multiple of pi/2 into the first quadrant (exact); a fp32
+//              arctangent gives the bin m0 to within one; the fp64 cross products with the two
+//              bin edges around m0 decide the bin exactly (up to rounding at an edge).
+// In LDS:
+//   t2[i]   = fl64(t_i^2), the Na - 1 squared thresholds;
+//   mg[g]   = #{i : t_i < g w}, w = 1.5 t_max / kPolarGrid;
+//   edge[k] = (cos, sin) of the bin edge (2k + 1) pi / Np, k = 0 .. Np/4 - 1 (first quadrant).
 constexpr int kPolarMaxBa = 8;
+constexpr int kPolarGrid = 1024;
 
 struct PolarLds {
     double* t2;
+    uint16_t* mg;
     double2* edge;
     int ba, bp;
+    float inv_w;   // kPolarGrid / (1.5 t_max)
 };
 
 __host__ __device__ inline size_t polar_lds_bytes(int bp) {
     const int nq = bp >= 2 ? (1 << bp) / 4 : 1;
-    return (size_t)(1 << kPolarMaxBa) * sizeof(double) + (size_t)nq * 2 * sizeof(double);
+    return (size_t)(1 << kPolarMaxBa) * sizeof(double) + (size_t)kPolarGrid * sizeof(uint16_t) +
+           (size_t)nq * 2 * sizeof(double);
 }
 
 __device__ inline PolarLds polar_lds_carve(char* smem, int ba, int bp) {
     PolarLds p;
     p.t2 = reinterpret_cast<double*>(smem);
-    p.edge = reinterpret_cast<double2*>(smem + (size_t)(1 << kPolarMaxBa) * sizeof(double));
+    p.mg = reinterpret_cast<uint16_t*>(smem + (size_t)(1 << kPolarMaxBa) * sizeof(double));
+    p.edge = reinterpret_cast<double2*>(smem + (size_t)(1 << kPolarMaxBa) * sizeof(double) +
+                                        (size_t)kPolarGrid * sizeof(uint16_t));
     p.ba = ba;
     p.bp = bp;
+    p.inv_w = 0.0f;
     return p;
 }
 
-// Fill the tables (all threads of the workgroup take part; a barrier must follow).  Returns true
-// in some thread when the thresholds are not finite, non-negative and non-decreasing.
-__device__ inline bool polar_lds_fill(const PolarLds& p, const double* __restrict__ thr, int tid, int nthreads) {
+// Fill the tables and p.inv_w (all threads of the workgroup take part; a barrier must follow).
+// Returns true in some thread when the thresholds are not finite, non-negative and non-decreasing.
+__device__ inline bool polar_lds_fill(PolarLds& p, const double* __restrict__ thr, int tid, int nthreads) {
     const int na = 1 << p.ba;
     bool bad = false;
     for (int i = tid; i < na - 1; i += nthreads) {
@@ -426,6 +442,17 @@ __device__ inline bool polar_lds_fill(const PolarLds& p, const double* __restric
         p.t2[i] = t * t;
         bad |= !(t >= 0.0 && t <= __builtin_huge_val());
         if (i + 1 < na - 1) bad |= !(t <= thr[i + 1]);
+    }
+    double rmax = 1.5 * thr[na - 2];
+    if (!(rmax > 1e-30 && rmax < 1e30)) rmax = 1.0;   // degenerate thresholds (flagged): any grid is valid
+    const double w = rmax / kPolarGrid;
+    p.inv_w = (float)(kPolarGrid / rmax);
+    for (int g = tid; g < kPolarGrid; g += nthreads) {
+        const double e = g * w;
+        int c = 0;   // #{t_i < e}, binary search over the sorted thresholds
+        for (int step = na >> 1; step >= 1; step >>= 1)
+            if (thr[c + step - 1] < e) c += step;
+        p.mg[g] = (uint16_t)c;
     }
     if (p.bp >= 2) {
         const int np = 1 << p.bp, nq = np / 4;
@@ -437,12 +464,19 @@ __device__ inline bool polar_lds_fill(const PolarLds& p, const double* __restric
     return bad;
 }
 
-// Polar indices of NB pairs.  Magnitude: ia = #{i : t2[i] < fl64(x^2 + y^2)} by a branch-free
-// binary search (ba steps; t2 is sorted).  Phase: the pair is rotated by a multiple of pi/2 into
-// the first quadrant (exact), and the bin inside it is the number of edges it lies on or past,
-// decided by the sign of the fp64 cross product with the edge direction (bp - 1 steps of binary
-// search).  This is floor(theta Np / (2 pi) + 1/2) mod Np up to rounding at a bin edge.  A pair
-// at the origin (or NaN) gets phase 0; an infinite component is taken as the direction it points.
+// atan(t) for t in [0, 1] to about 3e-5: t times a least-squares fit of atan(t)/t in t^2
+__device__ __forceinline__ float atan_unit(float t) {
+    const float s = t * t;
+    float q = 0.0245979764f;
+    q = q * s - 0.0935131311f;
+    q = q * s + 0.186332226f;
+    q = q * s - 0.331977546f;
+    q = q * s + 0.999985754f;
+    return q * t;
+}
+
+// Polar indices of NB pairs.  A pair at the origin (or NaN) gets phase 0; an infinite component is
+// taken as the direction it points.
 template <int NB>
 __device__ __forceinline__ void polar_batch(const float (&px)[NB], const float (&py)[NB], const PolarLds& p,
                                             int (&out)[NB]) {
@@ -455,15 +489,16 @@ __device__ __forceinline__ void polar_batch(const float (&px)[NB], const float (
         for (int i = 0; i < NB; ++i) {
             const double x = px[i], y = py[i];
             r2[i] = x * x + y * y;   // both products exact
-            ia[i] = 0;
             zero[i] = !(r2[i] > 0.0);   // the origin, or NaN
             big[i] = __builtin_isinf(r2[i]);
+            const float gf = __builtin_amdgcn_sqrtf((float)r2[i]) * p.inv_w;
+            // one cell below the cell of r: a lower bound however fp32 rounds (NaN -> cell 0)
+            const int g = gf >= 1.0f ? (int)__builtin_fminf(gf, (float)kPolarGrid) - 1 : 0;
+            ia[i] = p.mg[g];
         }
-        for (int step = na >> 1; step >= 1; step >>= 1) {
 #pragma unroll
-            for (int i = 0; i < NB; ++i)
-                if (p.t2[ia[i] + step - 1] < r2[i]) ia[i] += step;
-        }
+        for (int i = 0; i < NB; ++i)
+            while (ia[i] < na - 1 && p.t2[ia[i]] < r2[i]) ++ia[i];
     }
     // the pair, with an infinite component taken as the direction it points (r2 infinite)
     float fx[NB], fy[NB];
@@ -482,6 +517,9 @@ __device__ __forceinline__ void polar_batch(const float (&px)[NB], const float (
         for (int i = 0; i < NB; ++i) ip[i] = (fx[i] > 0.0f || (fx[i] == 0.0f && fy[i] < 0.0f)) ? 0 : 1;
     } else {
         const int nq = (1 << p.bp) >> 2;
+        const float bins_per_rad = (float)(1 << p.bp) * 0.159154943f;   // Np / (2 pi)
+        double2 elo[NB], ehi[NB];
+        int m0[NB];
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
             const float x = fx[i], y = fy[i];
@@ -498,20 +536,30 @@ __device__ __forceinline__ void polar_batch(const float (&px)[NB], const float (
                 q = 3; fx[i] = -y; fy[i] = x;
             }
             ip[i] = q * nq;
+            const float u = fx[i], v = fy[i];
+            float lo = __builtin_fminf(u, v), hi = __builtin_fmaxf(u, v);
+            // the fp32 reciprocal flushes denormal inputs and results, which would throw the guess
+            // off by more than a bin: an exact power-of-two scale keeps hi in [2^-49, 2^28]
+            const float sc = hi < 0x1p-100f ? 0x1p100f : (hi > 0x1p100f ? 0x1p-100f : 1.0f);
+            lo *= sc;
+            hi *= sc;
+            const float tq = hi > 0.0f ? __builtin_fminf(lo * __builtin_amdgcn_rcpf(hi), 1.0f) : 0.0f;
+            const float at = atan_unit(tq);
+            const float phi = v > u ? 1.57079633f - at : at;
+            const float mf = phi * bins_per_rad + 0.5f;
+            const int m = mf >= 1.0f ? (int)__builtin_fminf(mf, (float)nq) : 0;   // NaN -> 0
+            m0[i] = m;
+            elo[i] = p.edge[m > 0 ? m - 1 : 0];
+            ehi[i] = p.edge[m < nq ? m : nq - 1];
         }
-        int m[NB];
 #pragma unroll
-        for (int i = 0; i < NB; ++i) m[i] = 0;
-        for (int step = nq; step >= 1; step >>= 1) {
-#pragma unroll
-            for (int i = 0; i < NB; ++i) {
-                const int k = m[i] + step;
-                const double2 e = p.edge[(k <= nq ? k : nq) - 1];
-                if (k <= nq && e.x * (double)fy[i] - e.y * (double)fx[i] >= 0.0) m[i] = k;
-            }
+        for (int i = 0; i < NB; ++i) {
+            const double u = fx[i], v = fy[i];
+            // the true bin is m0 - 1, m0 or m0 + 1: below the edge of m0, or on or past the next one
+            const bool dec = m0[i] > 0 && elo[i].x * v - elo[i].y * u < 0.0;
+            const bool inc = m0[i] < nq && ehi[i].x * v - ehi[i].y * u >= 0.0;
+            ip[i] = (ip[i] + m0[i] - (dec ? 1 : 0) + (inc ? 1 : 0)) & ((1 << p.bp) - 1);
         }
-#pragma unroll
-        for (int i = 0; i < NB; ++i) ip[i] = (ip[i] + m[i]) & ((1 << p.bp) - 1);
     }
 #pragma unroll
     for (int i = 0; i < NB; ++i) out[i] = ia[i] + ((zero[i] ? 0 : ip[i]) << p.ba);
