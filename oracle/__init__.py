@@ -58,6 +58,7 @@ def _bind(lib):
                           ctypes.c_int),
         "oracle_decode": ([vp, vp, i64, i32, vp, vp, i32, vp, vp, i32, vp, vp, vp], ctypes.c_int),
         "oracle_lloyd": ([vp, i64, i32, i32, vp, vp, vp, vp], ctypes.c_int),
+        "oracle_qgemm": ([vp, i32, i64, vp, vp, i64, i32, vp, vp, i32, vp, vp, i32, vp], ctypes.c_int),
         "oracle_rayleigh_lloyd_max": ([i32, vp, vp], ctypes.c_int),
         "oracle_polar_index": ([f32, f32, i32, i32, vp], i32),
         "oracle_polar_table": ([i32, i32, vp, vp], None),
@@ -191,6 +192,20 @@ class Oracle:
                                     self._p(f64))
         assert rc == 0
         return {"f32": f32, "bf16": b16, "f64": f64}
+
+    def qgemm(self, x, codes, norm, d_in, sigma, cb, bits, s, sign_bits, block):
+        """y = x W^T (M x d_out, fp64) with W the decoder's output before rounding (section 1)."""
+        x = np.ascontiguousarray(np.atleast_2d(x), dtype=np.float32)
+        codes = np.ascontiguousarray(codes, dtype=np.uint8)
+        norm = np.ascontiguousarray(norm, dtype=np.uint16)
+        n = norm.shape[0]
+        y = np.empty((x.shape[0], n), dtype=np.float64)
+        cb = np.ascontiguousarray(cb, dtype=np.float32)
+        rc = self.lib.oracle_qgemm(self._p(x), x.shape[0], x.shape[1], self._p(codes), self._p(norm), n, d_in,
+                                   self._p(sigma), self._p(cb), bits, self._p(s), self._p(sign_bits), block,
+                                   self._p(y))
+        assert rc == 0
+        return y
 
     def lloyd(self, pts, bits, iters, init=None):
         pts = np.ascontiguousarray(pts, dtype=np.float32).reshape(-1, 2)

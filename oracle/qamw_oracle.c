@@ -513,6 +513,39 @@ int oracle_decode(const uint8_t* codes, const uint16_t* norm16, int64_t n_rows, 
     return 0;
 }
 
+/* Section 1 (the matrix product that follows dequantization): y = x W^T for
+ * M activation rows x (fp32, leading dimension ld_x), with W the decoder's
+ * output before any rounding (the fp64 values of oracle_decode):
+ *   y[m * n_rows + i] = sum over j of x[m][j] * w_ij, summed in order in fp64. */
+int oracle_qgemm(const float* x, int32_t M, int64_t ld_x, const uint8_t* codes, const uint16_t* norm16,
+                 int64_t n_rows, int32_t d_in, const float* sigma, const float* cb, int32_t bits,
+                 const float* s, const uint32_t* sign_bits, int32_t block, double* y)
+{
+    if (M < 0 || ld_x < d_in || n_rows < 0) return -1;
+    const int64_t chunk = 256;
+    double* w = malloc(sizeof(double) * (size_t)chunk * (size_t)d_in);
+    float* f32 = malloc(sizeof(float) * (size_t)chunk * (size_t)d_in);
+    uint16_t* b16 = malloc(sizeof(uint16_t) * (size_t)chunk * (size_t)d_in);
+    size_t stride = oracle_row_stride(d_in, bits);
+    int rc = 0;
+    for (int64_t i0 = 0; i0 < n_rows && rc == 0; i0 += chunk) {
+        int64_t n = n_rows - i0 < chunk ? n_rows - i0 : chunk;
+        rc = oracle_decode(codes + (size_t)i0 * stride, norm16 + i0, n, d_in, sigma, cb, bits, s, sign_bits,
+                           block, f32, b16, w);
+#pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < n; ++i)
+            for (int32_t m = 0; m < M; ++m) {
+                double acc = 0.0;
+                for (int32_t j = 0; j < d_in; ++j) acc += (double)x[(size_t)m * ld_x + j] * w[(size_t)i * d_in + j];
+                y[(size_t)m * n_rows + i0 + i] = acc;
+            }
+    }
+    free(w);
+    free(f32);
+    free(b16);
+    return rc;
+}
+
 /* Section 3.6, eq. 2: Lloyd iterations for the 2D codebook on samples of the
  * unit circular Gaussian (reading R7).  e_trace[t] = sum over points of
  * llrint(D * 2^32) for the assignment of iteration t (modulo 2^64). */

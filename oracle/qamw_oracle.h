@@ -58,6 +58,10 @@ int oracle_decode(const uint8_t* codes, const uint16_t* norm16, int64_t n_rows, 
                   double* out_f64);
 int oracle_lloyd(const float* pts, int64_t n, int32_t bits, int32_t iters, const float* init,
                  float* cb, int64_t* e_trace, int32_t* status);
+/* section 1: the product after dequantization, y = x W^T in fp64 */
+int oracle_qgemm(const float* x, int32_t M, int64_t ld_x, const uint8_t* codes, const uint16_t* norm16,
+                 int64_t n_rows, int32_t d_in, const float* sigma, const float* cb, int32_t bits,
+                 const float* s, const uint32_t* sign_bits, int32_t block, double* y);
 /* section 3.5, the polar baseline (reading R8) */
 int oracle_rayleigh_lloyd_max(int32_t ba, double* levels, double* thresholds);
 int32_t oracle_polar_index(float px, float py, int32_t ba, int32_t bp, const double* thresholds);

@@ -48,6 +48,13 @@ MUTANTS = [
     ("polar index layout swapped", "return ia + na * ip;", "return ip + np_ * ia;", "test_oracle_polar.py"),
     ("zero pair phase from atan2 of signed zeros", "    if (r2 > 0.0) {\n        double th", "    if (1) {\n        double th",
      "test_oracle_polar.py"),
+    # product after dequantization (section 1): caught by test_oracle_qgemm.py
+    ("qgemm output transposed", "y[(size_t)m * n_rows + i0 + i] = acc;", "y[(size_t)(i0 + i) * M + m] = acc;",
+     "test_oracle_qgemm.py"),
+    ("qgemm on fp32-rounded weights", "acc += (double)x[(size_t)m * ld_x + j] * w[(size_t)i * d_in + j];",
+     "acc += (double)x[(size_t)m * ld_x + j] * (double)f32[(size_t)i * d_in + j];", "test_oracle_qgemm.py"),
+    ("qgemm drops the last column", "for (int32_t j = 0; j < d_in; ++j) acc +=",
+     "for (int32_t j = 0; j < d_in - 1; ++j) acc +=", "test_oracle_qgemm.py"),
     ("polar table angle off by half a bin", "double th = 2.0 * ORACLE_PI * ip / np_;",
      "double th = 2.0 * ORACLE_PI * (ip + 0.5) / np_;", "test_oracle_polar.py"),
 ]
