@@ -154,6 +154,28 @@ int qamw_decode(const uint8_t* d_codes, const uint16_t* d_norm_f16, const float*
                 const uint32_t* d_sign_bits, int32_t d_out, int32_t d_in, int32_t block,
                 void* d_out_w, qamw_dtype out_dtype, int64_t ld_out, void* stream);
 
+/* Section 1 (the matrix product that follows dequantization), fused: for M activation rows
+ *   y[m][i] = sum_j x[m][j] w^_ij
+ * with w^ the qamw_decode weights before any rounding (f16(norm_i) eps_j (H_b x_i)_j / s_j, the
+ * decoder's arguments as there), computed without forming W^: the activation is rotated instead,
+ * u = sigma . blockdiag(H_b)(eps . x / s) (fp64, rounded to fp32 once), and
+ *   y[m][i] = f16(norm_i) * sum_k (c[idx_ik].x u_m,2k + c[idx_ik].y u_m,2k+1)
+ * summed in fp32 (blocked: 32 pairs per lane, then a fixed-order wavefront sum; rows longer than the
+ * LDS tile add per-split partial sums in a fixed order).  Error against the exact product: at most
+ * about 1e-6 of sum_j |x_mj w^_ij| for d_in <= 16384.
+ * Arguments:
+ *   d_x, x_dtype, M, ld_x   M x d_in activations (QAMW_F32 or QAMW_BF16), row m at d_x + m ld_x.
+ *                           1 <= M <= 16 (QAMW_ERR_UNSUPPORTED above; M = 0 is a no-op).
+ *   d_codes ... block       as qamw_decode (any block size 2..1024 dividing d_in; bits <= 12).
+ *   d_y, y_dtype, ld_y      M x d_out outputs, y[m][i] at d_y + m ld_y (ld_y >= d_out); BF16 is the
+ *                           fp32 result rounded to nearest even.
+ *   d_ws, ws_bytes          at least qamw_qgemm_workspace(M, d_out, d_in) bytes, 256-byte aligned. */
+size_t qamw_qgemm_workspace(int32_t M, int32_t d_out, int32_t d_in);
+int qamw_qgemm(const void* d_x, qamw_dtype x_dtype, int32_t M, int64_t ld_x, const uint8_t* d_codes,
+               const uint16_t* d_norm_f16, const float* d_sigma, const float* d_codebook, int32_t bits,
+               const float* d_scale, const uint32_t* d_sign_bits, int32_t d_out, int32_t d_in, int32_t block,
+               void* d_y, qamw_dtype y_dtype, int64_t ld_y, void* d_ws, size_t ws_bytes, void* stream);
+
 /* Section 3.5 (the polar baseline QAM-W is compared with): a pair is coded as a magnitude level
  * times a phase.  The magnitude quantizer is the Na = 2^ba level Lloyd-Max quantizer of the unit
  * Rayleigh density r exp(-r^2/2) (the modulus of a circular standard Gaussian pair, the

@@ -22,7 +22,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = q.header_symbols()
-    assert len(names) == 14
+    assert len(names) == 16
     out = subprocess.run(["nm", "-D", "--defined-only", q.LIB_PATH], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
     for n in names:
@@ -166,3 +166,32 @@ def test_polar_codebook_and_index_reject(lib):
     assert lib.qamw_polar_index(FAKE, 10, 4, 4, None, FAKE, None, None) == ARG
     assert lib.qamw_polar_index(FAKE + 4, 10, 4, 4, FAKE, FAKE, None, None) == ARG
     assert lib.qamw_polar_index(None, 0, 4, 4, None, None, None, None) == q.OK
+
+
+def _qg(lib, **kw):
+    a = dict(x=FAKE, xt=q.BF16, M=4, ld_x=256, codes=FAKE, norm=FAKE, sigma=FAKE, cb=FAKE, bits=8, scale=None,
+             sign=None, d_out=16, d_in=256, block=64, y=FAKE, yt=q.F32, ld_y=16, ws=FAKE, ws_bytes=1 << 20)
+    a.update(kw)
+    return lib.qamw_qgemm(a["x"], a["xt"], a["M"], a["ld_x"], a["codes"], a["norm"], a["sigma"], a["cb"], a["bits"],
+                          a["scale"], a["sign"], a["d_out"], a["d_in"], a["block"], a["y"], a["yt"], a["ld_y"], a["ws"],
+                          a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(M=-1), ARG), (dict(xt=5), ARG), (dict(yt=5), ARG), (dict(d_in=255, ld_x=255), ARG), (dict(block=48), ARG),
+    (dict(block=2048), ARG), (dict(bits=0), ARG), (dict(bits=13), UNSUP), (dict(M=17), UNSUP), (dict(ld_x=128), ARG),
+    (dict(ld_y=8), ARG), (dict(x=None), ARG), (dict(codes=None), ARG), (dict(y=FAKE + 2), ARG),
+    (dict(x=FAKE + 1), ARG), (dict(ws=None), WS), (dict(ws=FAKE + 16), WS), (dict(ws_bytes=64), WS),
+])
+def test_qgemm_rejects(lib, kw, code):
+    assert _qg(lib, **kw) == code
+
+
+def test_qgemm_noops_and_workspace(lib):
+    assert _qg(lib, M=0, x=None, y=None, ws=None) == q.OK
+    assert _qg(lib, d_out=0, codes=None, norm=None, ws=None) == q.OK
+    assert lib.qamw_qgemm_workspace(0, 16, 256) >= 0
+    assert lib.qamw_qgemm_workspace(1, 4096, 4096) >= 4096 * 4
+    # 13824 columns at 16 rows: the rotated activations of all 16 rows
+    assert lib.qamw_qgemm_workspace(16, 5120, 13824) >= 16 * 13824 * 4
+    assert lib.qamw_qgemm_workspace(1, 16, 255) == 0

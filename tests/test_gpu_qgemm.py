@@ -1,0 +1,171 @@
+"""GPU parity of the fused dequantize-and-multiply (paper section 1) against the CPU oracle.
+
+y = x W^T with W the decoder's weights before rounding.  The oracle decodes in fp64 and sums in
+fp64; the kernels rotate the activation instead and sum c[idx] . u in fp32 (on the vector units
+or the matrix cores).  Tolerance, from the summation: an output adds d_in products, each rounded
+at most once on its way (products, partial sums per lane or matrix-core accumulator, the
+cross-lane or cross-wavefront sum, the norm), so |y - y_ref| <= (d_in + 64) 2^-24 E, where E is
+the sum of the absolute values of the terms, f16(norm_i) sum_k |c[idx].x u_2k| + |c[idx].y u_2k+1|
+(computed here in fp64 from scipy's Hadamard matrix).  BF16 outputs are within one BF16 ulp of the oracle's value rounded to fp32
+then BF16.
+
+Cases: one and several passes per row, split rows (reduce kernel), M = 1..16 on both kernels
+(vector-unit m-tiles of 1, 2 and 4 rows with a ragged last tile; matrix-core tiles of 16 weight
+rows with a ragged last tile), every index width 1..12 on both, block sizes 2..1024, fp32 and BF16 inputs and
+outputs, padded leading dimensions, zero rows, and the benchmark's 4096 x 4096 matrix whole.
+"""
+import numpy as np
+import pytest
+import scipy.linalg
+import torch
+
+from helpers import DEV, assert_bf16_within_1ulp, log, sign_tensor, t
+
+pytestmark = pytest.mark.gpu
+
+
+def _problem(orc, seed, d_out, d_in, block, bits):
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_t(5, size=(d_out, d_in)) * 0.015).astype(np.float32)
+    w[:, rng.choice(d_in, size=max(1, d_in // 100), replace=False)] *= 10
+    w[min(2, d_out - 1)] = 0
+    s = (np.abs(rng.standard_normal(d_in)) ** 0.5 + 0.1).astype(np.float32)
+    sb = rng.integers(0, 2**32, size=(d_in + 31) // 32, dtype=np.uint64).astype(np.uint32)
+    cb = rng.standard_normal((1 << bits, 2)).astype(np.float32)
+    sig, _ = orc.calibrate(w[:1024], s, sb, block)
+    e = orc.encode(w, s, sb, block, cb, bits, sig)
+    return dict(codes=e["codes"], norm=e["norm"], d_in=d_in, sigma=sig, cb=cb, bits=bits, s=s, sign_bits=sb,
+                block=block)
+
+
+def _abs_terms(orc, x, pr):
+    """E[m][i]: the sum of the absolute values of the terms the kernel adds for y[m][i]."""
+    d_in, block = pr["d_in"], pr["block"]
+    n_pairs = d_in // 2
+    j = np.arange(d_in)
+    eps = np.where((pr["sign_bits"][j // 32] >> (j % 32)) & 1, -1.0, 1.0)
+    H = scipy.linalg.hadamard(block).astype(np.float64) / np.sqrt(block)
+    v = x.astype(np.float64) * eps / pr["s"].astype(np.float64)
+    u = (v.reshape(len(x), d_in // block, block) @ H).reshape(len(x), n_pairs, 2) * pr["sigma"].astype(np.float64)[None, :, None]
+    idx = np.stack([orc.unpack_row(pr["codes"][i], pr["bits"], d_in) for i in range(len(pr["norm"]))])
+    c = np.abs(pr["cb"].astype(np.float64)[idx])                         # d_out x n_pairs x 2
+    rn = pr["norm"].astype(np.uint16).view(np.float16).astype(np.float64)
+    return rn[None, :] * np.einsum("ikc,mkc->mi", c, np.abs(u))
+
+
+def _run(q, orc, pr, M, x_dtype="bf16", y_dtype=torch.float32, ld_x=None, ld_y=None, seed=0):
+    d_in, d_out = pr["d_in"], len(pr["norm"])
+    rng = np.random.default_rng(100 + seed)
+    x = rng.standard_normal((M, d_in)).astype(np.float32)
+    if x_dtype == "bf16":
+        xt = torch.from_numpy(x).to(torch.bfloat16)
+        x = xt.float().numpy()                     # the values the kernel sees
+    else:
+        xt = torch.from_numpy(x)
+    if ld_x is not None:
+        big = torch.zeros((M, ld_x), dtype=xt.dtype)
+        big[:, :d_in] = xt
+        xd = big.to(DEV)[:, :d_in]
+    else:
+        xd = xt.to(DEV)
+    out = full = None
+    if ld_y is not None:
+        full = torch.full((M, ld_y), 7.0, dtype=y_dtype, device=DEV)
+        out = full[:, :d_out]
+    y = q.qgemm(xd, t(pr["codes"]), t(pr["norm"].view(np.int16)), t(pr["sigma"]), t(pr["cb"]), pr["bits"],
+                scale=t(pr["s"]), sign_bits=sign_tensor(pr["sign_bits"]), block=pr["block"], out_dtype=y_dtype,
+                out=out)
+    torch.cuda.synchronize()
+    if full is not None:
+        assert torch.all(full[:, d_out:] == 7.0).item()   # padding untouched
+    ref = orc.qgemm(x, pr["codes"], pr["norm"], d_in, pr["sigma"], pr["cb"], pr["bits"], pr["s"], pr["sign_bits"],
+                    pr["block"])
+    return x, y, ref
+
+
+def _check_f32(orc, x, y, ref, pr):
+    bound = (pr["d_in"] + 64) * 2.0 ** -24
+    E = _abs_terms(orc, x, pr)
+    got = y.cpu().numpy().astype(np.float64)
+    err = np.abs(got - ref)
+    rel = float(np.max(err / np.maximum(E, 1e-30)))
+    assert np.all(err <= bound * E + 1e-37), "max error %.3g of the absolute term sum (bound %.3g)" % (rel, bound)
+    return rel
+
+
+CASES = {
+    # id: (d_out, d_in, block, bits, M, x dtype)
+    "4096_b128_B11_M1": (64, 4096, 128, 11, 1, "bf16"),
+    "4096_b128_B11_M4": (100, 4096, 128, 11, 4, "bf16"),
+    "768_b256_B8_M3_ragged": (33, 768, 256, 8, 3, "bf16"),
+    "13824_b512_B11_M16_split": (20, 13824, 512, 11, 16, "bf16"),
+    "5120_b128_B7_M2": (40, 5120, 128, 7, 2, "fp32"),
+    "11008_b256_B11_M1_3pass": (17, 11008, 256, 11, 1, "bf16"),
+    "5120_b128_B11_M5_split": (23, 5120, 128, 11, 5, "fp32"),
+    "256_b2_B1_M7": (9, 256, 2, 1, 7, "fp32"),
+    "2048_b1024_B12_M9": (31, 2048, 1024, 12, 9, "bf16"),
+    "512_b64_B3_M16": (70, 512, 64, 3, 16, "bf16"),
+}
+
+
+@pytest.mark.parametrize("case", list(CASES), ids=list(CASES))
+def test_qgemm_matches_oracle(q, orc, case):
+    d_out, d_in, block, bits, M, xdt = CASES[case]
+    log("qgemm %s" % case)
+    pr = _problem(orc, d_out + d_in + bits, d_out, d_in, block, bits)
+    x, y, ref = _run(q, orc, pr, M, x_dtype=xdt)
+    rel = _check_f32(orc, x, y, ref, pr)
+    assert np.all(y.cpu().numpy()[:, min(2, d_out - 1)] == 0)   # the zero row
+    log("  max error %.3g of the absolute term sum" % rel)
+
+
+@pytest.mark.parametrize("M", [2, 12])
+@pytest.mark.parametrize("bits", list(range(1, 13)))
+def test_qgemm_every_index_width(q, orc, bits, M):
+    """Every index width on both kernels (vector units for few activation rows, matrix cores for
+    many); 4352 columns: two passes of 2048 pairs (the second ragged), 34 chunks of 64 pairs."""
+    pr = _problem(orc, 500 + bits, 12, 4096 + 256, 256, bits)
+    x, y, ref = _run(q, orc, pr, M, seed=bits)
+    _check_f32(orc, x, y, ref, pr)
+
+
+def test_qgemm_bf16_output_and_padded_strides(q, orc):
+    pr = _problem(orc, 7, 50, 1024, 128, 10)
+    x, y, ref = _run(q, orc, pr, 6, x_dtype="fp32", y_dtype=torch.bfloat16, ld_x=1024 + 40, ld_y=50 + 14)
+    want = torch.from_numpy(ref.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = y.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    n = assert_bf16_within_1ulp(got, want)
+    log("  bf16: %d of %d outputs differ by one ulp" % (n, got.size))
+
+
+def test_qgemm_empty_and_limits(q, orc):
+    pr = _problem(orc, 8, 8, 256, 64, 8)
+    x = torch.zeros((0, 256), dtype=torch.bfloat16, device=DEV)
+    y = q.qgemm(x, t(pr["codes"]), t(pr["norm"].view(np.int16)), t(pr["sigma"]), t(pr["cb"]), 8,
+                scale=t(pr["s"]), sign_bits=sign_tensor(pr["sign_bits"]), block=64)
+    assert y.shape == (0, 8)
+    x17 = torch.zeros((17, 256), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(q.QamwError) as ei:
+        q.qgemm(x17, t(pr["codes"]), t(pr["norm"].view(np.int16)), t(pr["sigma"]), t(pr["cb"]), 8, block=64)
+    assert ei.value.code == q.ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("M", [1, 16])
+def test_qgemm_fullsize_attn4096(q, orc, synth, M):
+    """The benchmark's whole 4096 x 4096 matrix and K = 2048 codebook, multiplied as the benchmark
+    does; every output against the oracle's product (codes from the oracle's encoder)."""
+    cfg = synth.config(1)
+    m = cfg.matrices[0]
+    d_out, d_in, block, bits = m.d_out, m.d_in, cfg.block, cfg.bits[0]
+    log("qgemm fullsize 4096x4096 M=%d" % M)
+    cb = np.ascontiguousarray(np.load("tests/golden/cb_cfg1_k2048.npz")["codebook"]).astype(np.float32)
+    w = m.weights()
+    s = m.channel_scale()
+    sb = synth.sign_bits(d_in)
+    sig, _ = orc.calibrate(w[:1024], s, sb, block)
+    e = orc.encode(w, s, sb, block, cb, bits, sig, want_idx=False)
+    pr = dict(codes=e["codes"], norm=e["norm"], d_in=d_in, sigma=sig, cb=cb, bits=bits, s=s, sign_bits=sb,
+              block=block)
+    x, y, ref = _run(q, orc, pr, M, seed=M)
+    rel = _check_f32(orc, x, y, ref, pr)
+    log("  max error %.3g of the absolute term sum" % rel)

@@ -59,6 +59,9 @@ def load(path: Optional[str] = None):
         "qamw_encode": ([vp, ctypes.c_int, i32, i32, i64, vp, vp, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp],
                         ctypes.c_int),
         "qamw_decode": ([vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, vp, ctypes.c_int, i64, vp], ctypes.c_int),
+        "qamw_qgemm_workspace": ([i32, i32, i32], sz),
+        "qamw_qgemm": ([vp, ctypes.c_int, i32, i64, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, vp, ctypes.c_int, i64,
+                        vp, sz, vp], ctypes.c_int),
         "qamw_polar_codebook": ([i32, i32, vp, vp, vp, vp], ctypes.c_int),
         "qamw_polar_index": ([vp, i64, i32, i32, vp, vp, vp, vp], ctypes.c_int),
         "qamw_encode_polar": ([vp, ctypes.c_int, i32, i32, i64, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz,
@@ -220,6 +223,40 @@ def encode(w: torch.Tensor, codebook: torch.Tensor, bits: int, index: torch.Tens
                             0 if ws is None else ws.numel(), _stream())
     _check(rc, "qamw_encode")
     return {"codes": codes, "norm": norm, "sigma": sigma if sigma is not None else sig_out}
+
+
+def qgemm_workspace(M: int, d_out: int, d_in: int) -> int:
+    return load().qamw_qgemm_workspace(M, d_out, d_in)
+
+
+def qgemm(x: torch.Tensor, codes: torch.Tensor, norm: torch.Tensor, sigma: torch.Tensor, codebook: torch.Tensor,
+          bits: int, scale: Optional[torch.Tensor] = None, sign_bits: Optional[torch.Tensor] = None, block: int = 0,
+          out_dtype=torch.float32, out: Optional[torch.Tensor] = None,
+          workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y = x W^T (section 1) with W the decoder's weights, W never formed.  x: M x d_in (bf16/fp32)."""
+    if x.dim() == 1:
+        x = x.unsqueeze(0)
+    if x.dtype not in (torch.bfloat16, torch.float32) or not x.is_cuda or x.dim() != 2:
+        raise ValueError("x must be an M x d_in bf16 or fp32 device tensor")
+    M, d_in = x.shape
+    if M > 0 and x.stride(1) != 1:
+        raise ValueError("x rows must be contiguous")
+    _dev(codes, torch.uint8, "codes")
+    d_out = norm.numel()
+    if out is None:
+        out = torch.empty((M, d_out), dtype=out_dtype, device=x.device)
+    if out.dtype not in (torch.bfloat16, torch.float32) or (M > 0 and out.stride(1) != 1):
+        raise ValueError("out must be a bf16 or fp32 tensor with contiguous rows")
+    ws = workspace
+    if ws is None:
+        ws = _ws(qgemm_workspace(M, d_out, d_in), x.device)
+    rc = load().qamw_qgemm(_ptr(x), BF16 if x.dtype == torch.bfloat16 else F32, M, x.stride(0) if M > 0 else d_in,
+                           _ptr(codes), _ptr(norm), _ptr(sigma), _ptr(codebook), bits, _ptr(scale),
+                           _ptr(sign_bits), d_out, d_in, block, _ptr(out),
+                           BF16 if out.dtype == torch.bfloat16 else F32, out.stride(0) if M > 0 else d_out,
+                           _ptr(ws), ws.numel(), _stream())
+    _check(rc, "qamw_qgemm")
+    return out
 
 
 def polar_codebook(ba: int, bp: int, device=None):

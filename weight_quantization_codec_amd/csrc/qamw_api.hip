@@ -194,6 +194,57 @@ int qamw_encode(const void* d_w, qamw_dtype w_dtype, int32_t d_out, int32_t d_in
                          nullptr, 0, d_sigma_in, d_sigma_out, d_norm_f16, d_codes, d_status, d_ws, ws_bytes, stream);
 }
 
+size_t qamw_qgemm_workspace(int32_t M, int32_t d_out, int32_t d_in) {
+    if (M < 0 || d_out < 0 || d_in <= 0 || (d_in & 1)) return 0;
+    return qgemm_workspace(M, d_out, d_in);
+}
+
+int qamw_qgemm(const void* d_x, qamw_dtype x_dtype, int32_t M, int64_t ld_x, const uint8_t* d_codes,
+               const uint16_t* d_norm_f16, const float* d_sigma, const float* d_codebook, int32_t bits,
+               const float* d_scale, const uint32_t* d_sign_bits, int32_t d_out, int32_t d_in, int32_t block,
+               void* d_y, qamw_dtype y_dtype, int64_t ld_y, void* d_ws, size_t ws_bytes, void* stream) {
+    if (M < 0 || d_out < 0 || (x_dtype != QAMW_F32 && x_dtype != QAMW_BF16) ||
+        (y_dtype != QAMW_F32 && y_dtype != QAMW_BF16))
+        return QAMW_ERR_ARG;
+    if (d_in <= 0 || (d_in & 1)) return QAMW_ERR_ARG;
+    const int32_t b = block == 0 ? qamw_default_block(d_in) : block;
+    if (b < 2 || b > 1024 || !is_pow2(b) || d_in % b) return QAMW_ERR_ARG;
+    int rc = check_bits(bits);
+    if (rc) return rc;
+    if (M > 16) return QAMW_ERR_UNSUPPORTED;
+    if (ld_x < d_in || ld_y < d_out) return QAMW_ERR_ARG;
+    if (M == 0 || d_out == 0) return QAMW_OK;
+    if (!d_x || !d_codes || !d_norm_f16 || !d_sigma || !d_codebook || !d_y) return QAMW_ERR_ARG;
+    if (!aligned(d_x, x_dtype == QAMW_BF16 ? 2 : 4) || !aligned(d_y, y_dtype == QAMW_BF16 ? 2 : 4) ||
+        !aligned(d_codes, 4) || !aligned(d_codebook, 8) || !aligned(d_norm_f16, 2))
+        return QAMW_ERR_ARG;
+    if (!d_ws || !aligned(d_ws, 256) || ws_bytes < qamw_qgemm_workspace(M, d_out, d_in)) return QAMW_ERR_WORKSPACE;
+    QgemmArgs a{};
+    a.codes = d_codes;
+    a.stride = qamw_row_stride(d_in, bits);
+    a.norm = d_norm_f16;
+    a.cb = d_codebook;
+    a.bits = bits;
+    a.u = reinterpret_cast<float*>(d_ws);
+    a.M = M;
+    a.n_pairs = d_in / 2;
+    a.d_out = d_out;
+    a.y = d_y;
+    a.y_bf16 = y_dtype == QAMW_BF16;
+    a.ld_y = ld_y;
+    a.partial = reinterpret_cast<float*>(reinterpret_cast<char*>(d_ws) + ((size_t)M * d_in * sizeof(float) + 255) / 256 * 256);
+    QgemmRotateArgs r{};
+    r.x = d_x;
+    r.x_bf16 = x_dtype == QAMW_BF16;
+    r.ld_x = ld_x;
+    r.d_in = d_in;
+    r.block = b;
+    r.scale = d_scale;
+    r.sign = d_sign_bits;
+    r.sigma = d_sigma;
+    return hip_rc(launch_qgemm(a, r, (hipStream_t)stream));
+}
+
 int qamw_polar_codebook(int32_t ba, int32_t bp, double* d_levels, double* d_thresholds, float* d_codebook,
                         void* stream) {
     int rc = check_polar_bits(ba, bp);

@@ -83,6 +83,38 @@ hipError_t launch_polar_codebook(int ba, int bp, double* levels, double* thr, fl
 hipError_t launch_polar_index(const float* pts, int64_t n, int ba, int bp, const double* thr, int32_t* out,
                               int32_t* status, hipStream_t st);
 
+// Fused dequantize-and-multiply (k_qgemm.hip).
+struct QgemmArgs {
+    const uint8_t* codes;
+    size_t stride;
+    const uint16_t* norm;
+    const float* cb;
+    int bits;
+    float* u;            // M x d_in: the rotated, sigma-scaled activations
+    int M, n_pairs, d_out;
+    int n_pass, pps;     // passes of 2048 pairs per row; passes per split (set by the launcher)
+    void* y;
+    int y_bf16;
+    int64_t ld_y;
+    float* partial;      // splits x M x d_out, or null when a row fits one split
+};
+struct QgemmRotateArgs {
+    const void* x;
+    int x_bf16;
+    int64_t ld_x;
+    int d_in, block;
+    const float* scale;
+    const uint32_t* sign;
+    const float* sigma;
+};
+struct QgemmPlan {
+    int n_pass, mt, mtiles, pps, splits, grid_x;
+};
+size_t qgemm_lds_bytes(int bits, int mt, int pps);
+QgemmPlan qgemm_plan(int M, int d_out, int d_in);
+size_t qgemm_workspace(int M, int d_out, int d_in);
+hipError_t launch_qgemm(const QgemmArgs& a, const QgemmRotateArgs& r, hipStream_t st);
+
 struct LloydAcc;   // device accumulators, defined in k_lloyd.hip
 size_t lloyd_workspace(int bits);
 hipError_t launch_lloyd(const float* pts, int64_t n, int bits, int iters, const float* init, float* cb,
