@@ -11,7 +11,9 @@ copies of the buffers (>= 1 GiB) that the 256 MiB last-level cache cannot serve 
 The codebook training and the search-index build depend on the codebook only; they run and
 are timed once in the same run and reported beside the step.
 
-Beside the step: the polar baseline of section 3.5 (5 + 6 and 4 + 4 bits) on the same matrix:
+Beside the step: the fused dequantize-and-multiply of section 1 (y = x W^T from the codes, M = 1,
+4, 16 activation rows) against hipBLASLt on the decoded BF16 W and against decode-then-multiply; and
+the polar baseline of section 3.5 (5 + 6 and 4 + 4 bits) on the same matrix:
 codebook build, encode, encoder kernel alone, decode.
 
 After the step, unless --no-stack: a 40-layer 13B-shaped stack (per layer q, k, v, o 5120x5120,
@@ -220,6 +222,9 @@ def main():
         "roofline": roof_enc, "roofline_decode": roof_dec,
     }
 
+    # ---------------------------------------------------------------- fused dequantize-and-multiply (section 1)
+    result["qgemm"] = qgemm_run(torch, q, sets, n_sets, cb, bits, scale, sign, block, timed)
+
     # ---------------------------------------------------------------- polar baseline (section 3.5)
     for ba, bp in ((5, 6), (4, 4)):
         result["polar_%d_%d" % (ba, bp)] = polar_run(torch, q, sets, n_sets, scale, sign, block, ba, bp, timed, stream)
@@ -246,6 +251,54 @@ def main():
                                   "sample": "whole 4096x4096 round trip (calibrate 1024 rows, encode, decode), "
                                             "%.1f s" % t_cpu}
     print(json.dumps(result), flush=True)
+
+
+def qgemm_run(torch, q, sets, n_sets, cb, bits, scale, sign, block, timed):
+    """y = x W^T for M activation rows with W in its codes (qamw_qgemm), against hipBLASLt on the
+    decoded BF16 W (torch.matmul) and against decode-then-multiply, on the step's matrix; the code
+    and weight buffers rotate over the step's sets."""
+    dev = sets[0]["w"].device
+    d_out, d_in = sets[0]["w"].shape
+    for i in range(n_sets):   # every set holds the codes and the BF16 decode of the same matrix
+        q.decode(sets[i]["codes"], sets[i]["norm"], sets[i]["sigma"], cb, bits, d_in, scale=scale, sign_bits=sign,
+                 block=block, out=sets[i]["out"])
+    stride = q.row_stride(d_in, bits)
+    res = {}
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    for M in (1, 4, 16):
+        x = torch.randn((M, d_in), device=dev, generator=g).to(torch.bfloat16)
+        y = torch.empty((M, d_out), dtype=torch.float32, device=dev)
+        ws = torch.empty((q.qgemm_workspace(M, d_out, d_in),), dtype=torch.uint8, device=dev)
+        tmp = torch.empty((d_out, d_in), dtype=torch.bfloat16, device=dev)
+
+        def fused(i):
+            b = sets[i % n_sets]
+            q.qgemm(x, b["codes"], b["norm"], b["sigma"], cb, bits, scale=scale, sign_bits=sign, block=block, out=y,
+                    workspace=ws)
+
+        def bf16(i):
+            torch.matmul(x, sets[i % n_sets]["out"].t())
+
+        def dec_mm(i):
+            b = sets[i % n_sets]
+            q.decode(b["codes"], b["norm"], b["sigma"], cb, bits, d_in, scale=scale, sign_bits=sign, block=block, out=tmp)
+            torch.matmul(x, tmp.t())
+
+        for fn in (fused, bf16, dec_mm):   # first calls pick and load library kernels
+            for i in range(10):
+                fn(i)
+        torch.cuda.synchronize()
+        t_f, t_b, t_d = timed(fused, 200), timed(bf16, 200), timed(dec_mm, 100)
+        alg = d_out * stride + d_out * 2 + M * d_in * 2 + M * d_out * 4   # codes, norms, x, y
+        res["M%d" % M] = {"qgemm_us": round(t_f * 1e3, 2), "bf16_matmul_us": round(t_b * 1e3, 2),
+                          "decode_then_matmul_us": round(t_d * 1e3, 2),
+                          "speedup_vs_bf16": round(t_b / t_f, 3), "speedup_vs_decode_matmul": round(t_d / t_f, 3),
+                          "hbm_GBps": round(alg / (t_f * 1e-3) / 1e9, 1),
+                          "hbm_frac": round(alg / (t_f * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                          "kernel": "vector units" if M < 6 else "matrix cores (fp32)"}
+        del ws, tmp
+    return res
 
 
 def polar_run(torch, q, sets, n_sets, scale, sign, block, ba, bp, timed, stream):

@@ -138,6 +138,20 @@ __global__ __launch_bounds__(kQgThreads) void k_qgemm(QgemmArgs a) {
     const int pass0 = blockIdx.z * a.pps;                    // first pass of this split
     const int np_here = min(a.pps, a.n_pass - pass0);        // passes in this split (>= 1)
 
+    constexpr uint32_t mask = (1u << BITS) - 1u;
+    const int rstride = gridDim.x * nw;
+    // work items of this wavefront: (row, pass) for rows wave0, wave0 + rstride, ...
+    int row = blockIdx.x * nw + wave, p = 0;
+    auto codes_rsrc = [&](int r) {
+        const bool ok = r < a.d_out;
+        return __builtin_amdgcn_make_buffer_rsrc((void*)(a.codes + (size_t)(ok ? r : 0) * a.stride), (short)0,
+                                                 ok ? (int)a.stride : 0, 0x00020000);
+    };
+    auto lane_off = [&](int pp) { return (uint32_t)(((pass0 + pp) * kWave + lane) * BITS) * 4u; };
+    // the first work item's codes are in flight while the LDS tables fill
+    uint32_t nxt[BITS];
+    if (row < a.d_out) qg_load<BITS>(codes_rsrc(row), lane_off(0), nxt);
+
     // codebook and the u tile: u_l[((p * MT + m) * 32 + t) * 65 + l] = u pair (pass0 + p) * 2048 + l * 32 + t
     // every load of a thread issued before its stores: at most K / 1024 <= 4 codebook entries and
     // kQgMaxTile * 2048 / 1024 = 8 u values per thread
@@ -177,18 +191,6 @@ __global__ __launch_bounds__(kQgThreads) void k_qgemm(QgemmArgs a) {
     }
     __syncthreads();
 
-    constexpr uint32_t mask = (1u << BITS) - 1u;
-    const int rstride = gridDim.x * nw;
-    // work items of this wavefront: (row, pass) for rows wave0, wave0 + rstride, ...
-    int row = blockIdx.x * nw + wave, p = 0;
-    auto codes_rsrc = [&](int r) {
-        const bool ok = r < a.d_out;
-        return __builtin_amdgcn_make_buffer_rsrc((void*)(a.codes + (size_t)(ok ? r : 0) * a.stride), (short)0,
-                                                 ok ? (int)a.stride : 0, 0x00020000);
-    };
-    auto lane_off = [&](int pp) { return (uint32_t)(((pass0 + pp) * kWave + lane) * BITS) * 4u; };
-    uint32_t nxt[BITS];
-    if (row < a.d_out) qg_load<BITS>(codes_rsrc(row), lane_off(0), nxt);
     float acc[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
