@@ -60,6 +60,11 @@ def _bind(lib):
         "oracle_lloyd": ([vp, i64, i32, i32, vp, vp, vp, vp], ctypes.c_int),
         "oracle_qgemm": ([vp, i32, i64, vp, vp, i64, i32, vp, vp, i32, vp, vp, i32, vp], ctypes.c_int),
         "oracle_rayleigh_lloyd_max": ([i32, vp, vp], ctypes.c_int),
+        "oracle_gauss_lloyd_max": ([i32, vp, vp], ctypes.c_int),
+        "oracle_scalar_index": ([f32, i32, vp], i32),
+        "oracle_scalar_table": ([i32, vp, vp], None),
+        "oracle_encode_scalar": ([vp, i32, i64, i32, i64, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp],
+                                 ctypes.c_int),
         "oracle_polar_index": ([f32, f32, i32, i32, vp], i32),
         "oracle_polar_table": ([i32, i32, vp, vp], None),
         "oracle_encode_polar": ([vp, i32, i64, i32, i64, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp],
@@ -260,6 +265,42 @@ class Oracle:
         rc = self.lib.oracle_encode_polar(self._p(w), bf, n, d_in, d_in, self._p(s), self._p(sign_bits), block, ba,
                                           bp, self._p(thr), self._p(sigma), self._p(norm), self._p(codes),
                                           self._p(idx), self._p(p), self._p(st))
+        assert rc == 0
+        return {"norm": norm, "codes": codes, "idx": idx, "p": p, "status": int(st[0])}
+
+    # ---- the scalar (d = 1) ablation, reading R10
+    def gauss_lloyd_max(self, b):
+        L = 1 << b
+        levels = np.empty((L,), dtype=np.float64)
+        thr = np.zeros((L - 1,), dtype=np.float64)
+        rc = self.lib.oracle_gauss_lloyd_max(b, self._p(levels), self._p(thr))
+        assert rc == 0
+        return levels, thr
+
+    def scalar_index(self, p, b, thresholds):
+        thr = np.ascontiguousarray(thresholds, dtype=np.float64)
+        return np.array([self.lib.oracle_scalar_index(float(v), b, self._p(thr)) for v in np.ravel(p)],
+                        dtype=np.int32)
+
+    def scalar_table(self, b, levels):
+        cb = np.empty((1 << (2 * b), 2), dtype=np.float32)
+        self.lib.oracle_scalar_table(b, self._p(np.ascontiguousarray(levels, dtype=np.float64)), self._p(cb))
+        return cb
+
+    def encode_scalar(self, w, s, sign_bits, block, b, thresholds, sigma, want_idx=True, want_p=False):
+        w, bf = self._w(w)
+        n, d_in = w.shape
+        stride = self.row_stride(d_in, 2 * b)
+        norm = np.empty((n,), dtype=np.uint16)
+        codes = np.empty((n, stride), dtype=np.uint8)
+        idx = np.empty((n, d_in // 2), dtype=np.int32) if want_idx else None
+        p = np.empty((n, d_in), dtype=np.float32) if want_p else None
+        st = np.zeros((1,), dtype=np.int32)
+        thr = np.ascontiguousarray(thresholds, dtype=np.float64)
+        sigma = np.ascontiguousarray(sigma, dtype=np.float32)
+        rc = self.lib.oracle_encode_scalar(self._p(w), bf, n, d_in, d_in, self._p(s), self._p(sign_bits), block, b,
+                                           self._p(thr), self._p(sigma), self._p(norm), self._p(codes), self._p(idx),
+                                           self._p(p), self._p(st))
         assert rc == 0
         return {"norm": norm, "codes": codes, "idx": idx, "p": p, "status": int(st[0])}
 

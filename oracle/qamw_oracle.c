@@ -50,6 +50,17 @@
  *      B = Ba + Bp bit index is ia + Na * ip, and the
  *      decoder is the QAM-W decoder with the table
  *      c[ia + Na ip] = fl32(a_ia cos(2 pi ip / Np)), fl32(a_ia sin(2 pi ip / Np)).
+ *   R10 scalar (d = 1) ablation (section 2, the PolarQuant comparison): the
+ *      same front end, then each coordinate of the scaled pair is coded alone
+ *      with the L = 2^b level Lloyd-Max quantizer of the standard normal
+ *      density (the law of each coordinate of a unit circular Gaussian pair),
+ *      b bits per coordinate, B = 2b per pair.  The start is the conditional
+ *      means of L equal-probability cells, whose edges are the normal
+ *      quantiles found by bisection; the iteration and its stopping rule are
+ *      those of R8.  A coordinate's index is the number of thresholds t with
+ *      t < fl64(p) (ties to the lower level); the pair's index is ix + L iy,
+ *      and the decoder is the QAM-W decoder with the product table
+ *      c[ix + L iy] = (fl32(a_ix), fl32(a_iy)).
  */
 #include "qamw_oracle.h"
 
@@ -393,12 +404,78 @@ void oracle_polar_table(int32_t ba, int32_t bp, const double* levels, float* cb)
     }
 }
 
+/* Section 2 (the scalar ablation, reading R10): integrals of the standard
+ * normal density phi over [a, b] (either end may be infinite):
+ * mass = Phi(b) - Phi(a); first moment = phi(a) - phi(b). */
+static double normal_pdf(double x)
+{
+    return isinf(x) ? 0.0 : exp(-0.5 * x * x) / sqrt(2.0 * ORACLE_PI);
+}
+static double normal_cdf(double x)
+{
+    return 0.5 * erfc(-x / sqrt(2.0));
+}
+
+int oracle_gauss_lloyd_max(int32_t b, double* levels, double* thresholds)
+{
+    if (b < 1 || b > 8) return -1;
+    int32_t L = 1 << b;
+    /* cell edges at the quantiles Phi^-1(i / L), by bisection to the last bit */
+    double* q = malloc(sizeof(double) * (size_t)(L + 1));
+    q[0] = -INFINITY;
+    q[L] = INFINITY;
+    for (int i = 1; i < L; ++i) {
+        double lo = -40.0, hi = 40.0, target = (double)i / L;
+        for (;;) {
+            double mid = 0.5 * (lo + hi);
+            if (mid <= lo || mid >= hi) break;
+            if (normal_cdf(mid) < target) lo = mid; else hi = mid;
+        }
+        q[i] = 0.5 * (lo + hi);
+    }
+    for (int i = 0; i < L; ++i)
+        levels[i] = (normal_pdf(q[i]) - normal_pdf(q[i + 1])) / (normal_cdf(q[i + 1]) - normal_cdf(q[i]));
+    free(q);
+    for (int it = 0; it < 10000; ++it) {
+        for (int i = 0; i + 1 < L; ++i) thresholds[i] = 0.5 * (levels[i] + levels[i + 1]);
+        int moved = 0;
+        for (int i = 0; i < L; ++i) {
+            double a = (i == 0) ? -INFINITY : thresholds[i - 1];
+            double c = (i + 1 == L) ? INFINITY : thresholds[i];
+            double v = (normal_pdf(a) - normal_pdf(c)) / (normal_cdf(c) - normal_cdf(a));
+            if (fabs(v - levels[i]) > 1e-15 * fabs(levels[i])) moved = 1;
+            levels[i] = v;
+        }
+        if (!moved) break;
+    }
+    for (int i = 0; i + 1 < L; ++i) thresholds[i] = 0.5 * (levels[i] + levels[i + 1]);
+    return 0;
+}
+
+int32_t oracle_scalar_index(float p, int32_t b, const double* thresholds)
+{
+    int32_t L = 1 << b, ix = 0;
+    for (int i = 0; i + 1 < L; ++i)
+        if ((double)p > thresholds[i]) ix = i + 1;
+    return ix;
+}
+
+void oracle_scalar_table(int32_t b, const double* levels, float* cb)
+{
+    int32_t L = 1 << b;
+    for (int iy = 0; iy < L; ++iy)
+        for (int ix = 0; ix < L; ++ix) {
+            cb[2 * (ix + L * iy)] = (float)levels[ix];
+            cb[2 * (ix + L * iy) + 1] = (float)levels[iy];
+        }
+}
+
 /* Section 3.1, steps 1-6, for every row passed in; step 5 is the nearest
  * codeword of cb (QAM-W, section 3.6) or, when thresholds is given, the polar
  * index (section 3.5, reading R8) with bits = ba + bp. */
 static int encode_rows(const void* w, int32_t w_bf16, int64_t n_rows, int32_t d_in, int64_t ld,
                        const float* s, const uint32_t* sign_bits, int32_t block, const float* cb,
-                       int32_t bits, const double* thresholds, int32_t ba, const float* sigma,
+                       int32_t bits, const double* thresholds, int32_t ba, int32_t scalar, const float* sigma,
                        uint16_t* norm16, uint8_t* codes, int32_t* idx_out, float* p_out, int32_t* status)
 {
     if (check_block(d_in, block) || ld < d_in || n_rows < 0 || bits < 1 || bits > 16) return -1;
@@ -425,6 +502,10 @@ static int encode_rows(const void* w, int32_t w_bf16, int64_t n_rows, int32_t d_
                     p_out[i * d_in + 2 * k] = px;
                     p_out[i * d_in + 2 * k + 1] = py;
                 }
+                if (scalar) /* step 5, one scalar quantizer per coordinate (reading R10) */
+                    idx[k] = oracle_scalar_index(px, bits / 2, thresholds) +
+                             (oracle_scalar_index(py, bits / 2, thresholds) << (bits / 2));
+                else
                 idx[k] = thresholds ? oracle_polar_index(px, py, ba, bits - ba, thresholds) /* step 5 */
                                     : oracle_nearest(px, py, cb, K, NULL);
             }
@@ -452,7 +533,7 @@ int oracle_encode(const void* w, int32_t w_bf16, int64_t n_rows, int32_t d_in, i
                   int32_t bits, const float* sigma, uint16_t* norm16, uint8_t* codes,
                   int32_t* idx_out, float* p_out, int32_t* status)
 {
-    return encode_rows(w, w_bf16, n_rows, d_in, ld, s, sign_bits, block, cb, bits, NULL, 0, sigma, norm16,
+    return encode_rows(w, w_bf16, n_rows, d_in, ld, s, sign_bits, block, cb, bits, NULL, 0, 0, sigma, norm16,
                        codes, idx_out, p_out, status);
 }
 
@@ -462,7 +543,17 @@ int oracle_encode_polar(const void* w, int32_t w_bf16, int64_t n_rows, int32_t d
                         int32_t* idx_out, float* p_out, int32_t* status)
 {
     if (ba < 1 || bp < 1 || ba + bp > 16) return -1;
-    return encode_rows(w, w_bf16, n_rows, d_in, ld, s, sign_bits, block, NULL, ba + bp, thresholds, ba, sigma,
+    return encode_rows(w, w_bf16, n_rows, d_in, ld, s, sign_bits, block, NULL, ba + bp, thresholds, ba, 0, sigma,
+                       norm16, codes, idx_out, p_out, status);
+}
+
+int oracle_encode_scalar(const void* w, int32_t w_bf16, int64_t n_rows, int32_t d_in, int64_t ld,
+                         const float* s, const uint32_t* sign_bits, int32_t block, int32_t b,
+                         const double* thresholds, const float* sigma, uint16_t* norm16, uint8_t* codes,
+                         int32_t* idx_out, float* p_out, int32_t* status)
+{
+    if (b < 1 || b > 8) return -1;
+    return encode_rows(w, w_bf16, n_rows, d_in, ld, s, sign_bits, block, NULL, 2 * b, thresholds, 0, 1, sigma,
                        norm16, codes, idx_out, p_out, status);
 }
 

@@ -55,6 +55,13 @@ MUTANTS = [
      "acc += (double)x[(size_t)m * ld_x + j] * (double)f32[(size_t)i * d_in + j];", "test_oracle_qgemm.py"),
     ("qgemm drops the last column", "for (int32_t j = 0; j < d_in; ++j) acc +=",
      "for (int32_t j = 0; j < d_in - 1; ++j) acc +=", "test_oracle_qgemm.py"),
+    # scalar (d = 1) ablation: caught by test_oracle_scalar.py
+    ("scalar cell mean sign", "double v = (normal_pdf(a) - normal_pdf(c)) / (normal_cdf(c) - normal_cdf(a));",
+     "double v = (normal_pdf(c) - normal_pdf(a)) / (normal_cdf(c) - normal_cdf(a));", "test_oracle_scalar.py"),
+    ("scalar ties to the upper level", "if ((double)p > thresholds[i]) ix = i + 1;",
+     "if ((double)p >= thresholds[i]) ix = i + 1;", "test_oracle_scalar.py"),
+    ("scalar table transposed", "cb[2 * (ix + L * iy)] = (float)levels[ix];", "cb[2 * (ix + L * iy)] = (float)levels[iy];",
+     "test_oracle_scalar.py"),
     ("polar table angle off by half a bin", "double th = 2.0 * ORACLE_PI * ip / np_;",
      "double th = 2.0 * ORACLE_PI * (ip + 0.5) / np_;", "test_oracle_polar.py"),
 ]
