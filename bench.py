@@ -12,8 +12,9 @@ The codebook training and the search-index build depend on the codebook only; th
 are timed once in the same run and reported beside the step.
 
 Beside the step: the fused dequantize-and-multiply of section 1 (y = x W^T from the codes, M = 1,
-4, 16 activation rows) against hipBLASLt on the decoded BF16 W and against decode-then-multiply; and
-the polar baseline of section 3.5 (5 + 6 and 4 + 4 bits) on the same matrix:
+4, 16 activation rows) against hipBLASLt on the decoded BF16 W and against decode-then-multiply; the
+reconstruction error of joint 2D, polar and scalar (d = 1) coding at equal bits on the same matrix;
+and the polar baseline of section 3.5 (5 + 6 and 4 + 4 bits) on the same matrix:
 codebook build, encode, encoder kernel alone, decode.
 
 After the step, unless --no-stack: a 40-layer 13B-shaped stack (per layer q, k, v, o 5120x5120,
@@ -229,6 +230,9 @@ def main():
     for ba, bp in ((5, 6), (4, 4)):
         result["polar_%d_%d" % (ba, bp)] = polar_run(torch, q, sets, n_sets, scale, sign, block, ba, bp, timed, stream)
 
+    # ---------------------------------------------------------------- d = 2 vs polar vs d = 1 at equal bits
+    result["ablation"] = ablation_run(torch, q, sets[0], pts, cfg, cb, bits, scale, sign, block)
+
     # ---------------------------------------------------------------- 40-layer stack (sustained rates)
     if not args.no_stack:
         del sets
@@ -298,6 +302,51 @@ def qgemm_run(torch, q, sets, n_sets, cb, bits, scale, sign, block, timed):
                           "hbm_frac": round(alg / (t_f * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                           "kernel": "vector units" if M < 6 else "matrix cores (fp32)"}
         del ws, tmp
+    return res
+
+
+def ablation_run(torch, q, bset, pts, cfg, cb11, bits11, scale, sign, block):
+    """Relative reconstruction error ||W^ - W||_F / ||W||_F of the step's matrix (BF16 decode) for the
+    joint 2D code (QAM-W), the polar code (section 3.5) and the scalar d = 1 code (section 2) at
+    equal bits per pair; each is one GPU encode and decode.  QAM-W codebooks at B = 8 and 12 are
+    trained like the step's (same points and iteration count)."""
+    w = bset["w"]
+    d_out, d_in = w.shape
+    wf = w.float()
+    wn = float(torch.linalg.vector_norm(wf))
+    out = torch.empty_like(w)
+
+    def err(table, nbits, index=None, thr=None, ba=None):
+        if thr is None:
+            idx = q.codebook_index(table, nbits) if index is None else index
+            e = q.encode(w, table, nbits, idx, scale=scale, sign_bits=sign, block=block)
+        else:
+            e = q.encode_polar(w, ba, nbits - ba, thr, scale=scale, sign_bits=sign, block=block)
+        q.decode(e["codes"], e["norm"], e["sigma"], table, nbits, d_in, scale=scale, sign_bits=sign, block=block,
+                 out=out)
+        return round(float(torch.linalg.vector_norm(out.float() - wf)) / wn, 6)
+
+    res = {}
+    for B in (8, 11, 12):
+        row = {}
+        if B == bits11:
+            row["qamw_2d"] = err(cb11, B)
+        else:
+            cbB, _ = q.codebook_train(pts, B, cfg.lloyd_iters)
+            row["qamw_2d"] = err(cbB, B)
+        # the same training run longer: Lloyd from the first K points is far from converged after
+        # the workload's iterations at these K
+        cbL, trL = q.codebook_train(pts, B, 10 * cfg.lloyd_iters)
+        row["qamw_2d_%dit" % (10 * cfg.lloyd_iters)] = err(cbL, B)
+        row["lloyd_mse_%dit" % (10 * cfg.lloyd_iters)] = round(float(trL[-1].item()) / 2**32 / pts.shape[0], 7)
+        ba = {8: 4, 11: 5, 12: 6}[B]
+        _, thr, table = q.polar_codebook(ba, B - ba)
+        row["polar_%d+%d" % (ba, B - ba)] = err(table, B, thr=thr, ba=ba)
+        if B % 2 == 0:
+            _, _, tab1 = q.scalar_codebook(B // 2)
+            row["scalar_d1_%d+%d" % (B // 2, B // 2)] = err(tab1, B)
+        res["B%d" % B] = row
+    res["note"] = "relative Frobenius error of the BF16 decode of the step's synthetic matrix; lower is better"
     return res
 
 

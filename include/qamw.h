@@ -217,6 +217,21 @@ int qamw_encode_polar(const void* d_w, qamw_dtype w_dtype, int32_t d_out, int32_
                       uint16_t* d_norm_f16, uint8_t* d_codes, int32_t* d_status, void* d_ws, size_t ws_bytes,
                       void* stream);
 
+/* Section 2 (the scalar, d = 1, ablation that the paper names as its first follow-up): the same front
+ * end, with each coordinate of the scaled pair coded alone by the L = 2^b level Lloyd-Max quantizer of
+ * the standard normal density (the law of each coordinate of a unit circular Gaussian pair).  The
+ * start is the conditional means of L equal-probability cells (edges at the normal quantiles, by
+ * bisection); the rounds and the stopping rule are those of qamw_polar_codebook.  Writes:
+ *   d_levels      L doubles, increasing (symmetric about 0);
+ *   d_thresholds  L - 1 doubles, midpoints of adjacent levels;
+ *   d_codebook    L * L interleaved fp32 pairs, entry ix + L iy = (fl32(a_ix), fl32(a_iy)): the
+ *                 product table.  Nearest-codeword search over it (qamw_codebook_index +
+ *                 qamw_encode with bits = 2b) gives each coordinate its nearest level (ties between
+ *                 levels within fp32 rounding of the distance), and qamw_decode decodes it.
+ * Limits: 1 <= b <= 6 (QAMW_ERR_UNSUPPORTED for 7 and 8, QAMW_ERR_ARG otherwise).  Device pointers,
+ * 8-byte aligned, owned by the caller. */
+int qamw_scalar_codebook(int32_t b, double* d_levels, double* d_thresholds, float* d_codebook, void* stream);
+
 /* Human-readable text for a return code. */
 const char* qamw_status_string(int code);
 

@@ -22,7 +22,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = q.header_symbols()
-    assert len(names) == 16
+    assert len(names) == 17
     out = subprocess.run(["nm", "-D", "--defined-only", q.LIB_PATH], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
     for n in names:
@@ -195,3 +195,11 @@ def test_qgemm_noops_and_workspace(lib):
     # 13824 columns at 16 rows: the rotated activations of all 16 rows
     assert lib.qamw_qgemm_workspace(16, 5120, 13824) >= 16 * 13824 * 4
     assert lib.qamw_qgemm_workspace(1, 16, 255) == 0
+
+
+def test_scalar_codebook_rejects(lib):
+    assert lib.qamw_scalar_codebook(0, FAKE, FAKE, FAKE, None) == ARG
+    assert lib.qamw_scalar_codebook(9, FAKE, FAKE, FAKE, None) == ARG
+    assert lib.qamw_scalar_codebook(7, FAKE, FAKE, FAKE, None) == UNSUP
+    assert lib.qamw_scalar_codebook(4, None, FAKE, FAKE, None) == ARG
+    assert lib.qamw_scalar_codebook(4, FAKE, FAKE, FAKE + 4, None) == ARG

@@ -64,6 +64,7 @@ def load(path: Optional[str] = None):
                         vp, sz, vp], ctypes.c_int),
         "qamw_polar_codebook": ([i32, i32, vp, vp, vp, vp], ctypes.c_int),
         "qamw_polar_index": ([vp, i64, i32, i32, vp, vp, vp, vp], ctypes.c_int),
+        "qamw_scalar_codebook": ([i32, vp, vp, vp, vp], ctypes.c_int),
         "qamw_encode_polar": ([vp, ctypes.c_int, i32, i32, i64, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz,
                                vp], ctypes.c_int),
         "qamw_status_string": ([ctypes.c_int], ctypes.c_char_p),
@@ -270,6 +271,19 @@ def polar_codebook(ba: int, bp: int, device=None):
     rc = load().qamw_polar_codebook(ba, bp, _ptr(levels), _ptr(thr), _ptr(table), _stream())
     _check(rc, "qamw_polar_codebook")
     return levels, thr[: na - 1], table
+
+
+def scalar_codebook(b: int, device=None):
+    """Scalar (d = 1) ablation (section 2): (levels float64[2^b], thresholds float64[2^b - 1],
+    product table float32[2^(2b), 2]) for qamw_codebook_index / encode / decode with bits = 2b."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    L = 1 << b
+    levels = torch.empty((L,), dtype=torch.float64, device=dev)
+    thr = torch.empty((L - 1,), dtype=torch.float64, device=dev)
+    table = torch.empty((L * L, 2), dtype=torch.float32, device=dev)
+    rc = load().qamw_scalar_codebook(b, _ptr(levels), _ptr(thr), _ptr(table), _stream())
+    _check(rc, "qamw_scalar_codebook")
+    return levels, thr, table
 
 
 def polar_index(points: torch.Tensor, ba: int, bp: int, thresholds: torch.Tensor,

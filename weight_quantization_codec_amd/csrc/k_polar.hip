@@ -20,6 +20,7 @@ namespace qamw {
 namespace {
 
 constexpr int kPolarIters = 10000;
+constexpr int kScalarMaxB = 6;   // 2b <= 12 index bits
 
 __device__ inline double ray_F(double r) { return __builtin_isinf(r) ? 0.0 : exp(-0.5 * r * r); }
 
@@ -91,7 +92,79 @@ __global__ __launch_bounds__(256) void k_polar_index(const float2* __restrict__ 
     }
 }
 
+// Scalar (d = 1) ablation (paper section 2): the L-level Lloyd-Max quantizer of the standard
+// normal density, for each coordinate of a pair, and the L x L product table (entry ix + L iy =
+// (a_ix, a_iy)).  Start: the conditional means of L equal-probability cells, whose edges are the
+// quantiles Phi^-1(i / L) found by bisection to the last bit; then the Lloyd-Max rounds of
+// k_polar_codebook.  With phi the density and Phi the distribution function, a cell's mean is
+// (phi(a) - phi(c)) / (Phi(c) - Phi(a)); the mass is taken from the nearer tail (erfc), free of
+// cancellation.
+__device__ inline double nrm_pdf(double x) {
+    return __builtin_isinf(x) ? 0.0 : exp(-0.5 * x * x) * 0.39894228040143267794;   // 1/sqrt(2 pi)
+}
+__device__ inline double nrm_cdf(double x) { return 0.5 * erfc(-x * 0.70710678118654752440); }
+__device__ inline double nrm_mass(double a, double c) {
+    const double rs2 = 0.70710678118654752440;
+    if (a >= 0.0) return 0.5 * (erfc(a * rs2) - (__builtin_isinf(c) ? 0.0 : erfc(c * rs2)));
+    return 0.5 * ((__builtin_isinf(c) ? 2.0 : erfc(-c * rs2)) - erfc(-a * rs2));
+}
+__device__ inline double nrm_cell_mean(double a, double c) { return (nrm_pdf(a) - nrm_pdf(c)) / nrm_mass(a, c); }
+
+__global__ __launch_bounds__(256) void k_scalar_codebook(int b, double* __restrict__ levels, double* __restrict__ thr,
+                                                         float* __restrict__ cb) {
+    __shared__ double lv[1 << kScalarMaxB];
+    __shared__ double th[1 << kScalarMaxB];
+    __shared__ double q[(1 << kScalarMaxB) + 1];
+    const int L = 1 << b, i = threadIdx.x;
+    const bool mine = i < L;
+    const double inf = __builtin_huge_val();
+    if (i <= L) {
+        double e = i == 0 ? -inf : inf;
+        if (i > 0 && i < L) {
+            double lo = -40.0, hi = 40.0;
+            const double target = (double)i / (double)L;
+            for (;;) {
+                const double mid = 0.5 * (lo + hi);
+                if (mid <= lo || mid >= hi) break;
+                if (nrm_cdf(mid) < target) lo = mid; else hi = mid;
+            }
+            e = 0.5 * (lo + hi);
+        }
+        q[i] = e;
+    }
+    __syncthreads();
+    if (mine) lv[i] = nrm_cell_mean(q[i], q[i + 1]);
+    __syncthreads();
+    for (int it = 0; it < kPolarIters; ++it) {
+        if (i + 1 < L) th[i] = 0.5 * (lv[i] + lv[i + 1]);
+        __syncthreads();
+        bool moved = false;
+        double v = 0.0;
+        if (mine) {
+            const double a = i == 0 ? -inf : th[i - 1];
+            const double c = i + 1 == L ? inf : th[i];
+            v = nrm_cell_mean(a, c);
+            moved = fabs(v - lv[i]) > 1e-15 * fabs(lv[i]);
+        }
+        if (mine) lv[i] = v;
+        if (!__syncthreads_or(moved)) break;
+    }
+    if (i + 1 < L) th[i] = 0.5 * (lv[i] + lv[i + 1]);
+    __syncthreads();
+    if (mine) levels[i] = lv[i];
+    if (i + 1 < L) thr[i] = th[i];
+    for (int k = i; k < L * L; k += blockDim.x) {
+        cb[2 * k] = (float)lv[k & (L - 1)];
+        cb[2 * k + 1] = (float)lv[k >> b];
+    }
+}
+
 }  // namespace
+
+hipError_t launch_scalar_codebook(int b, double* levels, double* thr, float* cb, hipStream_t st) {
+    hipLaunchKernelGGL(k_scalar_codebook, dim3(1), dim3(256), 0, st, b, levels, thr, cb);
+    return hipGetLastError();
+}
 
 hipError_t launch_polar_index(const float* pts, int64_t n, int ba, int bp, const double* thr, int32_t* out,
                               int32_t* status, hipStream_t st) {

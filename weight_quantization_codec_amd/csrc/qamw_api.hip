@@ -255,6 +255,15 @@ int qamw_polar_codebook(int32_t ba, int32_t bp, double* d_levels, double* d_thre
     return hip_rc(launch_polar_codebook(ba, bp, d_levels, d_thresholds, d_codebook, (hipStream_t)stream));
 }
 
+int qamw_scalar_codebook(int32_t b, double* d_levels, double* d_thresholds, float* d_codebook, void* stream) {
+    if (b < 1 || b > 8) return QAMW_ERR_ARG;
+    if (b > 6) return QAMW_ERR_UNSUPPORTED;
+    if (!d_levels || !d_thresholds || !d_codebook || !aligned(d_levels, 8) || !aligned(d_thresholds, 8) ||
+        !aligned(d_codebook, 8))
+        return QAMW_ERR_ARG;
+    return hip_rc(launch_scalar_codebook(b, d_levels, d_thresholds, d_codebook, (hipStream_t)stream));
+}
+
 int qamw_polar_index(const float* d_points, int64_t n, int32_t ba, int32_t bp, const double* d_thresholds,
                      int32_t* d_idx, int32_t* d_status, void* stream) {
     int rc = check_polar_bits(ba, bp);

@@ -80,6 +80,7 @@ hipError_t launch_calibrate(const CalibArgs& a, int L, float* sigma_out, hipStre
 hipError_t launch_encode(const EncodeArgs& a, int L, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, int L, hipStream_t st);
 hipError_t launch_polar_codebook(int ba, int bp, double* levels, double* thr, float* cb, hipStream_t st);
+hipError_t launch_scalar_codebook(int b, double* levels, double* thr, float* cb, hipStream_t st);
 hipError_t launch_polar_index(const float* pts, int64_t n, int ba, int bp, const double* thr, int32_t* out,
                               int32_t* status, hipStream_t st);
 
