@@ -61,6 +61,7 @@ def _bind(lib):
         "oracle_qgemm": ([vp, i32, i64, vp, vp, i64, i32, vp, vp, i32, vp, vp, i32, vp], ctypes.c_int),
         "oracle_rayleigh_lloyd_max": ([i32, vp, vp], ctypes.c_int),
         "oracle_gauss_lloyd_max": ([i32, vp, vp], ctypes.c_int),
+        "oracle_act_scale": ([vp, i64, i32, i64, dbl, vp, vp], ctypes.c_int),
         "oracle_scalar_index": ([f32, i32, vp], i32),
         "oracle_scalar_table": ([i32, vp, vp], None),
         "oracle_encode_scalar": ([vp, i32, i64, i32, i64, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp],
@@ -267,6 +268,16 @@ class Oracle:
                                           self._p(idx), self._p(p), self._p(st))
         assert rc == 0
         return {"norm": norm, "codes": codes, "idx": idx, "p": p, "status": int(st[0])}
+
+    def act_scale(self, x, alpha):
+        """Activation-aware channel scale (reading R11): (s fp32[d_in], r fp64[d_in])."""
+        x = np.ascontiguousarray(np.atleast_2d(x), dtype=np.float32)
+        T, d_in = x.shape
+        s = np.empty((d_in,), dtype=np.float32)
+        r = np.empty((d_in,), dtype=np.float64)
+        rc = self.lib.oracle_act_scale(self._p(x), T, d_in, d_in, float(alpha), self._p(s), self._p(r))
+        assert rc == 0
+        return s, r
 
     # ---- the scalar (d = 1) ablation, reading R10
     def gauss_lloyd_max(self, b):

@@ -61,6 +61,13 @@
  *      t < fl64(p) (ties to the lower level); the pair's index is ix + L iy,
  *      and the decoder is the QAM-W decoder with the product table
  *      c[ix + L iy] = (fl32(a_ix), fl32(a_iy)).
+ *   R11 activation-aware channel scale (section 1 and the summary of the
+ *      AWQ-style scaling): s_j = fl32(r_j^alpha), r_j the RMS of input channel j
+ *      over the calibration activations, sqrt(sum_t x_tj^2 / T) in fp64; a
+ *      channel that is zero over the batch gets s_j = 1 (its weights never
+ *      reach the output, any positive scale serves).  The pages state s_j only
+ *      up to a constant; a global factor cancels between the row norm and the
+ *      decoder's division by s, so the constant 1 is taken.
  */
 #include "qamw_oracle.h"
 
@@ -635,6 +642,24 @@ int oracle_qgemm(const float* x, int32_t M, int64_t ld_x, const uint8_t* codes, 
     free(f32);
     free(b16);
     return rc;
+}
+
+/* Activation-aware channel scale (reading R11): x is T x d_in (fp32 values,
+ * leading dimension ld); rms (may be NULL) receives r_j. */
+int oracle_act_scale(const float* x, int64_t T, int32_t d_in, int64_t ld, double alpha, float* scale, double* rms)
+{
+    if (T < 1 || d_in < 1 || ld < d_in) return -1;
+    for (int32_t j = 0; j < d_in; ++j) {
+        double acc = 0.0;
+        for (int64_t t = 0; t < T; ++t) {
+            double v = (double)x[t * ld + j];
+            acc += v * v;
+        }
+        double r = sqrt(acc / (double)T);
+        if (rms) rms[j] = r;
+        scale[j] = r > 0.0 ? (float)pow(r, alpha) : 1.0f;
+    }
+    return 0;
 }
 
 /* Section 3.6, eq. 2: Lloyd iterations for the 2D codebook on samples of the

@@ -70,6 +70,8 @@ int oracle_encode_polar(const void* w, int32_t w_bf16, int64_t n_rows, int32_t d
                         const float* s, const uint32_t* sign_bits, int32_t block, int32_t ba, int32_t bp,
                         const double* thresholds, const float* sigma, uint16_t* norm16, uint8_t* codes,
                         int32_t* idx_out, float* p_out, int32_t* status);
+/* the activation-aware channel scale (reading R11) */
+int oracle_act_scale(const float* x, int64_t T, int32_t d_in, int64_t ld, double alpha, float* scale, double* rms);
 /* section 2, the scalar (d = 1) ablation (reading R10) */
 int oracle_gauss_lloyd_max(int32_t b, double* levels, double* thresholds);
 int32_t oracle_scalar_index(float p, int32_t b, const double* thresholds);

@@ -62,6 +62,13 @@ MUTANTS = [
      "if ((double)p >= thresholds[i]) ix = i + 1;", "test_oracle_scalar.py"),
     ("scalar table transposed", "cb[2 * (ix + L * iy)] = (float)levels[ix];", "cb[2 * (ix + L * iy)] = (float)levels[iy];",
      "test_oracle_scalar.py"),
+    # activation-aware channel scale: caught by test_oracle_actscale.py
+    ("act scale without the root", "double r = sqrt(acc / (double)T);", "double r = acc / (double)T;",
+     "test_oracle_actscale.py"),
+    ("act scale over T - 1", "double r = sqrt(acc / (double)T);", "double r = sqrt(acc / (double)(T - 1));",
+     "test_oracle_actscale.py"),
+    ("dead channel scale 0", "scale[j] = r > 0.0 ? (float)pow(r, alpha) : 1.0f;", "scale[j] = (float)pow(r, alpha);",
+     "test_oracle_actscale.py"),
     ("polar table angle off by half a bin", "double th = 2.0 * ORACLE_PI * ip / np_;",
      "double th = 2.0 * ORACLE_PI * (ip + 0.5) / np_;", "test_oracle_polar.py"),
 ]
