@@ -14,6 +14,8 @@ are timed once in the same run and reported beside the step.
 Beside the step: the fused dequantize-and-multiply of section 1 (y = x W^T from the codes, M = 1,
 4, 16 activation rows) against hipBLASLt on the decoded BF16 W and against decode-then-multiply; the
 reconstruction error of joint 2D, polar and scalar (d = 1) coding at equal bits on the same matrix;
+the activation-aware channel scale (time on a 2048-row calibration batch, and the layer-output error
+it leaves for several alpha);
 and the polar baseline of section 3.5 (5 + 6 and 4 + 4 bits) on the same matrix:
 codebook build, encode, encoder kernel alone, decode.
 
@@ -230,6 +232,9 @@ def main():
     for ba, bp in ((5, 6), (4, 4)):
         result["polar_%d_%d" % (ba, bp)] = polar_run(torch, q, sets, n_sets, scale, sign, block, ba, bp, timed, stream)
 
+    # ---------------------------------------------------------------- activation-aware channel scale
+    result["act_scale"] = act_scale_run(torch, q, sets[0], cb, bits, index, sign, block, timed)
+
     # ---------------------------------------------------------------- d = 2 vs polar vs d = 1 at equal bits
     result["ablation"] = ablation_run(torch, q, sets[0], pts, cfg, cb, bits, scale, sign, block)
 
@@ -302,6 +307,44 @@ def qgemm_run(torch, q, sets, n_sets, cb, bits, scale, sign, block, timed):
                           "hbm_frac": round(alg / (t_f * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                           "kernel": "vector units" if M < 6 else "matrix cores (fp32)"}
         del ws, tmp
+    return res
+
+
+def act_scale_run(torch, q, bset, cb, bits, index, sign, block, timed):
+    """qamw_act_scale on a 2048 x d_in BF16 calibration batch (time, HBM rate), and the layer-output
+    error ||X dW^T||_F^2 / ||X W^T||_F^2 of the step's matrix coded with s = r^alpha for several
+    alpha (alpha = 0 is s = 1).  Activations: synthetic, drawn on the GPU, per-channel RMS
+    exp(0.5 N(0,1)) with 1% of the channels x30 (the strong channels of LLM activations)."""
+    w = bset["w"]
+    d_out, d_in = w.shape
+    dev = w.device
+    g = torch.Generator(device=dev)
+    g.manual_seed(17)
+    T = 2048
+    rho = torch.exp(0.5 * torch.randn(d_in, device=dev, generator=g))
+    strong = torch.randperm(d_in, device=dev, generator=g)[: d_in // 100]
+    rho[strong] *= 30
+    x = (torch.randn((T, d_in), device=dev, generator=g) * rho).to(torch.bfloat16)
+    ws = torch.empty((q.load().qamw_act_scale_workspace(T, d_in),), dtype=torch.uint8, device=dev)
+    for _ in range(5):
+        q.act_scale(x, 0.3, workspace=ws)
+    torch.cuda.synchronize()
+    t_ms = timed(lambda i: q.act_scale(x, 0.3, workspace=ws), 100)
+    res = {"T": T, "d_in": d_in, "act_scale_us": round(t_ms * 1e3, 2),
+           "hbm_GBps": round(T * d_in * 2 / (t_ms * 1e-3) / 1e9, 1),
+           "hbm_frac": round(T * d_in * 2 / (t_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+    xf = x.float()
+    wf = w.float()
+    y2 = float(torch.sum((xf @ wf.t()) ** 2))
+    out = torch.empty((d_out, d_in), dtype=torch.float32, device=dev)
+    errs = {}
+    for alpha in (0.0, 0.3, 0.5):
+        s = q.act_scale(x, alpha, workspace=ws)
+        e = q.encode(w, cb, bits, index, scale=s, sign_bits=sign, block=block)
+        q.decode(e["codes"], e["norm"], e["sigma"], cb, bits, d_in, scale=s, sign_bits=sign, block=block, out=out)
+        errs["alpha_%g" % alpha] = round(float(torch.sum((xf @ (out - wf).t()) ** 2)) / y2, 7)
+    res["output_error"] = errs
+    res["data"] = "synthetic activations drawn on the GPU; relative layer-output error, lower is better"
     return res
 
 

@@ -217,6 +217,20 @@ int qamw_encode_polar(const void* d_w, qamw_dtype w_dtype, int32_t d_out, int32_
                       uint16_t* d_norm_f16, uint8_t* d_codes, int32_t* d_status, void* d_ws, size_t ws_bytes,
                       void* stream);
 
+/* The activation-aware per-channel scale (the AWQ-style scaling of the paper, motivated by the
+ * layer-output trace identity ||X dW^T||_F^2 = Tr(dW X^T X dW^T)): from T calibration activation
+ * rows X (T x d_in, QAMW_F32 or QAMW_BF16, leading dimension ld_x >= d_in),
+ *   r_j = sqrt(sum_t x_tj^2 / T)   (fp64, fixed-order chunked sums: deterministic)
+ *   s_j = fl32(r_j^alpha), or 1 for a channel that is zero over the batch,
+ * written to d_scale (d_in fp32, the d_scale of qamw_encode / qamw_decode / qamw_qgemm) and, when
+ * d_rms is not NULL, r to d_rms (d_in doubles).  The pages give s only up to a constant factor; a
+ * global factor cancels between the row norm and the decoder's division, so none is applied.
+ * alpha must be finite (the paper uses 0.3).  d_ws: at least qamw_act_scale_workspace(T, d_in)
+ * bytes, 8-byte aligned.  T >= 1, d_in >= 1, else QAMW_ERR_ARG. */
+size_t qamw_act_scale_workspace(int64_t T, int32_t d_in);
+int qamw_act_scale(const void* d_x, qamw_dtype x_dtype, int64_t T, int32_t d_in, int64_t ld_x, double alpha,
+                   float* d_scale, double* d_rms, void* d_ws, size_t ws_bytes, void* stream);
+
 /* Section 2 (the scalar, d = 1, ablation that the paper names as its first follow-up): the same front
  * end, with each coordinate of the scaled pair coded alone by the L = 2^b level Lloyd-Max quantizer of
  * the standard normal density (the law of each coordinate of a unit circular Gaussian pair).  The

@@ -22,7 +22,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = q.header_symbols()
-    assert len(names) == 17
+    assert len(names) == 19
     out = subprocess.run(["nm", "-D", "--defined-only", q.LIB_PATH], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
     for n in names:
@@ -203,3 +203,18 @@ def test_scalar_codebook_rejects(lib):
     assert lib.qamw_scalar_codebook(7, FAKE, FAKE, FAKE, None) == UNSUP
     assert lib.qamw_scalar_codebook(4, None, FAKE, FAKE, None) == ARG
     assert lib.qamw_scalar_codebook(4, FAKE, FAKE, FAKE + 4, None) == ARG
+
+
+def test_act_scale_rejects(lib):
+    import math
+    ok = dict(x=FAKE, dt=q.BF16, T=16, d=64, ld=64, a=0.3, s=FAKE, r=None, ws=FAKE, wsb=1 << 20)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return lib.qamw_act_scale(a["x"], a["dt"], a["T"], a["d"], a["ld"], a["a"], a["s"], a["r"], a["ws"], a["wsb"], None)
+    assert call(T=0) == ARG and call(d=0) == ARG and call(ld=32) == ARG and call(dt=9) == ARG
+    assert call(a=math.inf) == ARG and call(a=math.nan) == ARG and call(x=None) == ARG and call(s=FAKE + 2) == ARG
+    assert call(x=FAKE + 1) == ARG and call(r=FAKE + 4) == ARG
+    assert call(ws=None) == WS and call(wsb=8) == WS
+    assert lib.qamw_act_scale_workspace(2048, 4096) >= 4096 * 8 and lib.qamw_act_scale_workspace(0, 8) == 0

@@ -65,6 +65,8 @@ def load(path: Optional[str] = None):
         "qamw_polar_codebook": ([i32, i32, vp, vp, vp, vp], ctypes.c_int),
         "qamw_polar_index": ([vp, i64, i32, i32, vp, vp, vp, vp], ctypes.c_int),
         "qamw_scalar_codebook": ([i32, vp, vp, vp, vp], ctypes.c_int),
+        "qamw_act_scale_workspace": ([i64, i32], sz),
+        "qamw_act_scale": ([vp, ctypes.c_int, i64, i32, i64, ctypes.c_double, vp, vp, vp, sz, vp], ctypes.c_int),
         "qamw_encode_polar": ([vp, ctypes.c_int, i32, i32, i64, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz,
                                vp], ctypes.c_int),
         "qamw_status_string": ([ctypes.c_int], ctypes.c_char_p),
@@ -271,6 +273,21 @@ def polar_codebook(ba: int, bp: int, device=None):
     rc = load().qamw_polar_codebook(ba, bp, _ptr(levels), _ptr(thr), _ptr(table), _stream())
     _check(rc, "qamw_polar_codebook")
     return levels, thr[: na - 1], table
+
+
+def act_scale(x: torch.Tensor, alpha: float = 0.3, want_rms: bool = False, workspace: Optional[torch.Tensor] = None):
+    """Activation-aware channel scale s_j = r_j^alpha from T x d_in calibration activations (bf16/fp32).
+    Returns s (fp32[d_in]), or (s, r fp64[d_in]) with want_rms."""
+    if x.dtype not in (torch.bfloat16, torch.float32) or not x.is_cuda or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a T x d_in bf16 or fp32 device tensor with contiguous rows")
+    T, d_in = x.shape
+    s = torch.empty((d_in,), dtype=torch.float32, device=x.device)
+    r = torch.empty((d_in,), dtype=torch.float64, device=x.device) if want_rms else None
+    ws = workspace if workspace is not None else _ws(load().qamw_act_scale_workspace(T, d_in), x.device)
+    rc = load().qamw_act_scale(_ptr(x), BF16 if x.dtype == torch.bfloat16 else F32, T, d_in, x.stride(0), float(alpha),
+                               _ptr(s), _ptr(r), _ptr(ws), ws.numel(), _stream())
+    _check(rc, "qamw_act_scale")
+    return (s, r) if want_rms else s
 
 
 def scalar_codebook(b: int, device=None):

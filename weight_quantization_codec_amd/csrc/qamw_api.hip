@@ -255,6 +255,23 @@ int qamw_polar_codebook(int32_t ba, int32_t bp, double* d_levels, double* d_thre
     return hip_rc(launch_polar_codebook(ba, bp, d_levels, d_thresholds, d_codebook, (hipStream_t)stream));
 }
 
+size_t qamw_act_scale_workspace(int64_t T, int32_t d_in) {
+    if (T < 1 || d_in < 1) return 0;
+    return (size_t)act_chunks(T) * (size_t)d_in * sizeof(double);
+}
+
+int qamw_act_scale(const void* d_x, qamw_dtype x_dtype, int64_t T, int32_t d_in, int64_t ld_x, double alpha,
+                   float* d_scale, double* d_rms, void* d_ws, size_t ws_bytes, void* stream) {
+    if (T < 1 || d_in < 1 || ld_x < d_in || (x_dtype != QAMW_F32 && x_dtype != QAMW_BF16) || !std::isfinite(alpha))
+        return QAMW_ERR_ARG;
+    if (!d_x || !d_scale || !aligned(d_x, x_dtype == QAMW_BF16 ? 2 : 4) || !aligned(d_scale, 4) ||
+        (d_rms && !aligned(d_rms, 8)))
+        return QAMW_ERR_ARG;
+    if (!d_ws || !aligned(d_ws, 8) || ws_bytes < qamw_act_scale_workspace(T, d_in)) return QAMW_ERR_WORKSPACE;
+    return hip_rc(launch_act_scale(d_x, x_dtype == QAMW_BF16, T, d_in, ld_x, alpha, d_scale, d_rms,
+                                   reinterpret_cast<double*>(d_ws), (hipStream_t)stream));
+}
+
 int qamw_scalar_codebook(int32_t b, double* d_levels, double* d_thresholds, float* d_codebook, void* stream) {
     if (b < 1 || b > 8) return QAMW_ERR_ARG;
     if (b > 6) return QAMW_ERR_UNSUPPORTED;

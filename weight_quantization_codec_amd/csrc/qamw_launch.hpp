@@ -81,6 +81,9 @@ hipError_t launch_encode(const EncodeArgs& a, int L, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, int L, hipStream_t st);
 hipError_t launch_polar_codebook(int ba, int bp, double* levels, double* thr, float* cb, hipStream_t st);
 hipError_t launch_scalar_codebook(int b, double* levels, double* thr, float* cb, hipStream_t st);
+int act_chunks(int64_t T);
+hipError_t launch_act_scale(const void* x, int x_bf16, int64_t T, int d_in, int64_t ld, double alpha, float* scale,
+                            double* rms, double* partial, hipStream_t st);
 hipError_t launch_polar_index(const float* pts, int64_t n, int ba, int bp, const double* thr, int32_t* out,
                               int32_t* status, hipStream_t st);
 
