@@ -160,9 +160,12 @@ int qamw_decode(const uint8_t* d_codes, const uint16_t* d_norm_f16, const float*
  * decoder's arguments as there), computed without forming W^: the activation is rotated instead,
  * u = sigma . blockdiag(H_b)(eps . x / s) (fp64, rounded to fp32 once), and
  *   y[m][i] = f16(norm_i) * sum_k (c[idx_ik].x u_m,2k + c[idx_ik].y u_m,2k+1)
- * summed in fp32 (blocked: 32 pairs per lane, then a fixed-order wavefront sum; rows longer than the
- * LDS tile add per-split partial sums in a fixed order).  Error against the exact product: at most
- * about 1e-6 of sum_j |x_mj w^_ij| for d_in <= 16384.
+ * summed in fp32 (up to 5 rows on the vector units: 32 pairs per lane, then a fixed-order wavefront
+ * sum, rows longer than the LDS tile adding per-split partial sums in a fixed order; from 6 rows on
+ * the matrix cores, v_mfma_f32_16x16x4f32 with per-wavefront partials added in a fixed order).
+ * Every one of the d_in products rounds at most once on its way, so the error against the exact
+ * product is at most (d_in + 64) 2^-24 times f16(norm_i) sum_k |c[idx_ik].x u_m,2k| + |c.y u_m,2k+1|
+ * (measured: below 1e-7 of that sum).
  * Arguments:
  *   d_x, x_dtype, M, ld_x   M x d_in activations (QAMW_F32 or QAMW_BF16), row m at d_x + m ld_x.
  *                           1 <= M <= 16 (QAMW_ERR_UNSUPPORTED above; M = 0 is a no-op).
