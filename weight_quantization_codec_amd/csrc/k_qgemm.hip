@@ -249,7 +249,7 @@ __global__ __launch_bounds__(kQgThreads) void k_qgemm(QgemmArgs a) {
 // r for pairs 32 (q / 2) .. + 31 of the chunk: 32 B bits, dword-aligned, as in k_qgemm.
 // Workgroup: one tile of 16 rows, kQmWaves wavefronts taking the chunks c = w, w + kQmWaves, ...;
 // their partial D are added in LDS in wavefront order.
-constexpr int kQmWaves = 8;
+constexpr int kQmWaves = 4;
 
 template <int BITS>
 __global__ __launch_bounds__(kQmWaves * kWave) void k_qgemm_mfma(QgemmArgs a) {
@@ -259,19 +259,20 @@ __global__ __launch_bounds__(kQmWaves * kWave) void k_qgemm_mfma(QgemmArgs a) {
     float* cbf = reinterpret_cast<float*>(smem);                                   // K x 2
     f32x4* part = reinterpret_cast<f32x4*>(smem + (size_t)K * sizeof(float2));     // kQmWaves x 64
     const int lane = threadIdx.x & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    {   // the codebook: every load issued before the stores (K / 2 <= 2048 float4: four per thread)
+    {   // the codebook: every load issued before the stores (K / 2 <= 2048 float4)
         typedef float f4 __attribute__((ext_vector_type(4)));
+        constexpr int kPer = (2048 + kQmWaves * kWave - 1) / (kQmWaves * kWave);   // float4 per thread
         const f4* src = reinterpret_cast<const f4*>(a.cb);
         f4* dst = reinterpret_cast<f4*>(cbf);
         const int n4 = K / 2;   // K >= 2
-        f4 v[4];
+        f4 v[kPer];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < kPer; ++j) {
             const int t = threadIdx.x + j * kQmWaves * kWave;
             v[j] = t < n4 ? src[t] : f4{0, 0, 0, 0};
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < kPer; ++j) {
             const int t = threadIdx.x + j * kQmWaves * kWave;
             if (t < n4) dst[t] = v[j];
         }
