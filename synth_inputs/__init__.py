@@ -204,7 +204,7 @@ def _layer13b(seed: int, layer: int) -> List[MatrixSpec]:
 
 
 def config(index: int, n_layers: int = 40) -> Config:
-    """The five workloads (0-based), with the readings listed in the design doc."""
+    """The five workloads (0-based): shapes, value distributions and codebook sizes."""
     seed = CONFIG_SEED_BASE + index
     if index == 0:
         ms = [_spec("W", 256, 512, False, 0, 0, 0.02, 4.0 / 512.0, 20.0, seed, sid_matrix(0, 0))]
