@@ -49,6 +49,11 @@ enum {
     QAMW_FLAG_BAD_THRESHOLDS = 16 /* polar thresholds not finite, >= 0 and non-decreasing        */
 };
 
+/* Most rows a matrix may have in qamw_encode, qamw_encode_polar, qamw_decode and qamw_qgemm
+ * (QAMW_ERR_UNSUPPORTED above): the kernels address the d_out row norms through 32-bit byte
+ * ranges. */
+#define QAMW_MAX_ROWS ((1 << 30) - 1)
+
 /* Bytes per row of the packed index stream: ceil((d_in/2) * bits / 8) rounded up to 16.
  * Index k of a row occupies stream bits k*bits .. k*bits+bits-1, least significant first;
  * stream bit q is bit q%8 of byte q/8; padding bytes are zero.
@@ -116,7 +121,8 @@ int qamw_nearest(const float* d_points, int64_t n, const float* d_codebook, int3
  *   norm_i = f16(fl32(r)) round-to-nearest-even (section 3.2: 16-bit row norm);
  *   indices packed as in qamw_row_stride.
  * Arguments:
- *   d_w, w_dtype   weights (QAMW_F32 or QAMW_BF16), d_out x d_in, leading dimension ld_w >= d_in.
+ *   d_w, w_dtype   weights (QAMW_F32 or QAMW_BF16), d_out x d_in, leading dimension ld_w >= d_in;
+ *                  0 <= d_out <= QAMW_MAX_ROWS.
  *   d_scale        d_in fp32 channel scales s_j > 0, or NULL for all ones.
  *   d_sign_bits    (d_in + 31) / 32 words of sign-mask bits, or NULL for all +1.
  *   block          Hadamard block size b: a power of two in [2, 1024] dividing d_in, or 0 for

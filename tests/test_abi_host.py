@@ -86,6 +86,7 @@ def _dec(lib, **kw):
     (dict(sig_in=None, sig_out=FAKE, ws=None), WS), (dict(sig_in=None, sig_out=FAKE, ws=FAKE, ws_bytes=64), WS),
     (dict(d_in=16384 + 256, ld=16384 + 256, block=64), UNSUP), (dict(d_in=16384 + 256, ld=16640, block=256), UNSUP),
     (dict(d_in=24, ld=24, block=8), UNSUP), (dict(d_in=8, ld=8, block=8), UNSUP),
+    (dict(d_out=1 << 30), UNSUP), (dict(d_out=2**31 - 1), UNSUP),
 ])
 def test_encode_rejects(lib, kw, code):
     assert _enc(lib, **kw) == code
@@ -95,7 +96,7 @@ def test_encode_rejects(lib, kw, code):
     (dict(d_in=255), ARG), (dict(block=12), ARG), (dict(ld=255), ARG), (dict(ld=128), ARG), (dict(dt=3), ARG),
     (dict(bits=14), UNSUP), (dict(bits=0), ARG), (dict(codes=None), ARG), (dict(out=FAKE + 2), ARG),
     (dict(out=FAKE + 4, dt=q.F32), ARG), (dict(sigma=None), ARG), (dict(d_out=-3), ARG),
-    (dict(d_in=40, ld=40, block=8), UNSUP),
+    (dict(d_in=40, ld=40, block=8), UNSUP), (dict(d_out=1 << 30), UNSUP),
 ])
 def test_decode_rejects(lib, kw, code):
     assert _dec(lib, **kw) == code
@@ -150,7 +151,7 @@ def _encp(lib, **kw):
     (dict(ba=0), ARG), (dict(bp=0), ARG), (dict(ba=9, bp=1), UNSUP), (dict(ba=6, bp=7), UNSUP),
     (dict(ba=8, bp=9), ARG), (dict(thr=None), ARG), (dict(thr=FAKE + 4), ARG), (dict(d_in=255, ld=255), ARG),
     (dict(w=None), ARG), (dict(codes=FAKE + 2), ARG), (dict(sig_in=None, sig_out=FAKE, ws=None), WS),
-    (dict(d_in=24, ld=24, block=8), UNSUP),
+    (dict(d_in=24, ld=24, block=8), UNSUP), (dict(d_out=1 << 30), UNSUP),
 ])
 def test_encode_polar_rejects(lib, kw, code):
     assert _encp(lib, **kw) == code
@@ -182,6 +183,7 @@ def _qg(lib, **kw):
     (dict(block=2048), ARG), (dict(bits=0), ARG), (dict(bits=13), UNSUP), (dict(M=17), UNSUP), (dict(ld_x=128), ARG),
     (dict(ld_y=8), ARG), (dict(x=None), ARG), (dict(codes=None), ARG), (dict(y=FAKE + 2), ARG),
     (dict(x=FAKE + 1), ARG), (dict(ws=None), WS), (dict(ws=FAKE + 16), WS), (dict(ws_bytes=64), WS),
+    (dict(d_out=1 << 30, ld_y=1 << 30), UNSUP),
 ])
 def test_qgemm_rejects(lib, kw, code):
     assert _qg(lib, **kw) == code

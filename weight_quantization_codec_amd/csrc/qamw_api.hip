@@ -53,6 +53,7 @@ int encode_common(const void* d_w, qamw_dtype w_dtype, int32_t d_out, int32_t d_
                   float* d_sigma_out, uint16_t* d_norm_f16, uint8_t* d_codes, int32_t* d_status, void* d_ws,
                   size_t ws_bytes, void* stream) {
     if (d_out < 0 || (w_dtype != QAMW_F32 && w_dtype != QAMW_BF16)) return QAMW_ERR_ARG;
+    if (d_out > QAMW_MAX_ROWS) return QAMW_ERR_UNSUPPORTED;
     int L = check_shape(d_in, block);
     if (L < 0) return L;
     int rc = check_bits(bits);
@@ -206,6 +207,7 @@ int qamw_qgemm(const void* d_x, qamw_dtype x_dtype, int32_t M, int64_t ld_x, con
     if (M < 0 || d_out < 0 || (x_dtype != QAMW_F32 && x_dtype != QAMW_BF16) ||
         (y_dtype != QAMW_F32 && y_dtype != QAMW_BF16))
         return QAMW_ERR_ARG;
+    if (d_out > QAMW_MAX_ROWS) return QAMW_ERR_UNSUPPORTED;
     if (d_in <= 0 || (d_in & 1)) return QAMW_ERR_ARG;
     const int32_t b = block == 0 ? qamw_default_block(d_in) : block;
     if (b < 2 || b > 1024 || !is_pow2(b) || d_in % b) return QAMW_ERR_ARG;
@@ -310,6 +312,7 @@ int qamw_decode(const uint8_t* d_codes, const uint16_t* d_norm_f16, const float*
                 int32_t bits, const float* d_scale, const uint32_t* d_sign_bits, int32_t d_out, int32_t d_in,
                 int32_t block, void* d_out_w, qamw_dtype out_dtype, int64_t ld_out, void* stream) {
     if (d_out < 0 || (out_dtype != QAMW_F32 && out_dtype != QAMW_BF16)) return QAMW_ERR_ARG;
+    if (d_out > QAMW_MAX_ROWS) return QAMW_ERR_UNSUPPORTED;
     int L = check_shape(d_in, block);
     if (L < 0) return L;
     int rc = check_bits(bits);
