@@ -3,7 +3,8 @@
 Covers the search index (exact nearest codeword), decode cross-fed with oracle codes, encode
 (calibration, norms, indices, packed bytes), the encode -> decode round trip, Lloyd training,
 data-fault flags, and edge shapes: ragged row counts, partial wavefronts, every block size from
-2 to 1024, index widths 1..12 bits, padded leading dimensions and zero rows.
+2 to 1024, index widths 1..12 bits, padded leading dimensions, zero rows, and the widest rows
+accepted (16384 columns at b = 128 and 512, 32768 at b = 1024).
 """
 import os
 
@@ -99,6 +100,8 @@ SHAPES = [  # d_out, d_in, block, bits
     (64, 512, 64, 8), (37, 320, 64, 5), (17, 256, 2, 3), (9, 128, 16, 7), (33, 1024, 32, 11),
     (12, 2048, 256, 11), (8, 4096, 512, 12), (5, 2048, 1024, 1), (40, 4096, 128, 11),
     (3, 13824, 128, 11), (4, 11008, 256, 11), (6, 5120, 128, 7), (7, 192, 4, 9), (11, 96, 8, 6),
+    # the widest rows the kernels take: 1024 lanes of 16 columns, 512 of 32, 512 of 64
+    (2, 16384, 128, 11), (3, 16384, 512, 12), (2, 32768, 1024, 8),
 ]
 
 
