@@ -9,7 +9,7 @@ the sum of the absolute values of the terms, f16(norm_i) sum_k |c[idx].x u_2k| +
 (computed here in fp64 from scipy's Hadamard matrix).  BF16 outputs are within one BF16 ulp of the oracle's value rounded to fp32
 then BF16.
 
-Cases: one and several passes per row, split rows (reduce kernel), M = 1..16 on both kernels
+Cases: one and several passes per row, split rows (reduce kernel), rows beyond one grid, M = 1..16 on both kernels
 (vector-unit m-tiles of 1, 2 and 4 rows with a ragged last tile; matrix-core tiles of 16 weight
 rows with a ragged last tile), every index width 1..12 on both, block sizes 2..1024, fp32 and BF16 inputs and
 outputs, padded leading dimensions, zero rows, and the benchmark's 4096 x 4096 matrix whole.
@@ -126,6 +126,17 @@ def test_qgemm_every_index_width(q, orc, bits, M):
     many); 4352 columns: two passes of 2048 pairs (the second ragged), 34 chunks of 64 pairs."""
     pr = _problem(orc, 500 + bits, 12, 4096 + 256, 256, bits)
     x, y, ref = _run(q, orc, pr, M, seed=bits)
+    _check_f32(orc, x, y, ref, pr)
+
+
+@pytest.mark.parametrize("d_out,M", [(8229, 1), (8229, 3), (32851, 8)])
+def test_qgemm_tall_matrices(q, orc, d_out, M):
+    """Matrices taller than one grid covers: the vector kernels launch at most 256 workgroups of
+    16 rows and walk further rows with a stride (8229 rows: two or three rows per wavefront), the
+    matrix-core kernel at most 2048 tiles of 16 rows (32851 rows: a ragged 2054th tile)."""
+    log("qgemm tall %d rows M=%d" % (d_out, M))
+    pr = _problem(orc, 900 + M, d_out, 256, 64, 6)
+    x, y, ref = _run(q, orc, pr, M, seed=M)
     _check_f32(orc, x, y, ref, pr)
 
 
