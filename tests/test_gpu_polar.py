@@ -111,6 +111,21 @@ def _crafted_points(ba, bp, thr, seed):
     return np.concatenate(pts).astype(np.float32)
 
 
+def test_polar_index_beyond_one_grid(q, orc):
+    """More pairs than one launch covers (at most 2048 workgroups of 256 threads, then a grid
+    stride): 2048 * 256 + 12345 Gaussian pairs, ba = 5, bp = 6."""
+    _, thr = orc.rayleigh_lloyd_max(5)
+    n = 2048 * 256 + 12345
+    p = np.random.default_rng(77).standard_normal((n, 2)).astype(np.float32)
+    log("polar index %d points" % n)
+    st = torch.zeros((1,), dtype=torch.int32, device=DEV)
+    got = q.polar_index(t(p), 5, 6, t(thr.astype(np.float64)), status=st).cpu().numpy()
+    ref = orc.polar_index(p, 5, 6, thr)
+    assert int(st.item()) == 0
+    flips = check_polar(got, ref, p, 5, 6, thr)
+    log("  %d near-tie flips" % flips)
+
+
 @pytest.mark.parametrize("ba,bp", [(1, 1), (1, 2), (2, 2), (3, 3), (4, 4), (5, 6), (8, 4), (3, 9), (1, 11)],
                          ids=lambda v: str(v))
 def test_polar_index_matches_oracle(q, orc, ba, bp):
