@@ -66,9 +66,9 @@ def _probes(cb, n, seed):
     return np.concatenate(parts).astype(np.float32)
 
 
-@pytest.mark.parametrize("name", ["cfg0", "cfg1", "cfg3", "rand12", "rand1", "dup4", "grid8"])
+@pytest.mark.parametrize("name", ["cfg0", "cfg1", "cfg3", "rand12", "rand1", "dup4", "grid8", "cfg0_beyond_grid"])
 def test_nearest_matches_bruteforce(q, orc, name):
-    if name == "cfg0":
+    if name in ("cfg0", "cfg0_beyond_grid"):
         cb, bits = golden_cb("cb_cfg0_k256")[0], 8
     elif name == "cfg1":
         cb, bits = golden_cb("cb_cfg1_k2048")[0], 11
@@ -84,7 +84,8 @@ def test_nearest_matches_bruteforce(q, orc, name):
     else:  # lattice codebook: many exact ties on the cell boundaries
         g = np.arange(16) - 7.5
         cb, bits = np.stack(np.meshgrid(g, g), -1).reshape(-1, 2).astype(np.float32) * 0.25, 8
-    n = 60000 if bits >= 11 else 200000
+    # more probes than one launch covers (2048 workgroups of 256 threads, then a grid stride)
+    n = 2048 * 256 + 5000 if name == "cfg0_beyond_grid" else (60000 if bits >= 11 else 200000)
     p = _probes(cb, n, bits)
     log("nearest %s: K=%d probes=%d" % (name, len(cb), len(p)))
     cbd = t(cb)
