@@ -12,8 +12,8 @@ import numpy as np
 import pytest
 import torch
 
-from helpers import (DEV, assert_bf16_within_1ulp, assert_rel_l2, check_indices, gpu_decode, gpu_encode, log, t,
-                     unpack_rows)
+from helpers import (DEV, assert_bf16_within_1ulp, assert_rel_l2, check_indices, gpu_decode, gpu_encode, log,
+                     sign_tensor, t, unpack_rows, w_tensor)
 
 pytestmark = pytest.mark.gpu
 
@@ -189,6 +189,33 @@ def test_roundtrip_gpu_encode_gpu_decode(q, orc):
     dec = gpu_decode(q, got["codes"], got["norm"], got["sigma"], cb, 11, s, sb, 2048, 128)
     if np.array_equal(got["codes"], ref["codes"]):
         assert_bf16_within_1ulp(dec, dec_ref["bf16"])
+
+
+def test_side_stream_matches_default_stream(q):
+    """Every call runs on the caller's current stream: encode (with calibration), decode and the
+    fused product issued on a second stream give the bytes they give on the default stream."""
+    w, s, sb = rand_problem(41, 300, 2048)
+    cb = t(rand_cb(11, 11))
+    wd, sd, sbd = w_tensor(w), t(s), sign_tensor(sb)
+    idx = q.codebook_index(cb, 11)
+    x = torch.from_numpy(np.random.default_rng(5).standard_normal((8, 2048)).astype(np.float32)).to(DEV)
+
+    def run():
+        e = q.encode(wd, cb, 11, idx, scale=sd, sign_bits=sbd, block=128)
+        dec = q.decode(e["codes"], e["norm"], e["sigma"], cb, 11, 2048, scale=sd, sign_bits=sbd, block=128)
+        y = q.qgemm(x, e["codes"], e["norm"], e["sigma"], cb, 11, scale=sd, sign_bits=sbd, block=128)
+        return [e["codes"], e["norm"], e["sigma"], dec.view(torch.int16), y]
+
+    ref = [v.cpu() for v in run()]
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        got = run()
+    side.synchronize()
+    got = [v.cpu() for v in got]
+    for a, b in zip(ref, got):
+        assert torch.equal(a, b)
 
 
 def test_encode_is_deterministic(q):
