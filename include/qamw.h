@@ -154,7 +154,7 @@ int qamw_encode(const void* d_w, qamw_dtype w_dtype, int32_t d_out, int32_t d_in
  * computed in double and rounded to fp32 (QAMW_F32) or to fp32 then BF16 with
  * round-to-nearest-even (QAMW_BF16).  A zero norm gives a row of +0.
  * Arguments mirror qamw_encode; d_out_w is d_out x d_in with leading dimension ld_out >= d_in
- * (ld_out even).  Same block / d_in limits as qamw_encode. */
+ * (ld_out even).  Same block / d_in / d_out limits as qamw_encode. */
 int qamw_decode(const uint8_t* d_codes, const uint16_t* d_norm_f16, const float* d_sigma,
                 const float* d_codebook, int32_t bits, const float* d_scale,
                 const uint32_t* d_sign_bits, int32_t d_out, int32_t d_in, int32_t block,
@@ -175,7 +175,8 @@ int qamw_decode(const uint8_t* d_codes, const uint16_t* d_norm_f16, const float*
  * Arguments:
  *   d_x, x_dtype, M, ld_x   M x d_in activations (QAMW_F32 or QAMW_BF16), row m at d_x + m ld_x.
  *                           1 <= M <= 16 (QAMW_ERR_UNSUPPORTED above; M = 0 is a no-op).
- *   d_codes ... block       as qamw_decode (any block size 2..1024 dividing d_in; bits <= 12).
+ *   d_codes ... block       as qamw_decode (any block size 2..1024 dividing d_in; bits <= 12;
+ *                           d_out <= QAMW_MAX_ROWS).
  *   d_y, y_dtype, ld_y      M x d_out outputs, y[m][i] at d_y + m ld_y (ld_y >= d_out); BF16 is the
  *                           fp32 result rounded to nearest even.
  *   d_ws, ws_bytes          at least qamw_qgemm_workspace(M, d_out, d_in) bytes, 256-byte aligned. */
