@@ -29,36 +29,6 @@ namespace qamw {
 
 namespace {
 
-constexpr int kPolyMax = 48;
-
-// Convex polygon clipped by a.x*px + a.y*py <= b (Sutherland-Hodgman, double precision).
-__device__ int clip_poly(double* vx, double* vy, int n, double ax, double ay, double b, double* tx, double* ty) {
-    int m = 0;
-    const double tol = 1e-12 * (fabs(b) + 1.0);
-    for (int i = 0; i < n; ++i) {
-        const int i2 = (i + 1 == n) ? 0 : i + 1;
-        const double s1 = ax * vx[i] + ay * vy[i] - b;
-        const double s2 = ax * vx[i2] + ay * vy[i2] - b;
-        const bool in1 = s1 <= tol, in2 = s2 <= tol;
-        if (in1 && m < kPolyMax) {
-            tx[m] = vx[i];
-            ty[m] = vy[i];
-            ++m;
-        }
-        if (in1 != in2 && m < kPolyMax) {
-            const double t = s1 / (s1 - s2);
-            tx[m] = vx[i] + t * (vx[i2] - vx[i]);
-            ty[m] = vy[i] + t * (vy[i2] - vy[i]);
-            ++m;
-        }
-    }
-    for (int i = 0; i < m; ++i) {
-        vx[i] = tx[i];
-        vy[i] = ty[i];
-    }
-    return m;
-}
-
 struct CellBox {
     double x0, x1, y0, y1;
 };
@@ -88,23 +58,56 @@ __device__ __forceinline__ double mind2(const CellBox& q, double px, double py) 
 }
 
 // Is codeword j a candidate of the (non-empty) cell box q?  pre[] holds the prefiltered set.
-__device__ bool voronoi_meets(const CellBox& q, const float2* __restrict__ cb, int j, const uint16_t* pre, int npre) {
-    double vx[kPolyMax], vy[kPolyMax], tx[kPolyMax], ty[kPolyMax];
-    vx[0] = q.x0; vy[0] = q.y0;
-    vx[1] = q.x1; vy[1] = q.y0;
-    vx[2] = q.x1; vy[2] = q.y1;
-    vx[3] = q.x0; vy[3] = q.y1;
+// Whether the Voronoi region of codeword j, widened by a margin, meets the cell box q: the box is
+// clipped (Sutherland-Hodgman, double precision) by the half-plane |p - c_j|^2 - |p - c_k|^2 <= m of
+// every other prefiltered codeword k, and the region meets the cell when something is left.  The
+// polygon lives in the lanes of one wavefront, vertex l in lane l: a clip tests each vertex and the
+// next one, counts the vertices each lane emits (the vertex if inside, the crossing point if the
+// edge crosses the line), places them by a ballot prefix count and moves them through the
+// wavefront's LDS buffer.  Called by a whole wavefront with a uniform j.  A polygon that would need
+// more than 64 vertices counts as meeting the cell (an extra list entry costs search time only).
+__device__ bool voronoi_meets_wave(const CellBox& q, const float2* __restrict__ cb, int j, const uint16_t* pre,
+                                   int npre, double2* wbuf, int lane) {
+    double px = lane == 1 || lane == 2 ? q.x1 : q.x0;
+    double py = lane >= 2 ? q.y1 : q.y0;
     int n = 4;
     const double cjx = cb[j].x, cjy = cb[j].y;
     const double mj = maxd2(q, cjx, cjy);
     const double nj = cjx * cjx + cjy * cjy;
-    for (int t = 0; t < npre && n > 0; ++t) {
+    for (int t = 0; t < npre; ++t) {
         const int k = pre[t];
         if (k == j) continue;
         const double ckx = cb[k].x, cky = cb[k].y;
         const double m = 1e-6 * (mj + maxd2(q, ckx, cky));
         // |p-cj|^2 - |p-ck|^2 <= m   <=>   2 (ck - cj).p <= |ck|^2 - |cj|^2 + m
-        n = clip_poly(vx, vy, n, 2.0 * (ckx - cjx), 2.0 * (cky - cjy), (ckx * ckx + cky * cky) - nj + m, tx, ty);
+        const double ax = 2.0 * (ckx - cjx), ay = 2.0 * (cky - cjy), b = (ckx * ckx + cky * cky) - nj + m;
+        const double tol = 1e-12 * (fabs(b) + 1.0);
+        const int nx = lane + 1 == n ? 0 : lane + 1;
+        const double px2 = __shfl(px, nx, kWave), py2 = __shfl(py, nx, kWave);
+        const double s1 = ax * px + ay * py - b;
+        const double s2 = ax * px2 + ay * py2 - b;
+        const bool live = lane < n;
+        const bool in1 = live && s1 <= tol;
+        const bool cross = live && (s1 <= tol) != (s2 <= tol);
+        const uint64_t ba = __ballot(in1), bc = __ballot(cross);
+        const int below = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(ba >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ba, 0u)) +
+                          (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bc >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bc, 0u));
+        const int m2 = __popcll(ba) + __popcll(bc);
+        if (m2 > kWave) return true;
+        if (in1) wbuf[below] = make_double2(px, py);
+        if (cross) {
+            const double tt = s1 / (s1 - s2);
+            wbuf[below + (in1 ? 1 : 0)] = make_double2(px + tt * (px2 - px), py + tt * (py2 - py));
+        }
+        wave_lds_sync();
+        n = m2;
+        if (lane < n) {
+            const double2 v = wbuf[lane];
+            px = v.x;
+            py = v.y;
+        }
+        wave_lds_sync();   // read before the next clip overwrites the buffer
+        if (n == 0) return false;
     }
     return n > 0;
 }
@@ -166,11 +169,22 @@ __global__ __launch_bounds__(1024) void k_ix_grid(const float* __restrict__ cb, 
 
 // 2./4. Candidate lists: one workgroup per cell.  pass 0 counts, pass 1 writes the list in
 // increasing codeword order at the cell's offset.
-__global__ __launch_bounds__(256) void k_ix_cells(const float* __restrict__ cb, int K, char* __restrict__ index,
+// LDS of k_ix_cells: the codebook (K float2), the prefiltered list (K uint16), one 64-vertex buffer
+// per wavefront (16-byte aligned), and a K-bit set of the codewords whose regions meet the cell.
+constexpr int kIxCellsThreads = 256;
+__host__ __device__ inline size_t ix_cells_wbuf_off(int K) { return ((size_t)K * 10 + 15) / 16 * 16; }
+__host__ __device__ inline size_t ix_cells_bits_off(int K) {
+    return ix_cells_wbuf_off(K) + (size_t)(kIxCellsThreads / kWave) * kWave * 16;
+}
+__host__ __device__ inline size_t ix_cells_lds(int K) { return ix_cells_bits_off(K) + (size_t)(K + 31) / 32 * 4; }
+
+__global__ __launch_bounds__(kIxCellsThreads) void k_ix_cells(const float* __restrict__ cb, int K, char* __restrict__ index,
                                                   int pass) {
     extern __shared__ __align__(16) char smem[];
     float2* scb = reinterpret_cast<float2*>(smem);
     uint16_t* pre = reinterpret_cast<uint16_t*>(smem + (size_t)K * sizeof(float2));
+    double2* wbuf = reinterpret_cast<double2*>(smem + ix_cells_wbuf_off(K)) + (threadIdx.x / kWave) * kWave;
+    uint32_t* meets = reinterpret_cast<uint32_t*>(smem + ix_cells_bits_off(K));   // K bits
     __shared__ double redU[256];
     __shared__ int npre, wbase;
     __shared__ int scan[256];
@@ -181,6 +195,7 @@ __global__ __launch_bounds__(256) void k_ix_cells(const float* __restrict__ cb, 
     const int cell = blockIdx.x, tid = threadIdx.x;
     if (pass && reinterpret_cast<const uint8_t*>(index + kIndexOvfOff)[cell]) return;   // uniform per block
     for (int j = tid; j < K; j += blockDim.x) scb[j] = reinterpret_cast<const float2*>(cb)[j];
+    for (int w = tid; w < (K + 31) / 32; w += blockDim.x) meets[w] = 0u;
     if (tid == 0) {
         npre = 0;
         wbase = 0;
@@ -207,13 +222,23 @@ __global__ __launch_bounds__(256) void k_ix_cells(const float* __restrict__ cb, 
     }
     __syncthreads();
     const int np = npre;
+    // the prefiltered codewords whose regions meet the cell, one per wavefront at a time
+    {
+        const int lane = tid & (kWave - 1);
+        const int nw = blockDim.x / kWave;
+        for (int i = __builtin_amdgcn_readfirstlane(tid / kWave); i < np; i += nw) {
+            const int j = pre[i];
+            if (voronoi_meets_wave(q, scb, j, pre, np, wbuf, lane) && lane == 0) atomicOr(&meets[j >> 5], 1u << (j & 31));
+        }
+    }
+    __syncthreads();
     uint32_t count = 0;
     const uint32_t base = pass ? offs[cell] : 0u;
     // candidates in increasing j: chunks of 256 codewords, ordered by a workgroup prefix sum
     for (int j0 = 0; j0 < K; j0 += blockDim.x) {
         const int j = j0 + tid;
         int is = 0;
-        if (!empty && j < K && mind2(q, scb[j].x, scb[j].y) <= lim) is = voronoi_meets(q, scb, j, pre, np) ? 1 : 0;
+        if (!empty && j < K) is = (int)((meets[j >> 5] >> (j & 31)) & 1u);
         scan[tid] = is;
         __syncthreads();
         for (int s = 1; s < 256; s <<= 1) {
@@ -324,11 +349,11 @@ hipError_t launch_index_build(const float* cb, int bits, void* index, hipStream_
     const int G = index_grid_size(bits);
     char* ix = reinterpret_cast<char*>(index);
     hipLaunchKernelGGL(k_ix_grid, dim3(1), dim3(1024), 0, st, cb, K, G, kIndexFine, bits, ix);
-    const size_t smem = (size_t)K * sizeof(float2) + (size_t)K * sizeof(uint16_t);
+    const size_t smem = ix_cells_lds(K);
     allow_lds(k_ix_cells, smem);
-    hipLaunchKernelGGL(k_ix_cells, dim3(G * G), dim3(256), smem, st, cb, K, ix, 0);
+    hipLaunchKernelGGL(k_ix_cells, dim3(G * G), dim3(kIxCellsThreads), smem, st, cb, K, ix, 0);
     hipLaunchKernelGGL(k_ix_scan, dim3(1), dim3(64), 0, st, ix, index_lds_entries(K));
-    hipLaunchKernelGGL(k_ix_cells, dim3(G * G), dim3(256), smem, st, cb, K, ix, 1);
+    hipLaunchKernelGGL(k_ix_cells, dim3(G * G), dim3(kIxCellsThreads), smem, st, cb, K, ix, 1);
     hipLaunchKernelGGL(k_ix_order, dim3((K + 255) / 256), dim3(256), 0, st, cb, K, ix);
     hipLaunchKernelGGL(k_ix_image, dim3(64), dim3(256), 0, st, cb, K, ix);
     return hipGetLastError();
