@@ -60,56 +60,78 @@ __device__ __forceinline__ double mind2(const CellBox& q, double px, double py) 
 // Is codeword j a candidate of the (non-empty) cell box q?  pre[] holds the prefiltered set.
 // Whether the Voronoi region of codeword j, widened by a margin, meets the cell box q: the box is
 // clipped (Sutherland-Hodgman, double precision) by the half-plane |p - c_j|^2 - |p - c_k|^2 <= m of
-// every other prefiltered codeword k, and the region meets the cell when something is left.  The
-// polygon lives in the lanes of one wavefront, vertex l in lane l: a clip tests each vertex and the
-// next one, counts the vertices each lane emits (the vertex if inside, the crossing point if the
-// edge crosses the line), places them by a ballot prefix count and moves them through the
-// wavefront's LDS buffer.  Called by a whole wavefront with a uniform j.  A polygon that would need
-// more than 64 vertices counts as meeting the cell (an extra list entry costs search time only).
-__device__ bool voronoi_meets_wave(const CellBox& q, const float2* __restrict__ cb, int j, const uint16_t* pre,
+// every other prefiltered codeword k, and the region meets the cell when something is left.  Each
+// half of a wavefront (32 lanes) tests its own candidate j (j < 0: none), its polygon's vertex l in
+// lane l of the half: a clip tests each vertex and the next one, counts the vertices each lane
+// emits (the vertex if inside, the crossing point if the edge crosses the line), places them by a
+// ballot prefix count within the half and moves them through the half's part of the wavefront's
+// LDS buffer.  The loop is uniform over the wavefront: a half that has its answer clips nothing
+// further.  A polygon that would need more than 32 vertices counts as meeting the cell (an extra
+// list entry costs search time only).  Returns the answer of the lane's half.
+__device__ bool voronoi_meets_half(const CellBox& q, const float2* __restrict__ cb, int j, const uint16_t* pre,
                                    int npre, double2* wbuf, int lane) {
-    double px = lane == 1 || lane == 2 ? q.x1 : q.x0;
-    double py = lane >= 2 ? q.y1 : q.y0;
+    constexpr int kHalf = kWave / 2;
+    const int h = lane / kHalf, gl = lane % kHalf;
+    const uint64_t hmask = h ? 0xFFFFFFFF00000000ull : 0x00000000FFFFFFFFull;
+    double2* hb = wbuf + h * kHalf;
+    double px = gl == 1 || gl == 2 ? q.x1 : q.x0;
+    double py = gl >= 2 ? q.y1 : q.y0;
     int n = 4;
-    const double cjx = cb[j].x, cjy = cb[j].y;
+    bool done = j < 0, res = false;   // uniform within each half
+    const int jj = j < 0 ? 0 : j;
+    const double cjx = cb[jj].x, cjy = cb[jj].y;
     const double mj = maxd2(q, cjx, cjy);
     const double nj = cjx * cjx + cjy * cjy;
     for (int t = 0; t < npre; ++t) {
+        if (__ballot(!done) == 0) break;   // both halves have their answers
         const int k = pre[t];
-        if (k == j) continue;
         const double ckx = cb[k].x, cky = cb[k].y;
         const double m = 1e-6 * (mj + maxd2(q, ckx, cky));
         // |p-cj|^2 - |p-ck|^2 <= m   <=>   2 (ck - cj).p <= |ck|^2 - |cj|^2 + m
-        const double ax = 2.0 * (ckx - cjx), ay = 2.0 * (cky - cjy), b = (ckx * ckx + cky * cky) - nj + m;
+        double ax = 2.0 * (ckx - cjx), ay = 2.0 * (cky - cjy), b = (ckx * ckx + cky * cky) - nj + m;
+        if (done || k == jj) {   // no clip for this half: every vertex stays
+            ax = 0.0;
+            ay = 0.0;
+            b = 1.0;
+        }
         const double tol = 1e-12 * (fabs(b) + 1.0);
-        const int nx = lane + 1 == n ? 0 : lane + 1;
-        const double px2 = __shfl(px, nx, kWave), py2 = __shfl(py, nx, kWave);
+        const int nx = gl + 1 == n ? 0 : gl + 1;
+        const double px2 = __shfl(px, h * kHalf + nx, kWave), py2 = __shfl(py, h * kHalf + nx, kWave);
         const double s1 = ax * px + ay * py - b;
         const double s2 = ax * px2 + ay * py2 - b;
-        const bool live = lane < n;
+        const bool live = gl < n;
         const bool in1 = live && s1 <= tol;
         const bool cross = live && (s1 <= tol) != (s2 <= tol);
-        const uint64_t ba = __ballot(in1), bc = __ballot(cross);
+        const uint64_t ba = __ballot(in1) & hmask, bc = __ballot(cross) & hmask;
         const int below = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(ba >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ba, 0u)) +
                           (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bc >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bc, 0u));
         const int m2 = __popcll(ba) + __popcll(bc);
-        if (m2 > kWave) return true;
-        if (in1) wbuf[below] = make_double2(px, py);
-        if (cross) {
+        if (!done && m2 > kHalf) {
+            done = true;
+            res = true;
+        }
+        if (!done && in1) hb[below] = make_double2(px, py);
+        if (!done && cross) {
             const double tt = s1 / (s1 - s2);
-            wbuf[below + (in1 ? 1 : 0)] = make_double2(px + tt * (px2 - px), py + tt * (py2 - py));
+            hb[below + (in1 ? 1 : 0)] = make_double2(px + tt * (px2 - px), py + tt * (py2 - py));
         }
         wave_lds_sync();
-        n = m2;
-        if (lane < n) {
-            const double2 v = wbuf[lane];
-            px = v.x;
-            py = v.y;
+        if (!done) {
+            n = m2;
+            if (gl < n) {
+                const double2 v = hb[gl];
+                px = v.x;
+                py = v.y;
+            }
         }
         wave_lds_sync();   // read before the next clip overwrites the buffer
-        if (n == 0) return false;
+        if (!done && n == 0) {
+            done = true;
+            res = false;
+        }
     }
-    return n > 0;
+    if (!done) res = n > 0;
+    return res;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -170,7 +192,8 @@ __global__ __launch_bounds__(1024) void k_ix_grid(const float* __restrict__ cb, 
 // 2./4. Candidate lists: one workgroup per cell.  pass 0 counts, pass 1 writes the list in
 // increasing codeword order at the cell's offset.
 // LDS of k_ix_cells: the codebook (K float2), the prefiltered list (K uint16), one 64-vertex buffer
-// per wavefront (16-byte aligned), and a K-bit set of the codewords whose regions meet the cell.
+// per wavefront (32 vertices per half, 16-byte aligned), and a K-bit set of the codewords whose
+// regions meet the cell.
 constexpr int kIxCellsThreads = 256;
 __host__ __device__ inline size_t ix_cells_wbuf_off(int K) { return ((size_t)K * 10 + 15) / 16 * 16; }
 __host__ __device__ inline size_t ix_cells_bits_off(int K) {
@@ -222,13 +245,16 @@ __global__ __launch_bounds__(kIxCellsThreads) void k_ix_cells(const float* __res
     }
     __syncthreads();
     const int np = npre;
-    // the prefiltered codewords whose regions meet the cell, one per wavefront at a time
+    // the prefiltered codewords whose regions meet the cell
     {
         const int lane = tid & (kWave - 1);
         const int nw = blockDim.x / kWave;
-        for (int i = __builtin_amdgcn_readfirstlane(tid / kWave); i < np; i += nw) {
-            const int j = pre[i];
-            if (voronoi_meets_wave(q, scb, j, pre, np, wbuf, lane) && lane == 0) atomicOr(&meets[j >> 5], 1u << (j & 31));
+        // two candidates per wavefront at a time, one per half
+        for (int i0 = 2 * __builtin_amdgcn_readfirstlane(tid / kWave); i0 < np; i0 += 2 * nw) {
+            const int i = i0 + lane / (kWave / 2);
+            const int j = i < np ? pre[i] : -1;
+            const bool hit = voronoi_meets_half(q, scb, j, pre, np, wbuf, lane);
+            if (hit && j >= 0 && lane % (kWave / 2) == 0) atomicOr(&meets[j >> 5], 1u << (j & 31));
         }
     }
     __syncthreads();
