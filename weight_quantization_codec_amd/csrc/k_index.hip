@@ -29,6 +29,8 @@ namespace qamw {
 
 namespace {
 
+constexpr int kIxGroup = 16;   // lanes per candidate polygon (at most that many vertices)
+
 struct CellBox {
     double x0, x1, y0, y1;
 };
@@ -61,35 +63,35 @@ __device__ __forceinline__ double mind2(const CellBox& q, double px, double py) 
 // Whether the Voronoi region of codeword j, widened by a margin, meets the cell box q: the box is
 // clipped (Sutherland-Hodgman, double precision) by the half-plane |p - c_j|^2 - |p - c_k|^2 <= m of
 // every other prefiltered codeword k, and the region meets the cell when something is left.  Each
-// half of a wavefront (32 lanes) tests its own candidate j (j < 0: none), its polygon's vertex l in
-// lane l of the half: a clip tests each vertex and the next one, counts the vertices each lane
-// emits (the vertex if inside, the crossing point if the edge crosses the line), places them by a
-// ballot prefix count within the half and moves them through the half's part of the wavefront's
-// LDS buffer.  The loop is uniform over the wavefront: a half that has its answer clips nothing
-// further.  A polygon that would need more than 32 vertices counts as meeting the cell (an extra
-// list entry costs search time only).  Returns the answer of the lane's half.
-__device__ bool voronoi_meets_half(const CellBox& q, const float2* __restrict__ cb, int j, const uint16_t* pre,
+// group of kIxGroup lanes tests its own candidate j (j < 0: none), its polygon's vertex l in lane l
+// of the group: a clip tests each vertex and the next one, counts the vertices each lane emits (the
+// vertex if inside, the crossing point if the edge crosses the line), places them by a ballot
+// prefix count within the group and moves them through the group's part of the wavefront's LDS
+// buffer.  The loop is uniform over the wavefront: a group that has its answer clips nothing
+// further.  A polygon that would need more than kIxGroup vertices counts as meeting the cell (an
+// extra list entry costs search time only).  Returns the answer of the lane's group.
+__device__ bool voronoi_meets_group(const CellBox& q, const float2* __restrict__ cb, int j, const uint16_t* pre,
                                    int npre, double2* wbuf, int lane) {
-    constexpr int kHalf = kWave / 2;
+    constexpr int kHalf = kIxGroup;   // lanes of a group
     const int h = lane / kHalf, gl = lane % kHalf;
-    const uint64_t hmask = h ? 0xFFFFFFFF00000000ull : 0x00000000FFFFFFFFull;
+    const uint64_t hmask = (~0ull >> (kWave - kHalf)) << (h * kHalf);
     double2* hb = wbuf + h * kHalf;
     double px = gl == 1 || gl == 2 ? q.x1 : q.x0;
     double py = gl >= 2 ? q.y1 : q.y0;
     int n = 4;
-    bool done = j < 0, res = false;   // uniform within each half
+    bool done = j < 0, res = false;   // uniform within each group
     const int jj = j < 0 ? 0 : j;
     const double cjx = cb[jj].x, cjy = cb[jj].y;
     const double mj = maxd2(q, cjx, cjy);
     const double nj = cjx * cjx + cjy * cjy;
     for (int t = 0; t < npre; ++t) {
-        if (__ballot(!done) == 0) break;   // both halves have their answers
+        if (__ballot(!done) == 0) break;   // every group has its answer
         const int k = pre[t];
         const double ckx = cb[k].x, cky = cb[k].y;
         const double m = 1e-6 * (mj + maxd2(q, ckx, cky));
         // |p-cj|^2 - |p-ck|^2 <= m   <=>   2 (ck - cj).p <= |ck|^2 - |cj|^2 + m
         double ax = 2.0 * (ckx - cjx), ay = 2.0 * (cky - cjy), b = (ckx * ckx + cky * cky) - nj + m;
-        if (done || k == jj) {   // no clip for this half: every vertex stays
+        if (done || k == jj) {   // no clip for this group: every vertex stays
             ax = 0.0;
             ay = 0.0;
             b = 1.0;
@@ -192,7 +194,7 @@ __global__ __launch_bounds__(1024) void k_ix_grid(const float* __restrict__ cb, 
 // 2./4. Candidate lists: one workgroup per cell.  pass 0 counts, pass 1 writes the list in
 // increasing codeword order at the cell's offset.
 // LDS of k_ix_cells: the codebook (K float2), the prefiltered list (K uint16), one 64-vertex buffer
-// per wavefront (32 vertices per half, 16-byte aligned), and a K-bit set of the codewords whose
+// per wavefront (kIxGroup vertices per lane group, 16-byte aligned), and a K-bit set of the codewords whose
 // regions meet the cell.
 constexpr int kIxCellsThreads = 256;
 __host__ __device__ inline size_t ix_cells_wbuf_off(int K) { return ((size_t)K * 10 + 15) / 16 * 16; }
@@ -249,12 +251,13 @@ __global__ __launch_bounds__(kIxCellsThreads) void k_ix_cells(const float* __res
     {
         const int lane = tid & (kWave - 1);
         const int nw = blockDim.x / kWave;
-        // two candidates per wavefront at a time, one per half
-        for (int i0 = 2 * __builtin_amdgcn_readfirstlane(tid / kWave); i0 < np; i0 += 2 * nw) {
-            const int i = i0 + lane / (kWave / 2);
+        // kWave / kIxGroup candidates per wavefront at a time, one per lane group
+        constexpr int kPer = kWave / kIxGroup;
+        for (int i0 = kPer * __builtin_amdgcn_readfirstlane(tid / kWave); i0 < np; i0 += kPer * nw) {
+            const int i = i0 + lane / kIxGroup;
             const int j = i < np ? pre[i] : -1;
-            const bool hit = voronoi_meets_half(q, scb, j, pre, np, wbuf, lane);
-            if (hit && j >= 0 && lane % (kWave / 2) == 0) atomicOr(&meets[j >> 5], 1u << (j & 31));
+            const bool hit = voronoi_meets_group(q, scb, j, pre, np, wbuf, lane);
+            if (hit && j >= 0 && lane % kIxGroup == 0) atomicOr(&meets[j >> 5], 1u << (j & 31));
         }
     }
     __syncthreads();
