@@ -194,8 +194,8 @@ __global__ __launch_bounds__(1024) void k_ix_grid(const float* __restrict__ cb, 
 // 2./4. Candidate lists: one workgroup per cell.  pass 0 counts, pass 1 writes the list in
 // increasing codeword order at the cell's offset.
 // LDS of k_ix_cells: the codebook (K float2), the prefiltered list (K uint16), one 64-vertex buffer
-// per wavefront (kIxGroup vertices per lane group, 16-byte aligned), and a K-bit set of the codewords whose
-// regions meet the cell.
+// per wavefront (kIxGroup vertices per lane group, 16-byte aligned), and a K-bit set of the
+// codewords whose regions meet the cell.
 constexpr int kIxCellsThreads = 256;
 __host__ __device__ inline size_t ix_cells_wbuf_off(int K) { return ((size_t)K * 10 + 15) / 16 * 16; }
 __host__ __device__ inline size_t ix_cells_bits_off(int K) {
