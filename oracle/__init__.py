@@ -44,6 +44,8 @@ def _bind(lib):
         "oracle_f16_from_f32": ([f32], u16),
         "oracle_f32_from_f16": ([u16], f32),
         "oracle_bf16_from_f32": ([f32], u16),
+        "oracle_splitmix64": ([ctypes.c_uint64, i64, vp], None),
+        "oracle_sign_mask": ([ctypes.c_uint64, i32, vp], None),
         "oracle_hadamard": ([i32, vp], None),
         "oracle_default_block": ([i32], i32),
         "oracle_bpw": ([i32, i32], dbl),
@@ -121,6 +123,24 @@ class Oracle:
         return self.lib.oracle_row_stride(d_in, bits)
 
     # -- arrays --------------------------------------------------------------
+    def splitmix64(self, seed: int, n: int) -> np.ndarray:
+        """The first n outputs of splitmix64 started at `seed` (uint64)."""
+        out = np.empty((max(n, 1),), dtype=np.uint64)
+        self.lib.oracle_splitmix64(seed, n, self._p(out))
+        return out[:n]
+
+    def sign_mask(self, seed: int, d_in: int) -> np.ndarray:
+        """Sign-mask bits of a seed (section 3.3): bit j % 32 of word j / 32 set when eps_j = -1."""
+        out = np.zeros((max((d_in + 31) // 32, 1),), dtype=np.uint32)
+        self.lib.oracle_sign_mask(seed, d_in, self._p(out))
+        return out[: (d_in + 31) // 32]
+
+    @staticmethod
+    def signs(bits: np.ndarray, d_in: int) -> np.ndarray:
+        """+1 / -1 (float64) of mask bits."""
+        j = np.arange(d_in)
+        return np.where((bits[j >> 5] >> (j & 31).astype(np.uint32)) & 1, -1.0, 1.0)
+
     def hadamard(self, b: int) -> np.ndarray:
         H = np.empty((b, b), dtype=np.float64)
         self.lib.oracle_hadamard(b, self._p(H))

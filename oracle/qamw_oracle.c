@@ -15,8 +15,11 @@
  *
  * Readings where the paper is silent (each is also listed in the design
  * notes of the repository):
- *   R1 sign mask: given by the caller as bits, eps_j = -1 where bit j is set;
- *      rotation y = blockdiag(H_b) (eps . u), H_b in Sylvester order.
+ *   R1 sign mask: the functions below take it as bits, eps_j = -1 where bit j is
+ *      set; the bits are drawn from a 64-bit seed by oracle_sign_mask (section
+ *      3.3 only calls the mask deterministic): eps_j = -1 when the top bit of
+ *      the (j+1)-th output of the splitmix64 generator started at the seed is
+ *      set.  Rotation y = blockdiag(H_b) (eps . u), H_b in Sylvester order.
  *   R2 sigma_k: mean |z_k| over the non-zero, finite rows among those passed
  *      (the caller passes the first min(d_out, 1024) rows), in double, then
  *      divided by sqrt(pi/2) and rounded to float; fallback 1/sqrt(d_in).
@@ -170,6 +173,38 @@ size_t oracle_row_stride(int32_t d_in, int32_t bits)
 {
     size_t used = ((size_t)(d_in / 2) * (size_t)bits + 7) / 8;
     return (used + 15) / 16 * 16;
+}
+
+/* ------------------------------------------------------------------------
+ * The sign mask (section 3.3, reading R1).  splitmix64 (Steele, Lea and
+ * Flood, "Fast splittable pseudorandom number generators", OOPSLA 2014, with
+ * the constants of Vigna's reference code): the state advances by the golden
+ * gamma 0x9E3779B97F4A7C15 and each output is the new state passed through the
+ * finalizer below, all modulo 2^64.
+ * ------------------------------------------------------------------------ */
+void oracle_splitmix64(uint64_t seed, int64_t n, uint64_t* out)
+{
+    uint64_t state = seed;
+    for (int64_t t = 0; t < n; ++t) {
+        state += 0x9E3779B97F4A7C15ULL;
+        uint64_t z = state;
+        z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+        z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+        out[t] = z ^ (z >> 31);
+    }
+}
+
+/* Bit j % 32 of word j / 32 is set when eps_j = -1, i.e. when output j + 1 of
+ * the generator started at `seed` has its top bit set (0 <= j < d_in). */
+void oracle_sign_mask(uint64_t seed, int32_t d_in, uint32_t* bits)
+{
+    int32_t nw = (d_in + 31) / 32;
+    for (int32_t w = 0; w < nw; ++w) bits[w] = 0;
+    uint64_t* z = (uint64_t*)malloc(sizeof(uint64_t) * (size_t)(d_in > 0 ? d_in : 1));
+    oracle_splitmix64(seed, d_in, z);
+    for (int32_t j = 0; j < d_in; ++j)
+        if (z[j] >> 63) bits[j >> 5] |= 1u << (j & 31);
+    free(z);
 }
 
 static double eps_of(const uint32_t* sign_bits, int j)

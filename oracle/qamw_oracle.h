@@ -32,6 +32,9 @@ uint16_t oracle_f16_from_f32(float f);
 float oracle_f32_from_f16(uint16_t h);
 uint16_t oracle_bf16_from_f32(float f);
 
+/* section 3.3, the deterministic sign mask (reading R1): splitmix64 outputs and the mask bits */
+void oracle_splitmix64(uint64_t seed, int64_t n, uint64_t* out);
+void oracle_sign_mask(uint64_t seed, int32_t d_in, uint32_t* bits);
 void oracle_hadamard(int32_t b, double* H);
 int32_t oracle_default_block(int32_t d_in);
 double oracle_bpw(int32_t d_in, int32_t bits);

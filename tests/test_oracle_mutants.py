@@ -11,6 +11,11 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "qamw_oracle.c")
 
 MUTANTS = [
+    # sign mask (section 3.3, reading R1): caught by test_oracle_sign.py
+    ("splitmix64 first shift", "z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;", "z = (z ^ (z >> 31)) * 0xBF58476D1CE4E5B9ULL;",
+     "test_oracle_sign.py"),
+    ("sign from output j instead of j + 1", "oracle_splitmix64(seed, d_in, z);",
+     "z[0] = 0; oracle_splitmix64(seed, d_in - 1, z + 1);", "test_oracle_sign.py"),
     ("sign mask dropped", "a[j] = eps_of(sign_bits, j) * (a[j] / r);", "a[j] = (a[j] / r);"),
     ("Hadamard sign from i|k", "(__builtin_popcount(i & k) & 1) ? -scale : scale",
      "(__builtin_popcount(i | k) & 1) ? -scale : scale"),

@@ -374,7 +374,7 @@ def test_parseval_identity(orc, synth):
     m = c.matrices[0]
     w = m.weights(0, 64)
     s = m.channel_scale()
-    sbits = synth.sign_bits(m.d_in)
+    sbits = orc.sign_mask(0x51414D57, m.d_in)
     pts = synth.points(c.seed, 4, 1 << 12)
     cb, _, _ = orc.lloyd(pts, 8, 5)
     sigma, _ = orc.calibrate(w, s, sbits, c.block)
@@ -393,7 +393,7 @@ def test_reconstruction_improves_with_codebook_size(orc, synth):
     m = c.matrices[0]
     w = m.weights(0, 48)
     s = m.channel_scale()
-    sbits = synth.sign_bits(m.d_in)
+    sbits = orc.sign_mask(0x51414D57, m.d_in)
     pts = synth.points(c.seed, 4, 1 << 14)
     errs, dist = [], []
     for bits in (4, 6, 8):
