@@ -102,11 +102,10 @@ def main():
     # ---------------------------------------------------------------- inputs (host -> HBM, untimed)
     w_host = m.weights()
     s_host = m.channel_scale()
-    sb_host = synth.sign_bits(d_in)
+    sign = q.DEFAULT_SIGN_SEED   # seed of the rotation's sign mask
     pts_host = synth.points(cfg.seed, synth.SID_POINTS, cfg.n_points)
     w0 = torch.from_numpy(w_host.view(np.int16)).view(torch.bfloat16).to(dev)
     scale = torch.from_numpy(s_host).to(dev)
-    sign = torch.from_numpy(sb_host.view(np.int32)).to(dev)
     pts = torch.from_numpy(pts_host).to(dev)
 
     # plain copy of known size: calibrates the FETCH_SIZE / WRITE_SIZE counters in profiled runs
@@ -145,11 +144,11 @@ def main():
     status = torch.zeros((1,), dtype=torch.int32, device=dev)
 
     def enc(bset, sigma=None):
-        q.encode(bset["w"], cb, bits, index, scale=scale, sign_bits=sign, block=block, sigma=sigma, status=status,
+        q.encode(bset["w"], cb, bits, index, scale=scale, sign_seed=sign, block=block, sigma=sigma, status=status,
                  workspace=ws, out={"codes": bset["codes"], "norm": bset["norm"], "sigma": bset["sigma"]})
 
     def dec(bset):
-        q.decode(bset["codes"], bset["norm"], bset["sigma"], cb, bits, d_in, scale=scale, sign_bits=sign,
+        q.decode(bset["codes"], bset["norm"], bset["sigma"], cb, bits, d_in, scale=scale, sign_seed=sign,
                  block=block, out=bset["out"])
 
     def step(i):
@@ -251,6 +250,7 @@ def main():
         cb_h = cb.cpu().numpy()
         threads = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
         t0 = time.perf_counter()
+        sb_host = orc.sign_mask(sign, d_in)
         sig, _ = orc.calibrate(w_host[:1024], s_host, sb_host, block)
         e = orc.encode(w_host, s_host, sb_host, block, cb_h, bits, sig, want_idx=False)
         orc.decode(e["codes"], e["norm"], d_in, sig, cb_h, bits, s_host, sb_host, block)
@@ -269,7 +269,7 @@ def qgemm_run(torch, q, sets, n_sets, cb, bits, scale, sign, block, timed):
     dev = sets[0]["w"].device
     d_out, d_in = sets[0]["w"].shape
     for i in range(n_sets):   # every set holds the codes and the BF16 decode of the same matrix
-        q.decode(sets[i]["codes"], sets[i]["norm"], sets[i]["sigma"], cb, bits, d_in, scale=scale, sign_bits=sign,
+        q.decode(sets[i]["codes"], sets[i]["norm"], sets[i]["sigma"], cb, bits, d_in, scale=scale, sign_seed=sign,
                  block=block, out=sets[i]["out"])
     stride = q.row_stride(d_in, bits)
     res = {}
@@ -283,7 +283,7 @@ def qgemm_run(torch, q, sets, n_sets, cb, bits, scale, sign, block, timed):
 
         def fused(i):
             b = sets[i % n_sets]
-            q.qgemm(x, b["codes"], b["norm"], b["sigma"], cb, bits, scale=scale, sign_bits=sign, block=block, out=y,
+            q.qgemm(x, b["codes"], b["norm"], b["sigma"], cb, bits, scale=scale, sign_seed=sign, block=block, out=y,
                     workspace=ws)
 
         def bf16(i):
@@ -291,7 +291,7 @@ def qgemm_run(torch, q, sets, n_sets, cb, bits, scale, sign, block, timed):
 
         def dec_mm(i):
             b = sets[i % n_sets]
-            q.decode(b["codes"], b["norm"], b["sigma"], cb, bits, d_in, scale=scale, sign_bits=sign, block=block, out=tmp)
+            q.decode(b["codes"], b["norm"], b["sigma"], cb, bits, d_in, scale=scale, sign_seed=sign, block=block, out=tmp)
             torch.matmul(x, tmp.t())
 
         for fn in (fused, bf16, dec_mm):   # first calls pick and load library kernels
@@ -340,8 +340,8 @@ def act_scale_run(torch, q, bset, cb, bits, index, sign, block, timed):
     errs = {}
     for alpha in (0.0, 0.3, 0.5):
         s = q.act_scale(x, alpha, workspace=ws)
-        e = q.encode(w, cb, bits, index, scale=s, sign_bits=sign, block=block)
-        q.decode(e["codes"], e["norm"], e["sigma"], cb, bits, d_in, scale=s, sign_bits=sign, block=block, out=out)
+        e = q.encode(w, cb, bits, index, scale=s, sign_seed=sign, block=block)
+        q.decode(e["codes"], e["norm"], e["sigma"], cb, bits, d_in, scale=s, sign_seed=sign, block=block, out=out)
         errs["alpha_%g" % alpha] = round(float(torch.sum((xf @ (out - wf).t()) ** 2)) / y2, 7)
     res["output_error"] = errs
     res["data"] = "synthetic activations drawn on the GPU; relative layer-output error, lower is better"
@@ -362,10 +362,10 @@ def ablation_run(torch, q, bset, pts, cfg, cb11, bits11, scale, sign, block):
     def err(table, nbits, index=None, thr=None, ba=None):
         if thr is None:
             idx = q.codebook_index(table, nbits) if index is None else index
-            e = q.encode(w, table, nbits, idx, scale=scale, sign_bits=sign, block=block)
+            e = q.encode(w, table, nbits, idx, scale=scale, sign_seed=sign, block=block)
         else:
-            e = q.encode_polar(w, ba, nbits - ba, thr, scale=scale, sign_bits=sign, block=block)
-        q.decode(e["codes"], e["norm"], e["sigma"], table, nbits, d_in, scale=scale, sign_bits=sign, block=block,
+            e = q.encode_polar(w, ba, nbits - ba, thr, scale=scale, sign_seed=sign, block=block)
+        q.decode(e["codes"], e["norm"], e["sigma"], table, nbits, d_in, scale=scale, sign_seed=sign, block=block,
                  out=out)
         return round(float(torch.linalg.vector_norm(out.float() - wf)) / wn, 6)
 
@@ -413,12 +413,12 @@ def polar_run(torch, q, sets, n_sets, scale, sign, block, ba, bp, timed, stream)
 
     def enc(i, sigma=None):
         bset = sets[i % n_sets]
-        q.encode_polar(bset["w"], ba, bp, thr, scale=scale, sign_bits=sign, block=block, sigma=sigma, status=status,
+        q.encode_polar(bset["w"], ba, bp, thr, scale=scale, sign_seed=sign, block=block, sigma=sigma, status=status,
                        workspace=ws, out={"codes": codes[i % n_sets], "norm": bset["norm"], "sigma": bset["sigma"]})
 
     def dec(i):
         bset = sets[i % n_sets]
-        q.decode(codes[i % n_sets], bset["norm"], bset["sigma"], table, bits, d_in, scale=scale, sign_bits=sign,
+        q.decode(codes[i % n_sets], bset["norm"], bset["sigma"], table, bits, d_in, scale=scale, sign_seed=sign,
                  block=block, out=bset["out"])
 
     for i in range(n_sets):
@@ -443,29 +443,16 @@ def polar_run(torch, q, sets, n_sets, scale, sign, block, ba, bp, timed, stream)
 def stack_run(torch, q, cb, index, bits, block, stream):
     """Encode, then decode, the 280 matrices of a 40-layer 13B-shaped stack back to back."""
     dev = cb.device
-    shapes = [(5120, 5120)] * 4 + [(13824, 5120)] * 2 + [(5120, 13824)]
-    n_layers = 40
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(0x51414D5700000005)
+    import synth_inputs as synth
     mats = []
-    for layer in range(n_layers):
-        for (d_out, d_in) in shapes:
-            # Student-t(4) x 0.015: a normal over the root of a chi-square(4) / 4, drawn in fp32
-            g = torch.randn((d_out, d_in), generator=gen, device=dev)
-            c = torch.zeros_like(g)
-            for _ in range(4):
-                c.add_(torch.randn((d_out, d_in), generator=gen, device=dev).square_())
-            w = (g * 0.015 / torch.sqrt(c * 0.25)).to(torch.bfloat16)
-            del g, c
-            s = torch.randn((d_in,), generator=gen, device=dev).abs().sqrt() + 0.1
-            sign = torch.randint(-2**31, 2**31 - 1, ((d_in + 31) // 32,), generator=gen, device=dev,
-                                 dtype=torch.int32)
-            stride = q.row_stride(d_in, bits)
-            mats.append({"w": w, "s": s, "sign": sign, "d_in": d_in,
-                         "codes": torch.empty((d_out, stride), dtype=torch.uint8, device=dev),
-                         "norm": torch.empty((d_out,), dtype=torch.int16, device=dev),
-                         "sigma": torch.empty((d_in // 2,), dtype=torch.float32, device=dev),
-                         "out": torch.empty((d_out, d_in), dtype=torch.bfloat16, device=dev)})
+    for spec in synth.config(4).matrices:   # per-layer seeds, drawn on the GPU (synth_gpu.hip)
+        d_out, d_in = spec.d_out, spec.d_in
+        stride = q.row_stride(d_in, bits)
+        mats.append({"w": spec.weights_device(dev), "s": torch.from_numpy(spec.channel_scale()).to(dev), "d_in": d_in,
+                     "codes": torch.empty((d_out, stride), dtype=torch.uint8, device=dev),
+                     "norm": torch.empty((d_out,), dtype=torch.int16, device=dev),
+                     "sigma": torch.empty((d_in // 2,), dtype=torch.float32, device=dev),
+                     "out": torch.empty((d_out, d_in), dtype=torch.bfloat16, device=dev)})
     ws = torch.empty((max(q.encode_workspace(m["w"].shape[0], m["d_in"], bits) for m in mats),), dtype=torch.uint8,
                      device=dev)
     status = torch.zeros((1,), dtype=torch.int32, device=dev)
@@ -473,12 +460,12 @@ def stack_run(torch, q, cb, index, bits, block, stream):
 
     def enc_all():
         for m in mats:
-            q.encode(m["w"], cb, bits, index, scale=m["s"], sign_bits=m["sign"], block=block, status=status,
+            q.encode(m["w"], cb, bits, index, scale=m["s"], sign_seed=q.DEFAULT_SIGN_SEED, block=block, status=status,
                      workspace=ws, out={"codes": m["codes"], "norm": m["norm"], "sigma": m["sigma"]})
 
     def dec_all():
         for m in mats:
-            q.decode(m["codes"], m["norm"], m["sigma"], cb, bits, m["d_in"], scale=m["s"], sign_bits=m["sign"],
+            q.decode(m["codes"], m["norm"], m["sigma"], cb, bits, m["d_in"], scale=m["s"], sign_seed=q.DEFAULT_SIGN_SEED,
                      block=block, out=m["out"])
 
     def best_ms(fn, reps=3):
@@ -506,7 +493,7 @@ def stack_run(torch, q, cb, index, bits, block, stream):
            "decode_GB_per_s": round(dec_bytes / (dec_ms * 1e-3) / 1e9, 1),
            "decode_frac": round(dec_bytes / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
            "resident_GB": round((n_w * 2 + sum(m["codes"].numel() for m in mats) + n_w * 2) / 1e9, 1),
-           "data": "synthetic, drawn on the GPU; K=2048 codebook and b=128 of the step"}
+           "data": "synthetic, the seeded 40-layer workload drawn on the GPU; K=2048 codebook and b=128 of the step"}
     del mats
     torch.cuda.empty_cache()
     return res

@@ -46,8 +46,18 @@ enum {
     QAMW_FLAG_BAD_SCALE = 2,   /* some s_j <= 0 or NaN                                        */
     QAMW_FLAG_NORM_RANGE = 4,  /* the row norm overflows f16                                  */
     QAMW_FLAG_POINT_RANGE = 8, /* a training point is non-finite or out of the fixed-point range */
-    QAMW_FLAG_BAD_THRESHOLDS = 16 /* polar thresholds not finite, >= 0 and non-decreasing        */
+    QAMW_FLAG_BAD_THRESHOLDS = 16, /* polar thresholds not finite, >= 0 and non-decreasing       */
+    QAMW_FLAG_BAD_INDEX = 32   /* the search index was built for another codebook size: nothing
+                                  was encoded                                                 */
 };
+
+/* Section 3.3: the rotation's sign mask is deterministic and shared by every row.  It is drawn from
+ * a 64-bit seed: eps_j = -1 exactly when the top bit of the (j+1)-th output of the splitmix64
+ * generator started at the seed is set, i.e. of mix(seed + (j+1) * 0x9E3779B97F4A7C15) with the
+ * published splitmix64 finalizer mix(z): z ^= z >> 30; z *= 0xBF58476D1CE4E5B9; z ^= z >> 27;
+ * z *= 0x94D049BB133111EB; z ^= z >> 31 (arithmetic modulo 2^64).  Encoder and decoder must be
+ * given the same seed.  QAMW_DEFAULT_SIGN_SEED is the value used when the caller has no other. */
+#define QAMW_DEFAULT_SIGN_SEED 0x51414D57ull
 
 /* Most rows a matrix may have in qamw_encode, qamw_encode_polar, qamw_decode and qamw_qgemm
  * (QAMW_ERR_UNSUPPORTED above): the kernels address the d_out row norms through 32-bit byte
@@ -108,7 +118,8 @@ int qamw_codebook_index(const float* d_codebook, int32_t bits, void* d_index, si
                         void* stream);
 
 /* Section 3.6: nearest codeword of n 2D points (fp32, interleaved), written to d_idx (int32),
- * using an index from qamw_codebook_index.  Same distance and tie rule as above. */
+ * using an index from qamw_codebook_index.  Same distance and tie rule as above.  An index built
+ * for another codebook size gives -1 for every point. */
 int qamw_nearest(const float* d_points, int64_t n, const float* d_codebook, int32_t bits,
                  const void* d_index, int32_t* d_idx, void* stream);
 
@@ -116,7 +127,7 @@ int qamw_nearest(const float* d_points, int64_t n, const float* d_codebook, int3
  * per-channel scale).  For every row i of W:
  *   a_j = w_ij * s_j (double), r = ||a||_2; r == 0 gives a zero row (norm 0, all indices 0);
  *   y = blockdiag(H_b) (eps . a / r), H_b the Sylvester-ordered Hadamard matrix / sqrt(b),
- *   eps_j = -1 where bit j%32 of d_sign_bits[j/32] is set, else +1 (section 3.3);
+ *   eps the sign mask of sign_seed (section 3.3, QAMW_DEFAULT_SIGN_SEED above);
  *   p_k = (fl32(y_2k / sigma_k), fl32(y_2k+1 / sigma_k)), idx_k = nearest codeword;
  *   norm_i = f16(fl32(r)) round-to-nearest-even (section 3.2: 16-bit row norm);
  *   indices packed as in qamw_row_stride.
@@ -124,14 +135,18 @@ int qamw_nearest(const float* d_points, int64_t n, const float* d_codebook, int3
  *   d_w, w_dtype   weights (QAMW_F32 or QAMW_BF16), d_out x d_in, leading dimension ld_w >= d_in;
  *                  0 <= d_out <= QAMW_MAX_ROWS.
  *   d_scale        d_in fp32 channel scales s_j > 0, or NULL for all ones.
- *   d_sign_bits    (d_in + 31) / 32 words of sign-mask bits, or NULL for all +1.
  *   block          Hadamard block size b: a power of two in [2, 1024] dividing d_in, or 0 for
  *                  qamw_default_block(d_in).  d_in must be even.  The kernels give each lane E
  *                  consecutive columns (E = 16 for b <= 128, 32 for b = 256 or 512, 64 for
  *                  b = 1024): d_in must be a multiple of E and d_in / E at most 1024 (E = 16)
  *                  or 512 (E = 32, 64), i.e. d_in <= 16384, 16384 and 32768; otherwise
  *                  QAMW_ERR_UNSUPPORTED.
- *   d_codebook, bits, d_index   K = 2^bits codebook and its index; 1 <= bits <= 12.
+ *   sign_seed      seed of the sign mask.
+ *   d_codebook, bits, d_index   K = 2^bits codebook and its index; 1 <= bits <= 12.  The index
+ *                  argument is not in the problem statement of the pages: it is built once per
+ *                  codebook by qamw_codebook_index (tens of milliseconds) and serves every matrix
+ *                  coded with that codebook.  An index of another codebook size sets
+ *                  QAMW_FLAG_BAD_INDEX and nothing is written.
  *   d_sigma_in     d_in/2 fp32 per-pair scales to use, or NULL to calibrate (eq. 1):
  *                  sigma_k = fl32(mean |z_k| / sqrt(pi/2)), mean in double over the non-zero
  *                  finite rows among rows 0 .. min(d_out, 1024) - 1; 1/sqrt(d_in) when there
@@ -142,7 +157,7 @@ int qamw_nearest(const float* d_points, int64_t n, const float* d_codebook, int3
  *   d_codes        d_out x qamw_row_stride(d_in, bits) bytes.
  *   d_ws, ws_bytes at least qamw_encode_workspace(d_out, d_in, bits) bytes. */
 int qamw_encode(const void* d_w, qamw_dtype w_dtype, int32_t d_out, int32_t d_in, int64_t ld_w,
-                const float* d_scale, const uint32_t* d_sign_bits, int32_t block,
+                const float* d_scale, int32_t block, uint64_t sign_seed,
                 const float* d_codebook, int32_t bits, const void* d_index,
                 const float* d_sigma_in, float* d_sigma_out, uint16_t* d_norm_f16, uint8_t* d_codes,
                 int32_t* d_status, void* d_ws, size_t ws_bytes, void* stream);
@@ -153,12 +168,18 @@ int qamw_encode(const void* d_w, qamw_dtype w_dtype, int32_t d_out, int32_t d_in
  *   w^_ij = f16(norm_i) * eps_j * (H_b x)_j / s_j,  x_2k = sigma_k c_x[idx_k], x_2k+1 = sigma_k c_y[idx_k]
  * computed in double and rounded to fp32 (QAMW_F32) or to fp32 then BF16 with
  * round-to-nearest-even (QAMW_BF16).  A zero norm gives a row of +0.
- * Arguments mirror qamw_encode; d_out_w is d_out x d_in with leading dimension ld_out >= d_in
- * (ld_out even).  Same block / d_in / d_out limits as qamw_encode. */
+ * Arguments mirror qamw_encode (sign_seed must be the encoder's); d_out_w is d_out x d_in with
+ * leading dimension ld_out >= d_in (ld_out even).  Same block / d_in / d_out / bits limits as
+ * qamw_encode: every matrix qamw_encode accepts can be decoded. */
 int qamw_decode(const uint8_t* d_codes, const uint16_t* d_norm_f16, const float* d_sigma,
                 const float* d_codebook, int32_t bits, const float* d_scale,
-                const uint32_t* d_sign_bits, int32_t d_out, int32_t d_in, int32_t block,
+                int32_t d_out, int32_t d_in, int32_t block, uint64_t sign_seed,
                 void* d_out_w, qamw_dtype out_dtype, int64_t ld_out, void* stream);
+
+/* Section 3.3: the sign mask of a seed as bits, for callers and tests that need eps itself: bit
+ * j % 32 of d_bits[j / 32] is set when eps_j = -1 (j < d_in); the bits of the last word past d_in
+ * are 0.  d_bits: (d_in + 31) / 32 device words.  d_in >= 0 (0 is a no-op). */
+int qamw_sign_mask(uint64_t sign_seed, int32_t d_in, uint32_t* d_bits, void* stream);
 
 /* Section 1 (the matrix product that follows dequantization), fused: for M activation rows
  *   y[m][i] = sum_j x[m][j] w^_ij
@@ -183,7 +204,7 @@ int qamw_decode(const uint8_t* d_codes, const uint16_t* d_norm_f16, const float*
 size_t qamw_qgemm_workspace(int32_t M, int32_t d_out, int32_t d_in);
 int qamw_qgemm(const void* d_x, qamw_dtype x_dtype, int32_t M, int64_t ld_x, const uint8_t* d_codes,
                const uint16_t* d_norm_f16, const float* d_sigma, const float* d_codebook, int32_t bits,
-               const float* d_scale, const uint32_t* d_sign_bits, int32_t d_out, int32_t d_in, int32_t block,
+               const float* d_scale, int32_t d_out, int32_t d_in, int32_t block, uint64_t sign_seed,
                void* d_y, qamw_dtype y_dtype, int64_t ld_y, void* d_ws, size_t ws_bytes, void* stream);
 
 /* Section 3.5 (the polar baseline QAM-W is compared with): a pair is coded as a magnitude level
@@ -222,7 +243,7 @@ int qamw_polar_index(const float* d_points, int64_t n, int32_t ba, int32_t bp, c
  * writes them); otherwise QAMW_FLAG_BAD_THRESHOLDS is set and the indices are unspecified.
  * Decode with qamw_decode, the table of qamw_polar_codebook and bits = ba + bp. */
 int qamw_encode_polar(const void* d_w, qamw_dtype w_dtype, int32_t d_out, int32_t d_in, int64_t ld_w,
-                      const float* d_scale, const uint32_t* d_sign_bits, int32_t block, int32_t ba, int32_t bp,
+                      const float* d_scale, int32_t block, uint64_t sign_seed, int32_t ba, int32_t bp,
                       const double* d_thresholds, const float* d_sigma_in, float* d_sigma_out,
                       uint16_t* d_norm_f16, uint8_t* d_codes, int32_t* d_status, void* d_ws, size_t ws_bytes,
                       void* stream);

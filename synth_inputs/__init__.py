@@ -4,8 +4,9 @@ The QAM-W pages measure on real LLM checkpoints (TinyLlama-1.1B ... 13B) that ar
 not available here; these generators stand in for them with matrices of the
 same shapes and heavy-tailed, outlier-column statistics.  Everything is a pure
 function of (seed, stream id, counter), produced by ``synth.c``.  This module
-contains none of the codec's arithmetic; the CPU oracle and the GPU library both
-read the bytes it produces.
+contains none of the codec's arithmetic (the rotation's sign mask is drawn from
+its seed by the library and by the oracle, each on its own); the CPU oracle and
+the GPU library both read the bytes it produces.
 """
 from __future__ import annotations
 
@@ -20,9 +21,10 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "synth.c")
 _LIB = os.path.join(_HERE, "libsynth.so")
+_SRC_GPU = os.path.join(_HERE, "synth_gpu.hip")
+_LIB_GPU = os.path.join(_HERE, "libsynth_gpu.so")
 
 CONFIG_SEED_BASE = 0x51414D5700000000
-DEFAULT_SIGN_SEED = 0x51414D57
 SID_POINTS = 4
 SID_POINTS_K128 = 5
 
@@ -38,6 +40,34 @@ def build(force: bool = False) -> str:
         subprocess.check_call(cmd)
         os.replace(tmp, _LIB)
     return _LIB
+
+
+def build_gpu(force: bool = False) -> str:
+    """Compile synth_gpu.hip (the device form of synth_weights) for gfx950 into libsynth_gpu.so."""
+    if force or not os.path.exists(_LIB_GPU) or os.path.getmtime(_LIB_GPU) < os.path.getmtime(_SRC_GPU):
+        tmp = _LIB_GPU + ".tmp%d" % os.getpid()
+        cmd = [os.environ.get("HIPCC", "/opt/rocm/bin/hipcc"), "--offload-arch=gfx950", "-O3", "-std=c++17",
+               "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "-Wno-unused-command-line-argument", "-fPIC", "-shared", _SRC_GPU, "-o", tmp]
+        subprocess.check_call(cmd)
+        os.replace(tmp, _LIB_GPU)
+    return _LIB_GPU
+
+
+_lib_gpu = None
+
+
+def _load_gpu():
+    global _lib_gpu
+    if _lib_gpu is None:
+        if not os.path.exists(_LIB_GPU):
+            raise RuntimeError("libsynth_gpu.so is not built (%s); run __graft_entry__.build()" % _LIB_GPU)
+        lib = ctypes.CDLL(_LIB_GPU)
+        u64, i64, i32, dbl, vp = (ctypes.c_uint64, ctypes.c_int64, ctypes.c_int32, ctypes.c_double, ctypes.c_void_p)
+        lib.synth_weights_device.argtypes = [u64, u64, i64, i64, i32, i32, i32, dbl, vp, dbl, i32, vp, vp]
+        lib.synth_weights_device.restype = ctypes.c_int
+        _lib_gpu = lib
+    return _lib_gpu
 
 
 def _load():
@@ -64,8 +94,6 @@ def _load():
         lib.synth_channel_scale.restype = None
         lib.synth_points.argtypes = [u64, u64, i64, vp]
         lib.synth_points.restype = None
-        lib.synth_sign_bits.argtypes = [u64, i32, vp]
-        lib.synth_sign_bits.restype = None
         _lib = lib
     return _lib
 
@@ -93,20 +121,6 @@ def points(seed: int, sid: int, n: int) -> np.ndarray:
     out = np.empty((n, 2), dtype=np.float32)
     _load().synth_points(seed, sid, n, _ptr(out))
     return out
-
-
-def sign_bits(d_in: int, sign_seed: int = DEFAULT_SIGN_SEED) -> np.ndarray:
-    """Packed sign mask: bit j%32 of word j/32 is set when eps_j = -1."""
-    out = np.zeros(((d_in + 31) // 32,), dtype=np.uint32)
-    _load().synth_sign_bits(sign_seed, d_in, _ptr(out))
-    return out
-
-
-def signs_from_bits(words: np.ndarray, d_in: int) -> np.ndarray:
-    """Unpack the sign-mask bits into +1/-1 (float64), for test code."""
-    j = np.arange(d_in)
-    bit = (words[j >> 5] >> (j & 31).astype(np.uint32)) & 1
-    return np.where(bit == 1, -1.0, 1.0)
 
 
 def bf16_bits_to_f32(u16: np.ndarray) -> np.ndarray:
@@ -159,6 +173,30 @@ class MatrixSpec:
         _load().synth_weights(self.seed, self.sid_w, row0, nrows, self.d_in, self.dist, self.nu,
                               self.scale, _ptr(mask), self.outlier_factor, 1 if self.bf16 else 0,
                               _ptr(out))
+        return out
+
+    def weights_device(self, device, row0: int = 0, nrows: Optional[int] = None, out=None):
+        """The same rows as weights(), drawn on the GPU (synth_gpu.hip) into a torch tensor:
+        bfloat16 or float32, nrows x d_in, on `device`; generated on torch's current stream."""
+        import torch
+        if nrows is None:
+            nrows = self.d_out - row0
+        dt = torch.bfloat16 if self.bf16 else torch.float32
+        if out is None:
+            out = torch.empty((nrows, self.d_in), dtype=dt, device=device)
+        if out.dtype != dt or tuple(out.shape) != (nrows, self.d_in) or not out.is_contiguous():
+            raise ValueError("out must be a contiguous %d x %d %s tensor" % (nrows, self.d_in, dt))
+        mask = None
+        if self.n_outlier:
+            mask = torch.from_numpy(self.outlier_mask()).to(out.device)
+        rc = _load_gpu().synth_weights_device(self.seed, self.sid_w, row0, nrows, self.d_in, self.dist, self.nu,
+                                              self.scale, None if mask is None else mask.data_ptr(),
+                                              self.outlier_factor, 1 if self.bf16 else 0, out.data_ptr(),
+                                              torch.cuda.current_stream(out.device).cuda_stream)
+        if rc != 0:
+            raise RuntimeError("synth_weights_device failed")
+        if mask is not None:
+            torch.cuda.current_stream(out.device).synchronize()   # the mask tensor is freed here
         return out
 
     def channel_scale(self) -> np.ndarray:

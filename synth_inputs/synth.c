@@ -1,7 +1,7 @@
 /*
  * Seeded synthetic inputs for the QAM-W weight codec: weight matrices shaped
- * like LLM projections, per-input-channel scales, training points drawn from
- * the unit circular Gaussian, and the deterministic sign mask.
+ * like LLM projections, per-input-channel scales and training points drawn
+ * from the unit circular Gaussian.
  *
  * This module only produces inputs.  It holds none of the codec's arithmetic
  * and is shared, as a data source, by the CPU oracle and the GPU library.
@@ -171,17 +171,5 @@ void synth_points(uint64_t seed, uint64_t sid, int64_t n, float* xy)
     for (int64_t i = 0; i < n; ++i) {
         xy[2 * i] = (float)synth_gauss(key, (uint64_t)(2 * i));
         xy[2 * i + 1] = (float)synth_gauss(key, (uint64_t)(2 * i + 1));
-    }
-}
-
-/* Deterministic sign mask: eps_j = -1 when the top bit of
- * mix(seed + (j+1)*golden) is set.  Bit j%32 of word j/32 holds (eps_j == -1). */
-void synth_sign_bits(uint64_t sign_seed, int32_t d_in, uint32_t* words)
-{
-    int32_t nw = (d_in + 31) / 32;
-    for (int32_t w = 0; w < nw; ++w) words[w] = 0;
-    for (int32_t j = 0; j < d_in; ++j) {
-        uint64_t z = sx_mix(sign_seed + (uint64_t)(j + 1) * SX_GOLDEN);
-        if (z >> 63) words[j >> 5] |= 1u << (j & 31);
     }
 }

@@ -38,29 +38,27 @@ def w_tensor(w: np.ndarray, ld: int = None) -> torch.Tensor:
     return x.to(DEV)
 
 
-def sign_tensor(sb: np.ndarray) -> torch.Tensor:
-    return t(sb.view(np.int32))
-
-
-def gpu_encode(q, w, s, sb, block, cb, bits, sigma=None, ld=None, index=None, cb_dev=None):
+def gpu_encode(q, w, s, seed, block, cb, bits, sigma=None, ld=None, index=None, cb_dev=None):
+    """GPU encode through the binding; `seed` is the sign-mask seed (None: the library default)."""
     cb_dev = t(cb) if cb_dev is None else cb_dev
     index = q.codebook_index(cb_dev, bits) if index is None else index
     st = torch.zeros((1,), dtype=torch.int32, device=DEV)
     out = q.encode(w_tensor(w, ld), cb_dev, bits, index, scale=None if s is None else t(s),
-                   sign_bits=None if sb is None else sign_tensor(sb), block=block,
+                   sign_seed=q.DEFAULT_SIGN_SEED if seed is None else seed, block=block,
                    sigma=None if sigma is None else t(sigma), status=st)
     torch.cuda.synchronize()
     return {"codes": out["codes"].cpu().numpy(), "norm": out["norm"].cpu().numpy().view(np.uint16),
             "sigma": out["sigma"].cpu().numpy(), "status": int(st.item())}
 
 
-def gpu_decode(q, codes, norm, sigma, cb, bits, s, sb, d_in, block, out_dtype=torch.bfloat16, ld=None):
+def gpu_decode(q, codes, norm, sigma, cb, bits, s, seed, d_in, block, out_dtype=torch.bfloat16, ld=None):
     d_out = norm.shape[0]
     out = None
     if ld is not None and ld != d_in:
         out = torch.full((d_out, ld), 7.0, dtype=out_dtype, device=DEV)[:, :d_in]
     res = q.decode(t(codes), t(norm.view(np.int16)), t(sigma), t(cb), bits, d_in, scale=None if s is None else t(s),
-                   sign_bits=None if sb is None else sign_tensor(sb), block=block, out_dtype=out_dtype, out=out)
+                   sign_seed=q.DEFAULT_SIGN_SEED if seed is None else seed, block=block, out_dtype=out_dtype,
+                   out=out)
     torch.cuda.synchronize()
     if out_dtype == torch.bfloat16:
         return res.view(torch.int16).cpu().numpy().view(np.uint16)

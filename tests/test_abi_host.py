@@ -22,7 +22,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = q.header_symbols()
-    assert len(names) == 19
+    assert len(names) == 20
     out = subprocess.run(["nm", "-D", "--defined-only", q.LIB_PATH], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
     for n in names:
@@ -61,20 +61,20 @@ FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation
 
 
 def _enc(lib, **kw):
-    a = dict(w=FAKE, dt=q.BF16, d_out=16, d_in=256, ld=256, scale=None, sign=None, block=64, cb=FAKE, bits=8,
-             index=FAKE, sig_in=FAKE, sig_out=None, norm=FAKE, codes=FAKE, status=None, ws=None, ws_bytes=0)
+    a = dict(w=FAKE, dt=q.BF16, d_out=16, d_in=256, ld=256, scale=None, seed=q.DEFAULT_SIGN_SEED, block=64, cb=FAKE,
+             bits=8, index=FAKE, sig_in=FAKE, sig_out=None, norm=FAKE, codes=FAKE, status=None, ws=None, ws_bytes=0)
     a.update(kw)
-    return lib.qamw_encode(a["w"], a["dt"], a["d_out"], a["d_in"], a["ld"], a["scale"], a["sign"], a["block"],
+    return lib.qamw_encode(a["w"], a["dt"], a["d_out"], a["d_in"], a["ld"], a["scale"], a["block"], a["seed"],
                            a["cb"], a["bits"], a["index"], a["sig_in"], a["sig_out"], a["norm"], a["codes"],
                            a["status"], a["ws"], a["ws_bytes"], None)
 
 
 def _dec(lib, **kw):
-    a = dict(codes=FAKE, norm=FAKE, sigma=FAKE, cb=FAKE, bits=8, scale=None, sign=None, d_out=16, d_in=256,
-             block=64, out=FAKE, dt=q.BF16, ld=256)
+    a = dict(codes=FAKE, norm=FAKE, sigma=FAKE, cb=FAKE, bits=8, scale=None, seed=q.DEFAULT_SIGN_SEED, d_out=16,
+             d_in=256, block=64, out=FAKE, dt=q.BF16, ld=256)
     a.update(kw)
-    return lib.qamw_decode(a["codes"], a["norm"], a["sigma"], a["cb"], a["bits"], a["scale"], a["sign"],
-                           a["d_out"], a["d_in"], a["block"], a["out"], a["dt"], a["ld"], None)
+    return lib.qamw_decode(a["codes"], a["norm"], a["sigma"], a["cb"], a["bits"], a["scale"], a["d_out"], a["d_in"],
+                           a["block"], a["seed"], a["out"], a["dt"], a["ld"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -139,10 +139,10 @@ def test_product_path_does_not_use_the_oracle():
 
 
 def _encp(lib, **kw):
-    a = dict(w=FAKE, dt=q.BF16, d_out=16, d_in=256, ld=256, scale=None, sign=None, block=64, ba=5, bp=6, thr=FAKE,
-             sig_in=FAKE, sig_out=None, norm=FAKE, codes=FAKE, status=None, ws=None, ws_bytes=0)
+    a = dict(w=FAKE, dt=q.BF16, d_out=16, d_in=256, ld=256, scale=None, seed=q.DEFAULT_SIGN_SEED, block=64, ba=5,
+             bp=6, thr=FAKE, sig_in=FAKE, sig_out=None, norm=FAKE, codes=FAKE, status=None, ws=None, ws_bytes=0)
     a.update(kw)
-    return lib.qamw_encode_polar(a["w"], a["dt"], a["d_out"], a["d_in"], a["ld"], a["scale"], a["sign"], a["block"],
+    return lib.qamw_encode_polar(a["w"], a["dt"], a["d_out"], a["d_in"], a["ld"], a["scale"], a["block"], a["seed"],
                                  a["ba"], a["bp"], a["thr"], a["sig_in"], a["sig_out"], a["norm"], a["codes"],
                                  a["status"], a["ws"], a["ws_bytes"], None)
 
@@ -171,11 +171,12 @@ def test_polar_codebook_and_index_reject(lib):
 
 def _qg(lib, **kw):
     a = dict(x=FAKE, xt=q.BF16, M=4, ld_x=256, codes=FAKE, norm=FAKE, sigma=FAKE, cb=FAKE, bits=8, scale=None,
-             sign=None, d_out=16, d_in=256, block=64, y=FAKE, yt=q.F32, ld_y=16, ws=FAKE, ws_bytes=1 << 20)
+             seed=q.DEFAULT_SIGN_SEED, d_out=16, d_in=256, block=64, y=FAKE, yt=q.F32, ld_y=16, ws=FAKE,
+             ws_bytes=1 << 20)
     a.update(kw)
     return lib.qamw_qgemm(a["x"], a["xt"], a["M"], a["ld_x"], a["codes"], a["norm"], a["sigma"], a["cb"], a["bits"],
-                          a["scale"], a["sign"], a["d_out"], a["d_in"], a["block"], a["y"], a["yt"], a["ld_y"], a["ws"],
-                          a["ws_bytes"], None)
+                          a["scale"], a["d_out"], a["d_in"], a["block"], a["seed"], a["y"], a["yt"], a["ld_y"],
+                          a["ws"], a["ws_bytes"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -220,3 +221,69 @@ def test_act_scale_rejects(lib):
     assert call(x=FAKE + 1) == ARG and call(r=FAKE + 4) == ARG
     assert call(ws=None) == WS and call(wsb=8) == WS
     assert lib.qamw_act_scale_workspace(2048, 4096) >= 4096 * 8 and lib.qamw_act_scale_workspace(0, 8) == 0
+
+
+def test_sign_mask_rejects(lib):
+    assert lib.qamw_sign_mask(1, -1, FAKE, None) == ARG
+    assert lib.qamw_sign_mask(1, 64, None, None) == ARG
+    assert lib.qamw_sign_mask(1, 64, FAKE + 2, None) == ARG
+    assert lib.qamw_sign_mask(1, 0, None, None) == q.OK
+
+
+def test_header_default_seed_matches_binding():
+    import re
+    text = open(q.HEADER_PATH).read()
+    m = re.search(r"#define QAMW_DEFAULT_SIGN_SEED (0x[0-9A-Fa-f]+)ull", text)
+    assert m and int(m.group(1), 16) == q.DEFAULT_SIGN_SEED
+
+
+# ----------------------------------------------------------------------------- binding argument checks
+# The library trusts the sizes it is given, so the binding checks every tensor against the shape the
+# call implies before a pointer is passed.  These calls use host tensors: each must be rejected by a
+# size or dtype check (a ValueError naming the argument), before the device check.
+
+import torch  # noqa: E402
+
+
+def _bad(fn, match, *a, **kw):
+    with pytest.raises(ValueError, match=match):
+        fn(*a, **kw)
+
+
+def test_binding_rejects_short_or_mistyped_buffers(lib):
+    d_out, d_in, bits = 8, 256, 8
+    stride = q.row_stride(d_in, bits)
+    codes = torch.zeros((d_out, stride), dtype=torch.uint8)
+    norm = torch.zeros((d_out,), dtype=torch.int16)
+    sigma = torch.zeros((d_in // 2,), dtype=torch.float32)
+    cb = torch.zeros((1 << bits, 2), dtype=torch.float32)
+    # decode
+    _bad(q.decode, "codes", codes[:, :-16], norm, sigma, cb, bits, d_in)
+    _bad(q.decode, "codes", codes[:-1], norm, sigma, cb, bits, d_in)
+    _bad(q.decode, "sigma", codes, norm, sigma[:-1], cb, bits, d_in)
+    _bad(q.decode, "sigma", codes, norm, sigma.double(), cb, bits, d_in)
+    _bad(q.decode, "codebook", codes, norm, sigma, cb[:-1], bits, d_in)
+    _bad(q.decode, "codes", codes, norm, sigma, cb, bits + 1, d_in)   # the stride of 9-bit codes
+    _bad(q.decode, "norm", codes, norm.float(), sigma, cb, bits, d_in)
+    _bad(q.decode, "scale", codes, norm, sigma, cb, bits, d_in, scale=torch.ones(d_in - 1))
+    _bad(q.decode, "out", codes, norm, sigma, cb, bits, d_in, out=torch.zeros((d_out, d_in - 2), dtype=torch.bfloat16))
+    _bad(q.decode, "device", codes, norm, sigma, cb, bits, d_in)   # all sizes right: the device check
+    # encode
+    w = torch.zeros((d_out, d_in), dtype=torch.bfloat16)
+    index = torch.zeros((q.index_bytes(bits),), dtype=torch.uint8)
+    _bad(q.encode, "index", w, cb, bits, index[:-1])
+    _bad(q.encode, "codebook", w, cb[:3], bits, index)
+    _bad(q.encode, "w", w.to(torch.float16), cb, bits, index)
+    _bad(q.encode, "scale", w, cb, bits, index, scale=torch.ones(d_in // 2))
+    _bad(q.encode, "sigma", w, cb, bits, index, sigma=torch.ones(d_in // 4))
+    _bad(q.encode, "status", w, cb, bits, index, status=torch.zeros(1, dtype=torch.int64))
+    _bad(q.encode, "codes", w, cb, bits, index, out={"codes": torch.zeros((d_out, stride - 16), dtype=torch.uint8)})
+    # fused product, polar, nearest, training
+    _bad(q.qgemm, "codes", torch.zeros((2, d_in + 2)), codes, norm, sigma, cb, bits)   # x's width sets d_in
+    _bad(q.qgemm, "x", torch.zeros((2, d_in), dtype=torch.float16), codes, norm, sigma, cb, bits)
+    _bad(q.qgemm, "out", torch.zeros((2, d_in)), codes, norm, sigma, cb, bits, out=torch.zeros((2, d_out + 1)))
+    _bad(q.encode_polar, "thresholds", w, 4, 4, torch.zeros(14, dtype=torch.float64))
+    _bad(q.polar_index, "thresholds", torch.zeros((4, 2)), 4, 4, torch.zeros(15, dtype=torch.float32))
+    _bad(q.nearest, "index", torch.zeros((4, 2)), cb, bits, index[:10])
+    _bad(q.nearest, "pairs", torch.zeros((5,)), cb, bits, index)
+    _bad(q.codebook_train, "init", torch.zeros((1024, 2)), bits, 3, init=cb[:10])

@@ -19,7 +19,7 @@ import pytest
 import scipy.linalg
 import torch
 
-from helpers import DEV, assert_bf16_within_1ulp, log, sign_tensor, t
+from helpers import DEV, assert_bf16_within_1ulp, log, t
 
 pytestmark = pytest.mark.gpu
 
@@ -30,12 +30,13 @@ def _problem(orc, seed, d_out, d_in, block, bits):
     w[:, rng.choice(d_in, size=max(1, d_in // 100), replace=False)] *= 10
     w[min(2, d_out - 1)] = 0
     s = (np.abs(rng.standard_normal(d_in)) ** 0.5 + 0.1).astype(np.float32)
-    sb = rng.integers(0, 2**32, size=(d_in + 31) // 32, dtype=np.uint64).astype(np.uint32)
+    sseed = int(rng.integers(0, 2**62))   # sign-mask seed
+    sb = orc.sign_mask(sseed, d_in)
     cb = rng.standard_normal((1 << bits, 2)).astype(np.float32)
     sig, _ = orc.calibrate(w[:1024], s, sb, block)
     e = orc.encode(w, s, sb, block, cb, bits, sig)
     return dict(codes=e["codes"], norm=e["norm"], d_in=d_in, sigma=sig, cb=cb, bits=bits, s=s, sign_bits=sb,
-                block=block)
+                sign_seed=sseed, block=block)
 
 
 def _abs_terms(orc, x, pr):
@@ -73,7 +74,7 @@ def _run(q, orc, pr, M, x_dtype="bf16", y_dtype=torch.float32, ld_x=None, ld_y=N
         full = torch.full((M, ld_y), 7.0, dtype=y_dtype, device=DEV)
         out = full[:, :d_out]
     y = q.qgemm(xd, t(pr["codes"]), t(pr["norm"].view(np.int16)), t(pr["sigma"]), t(pr["cb"]), pr["bits"],
-                scale=t(pr["s"]), sign_bits=sign_tensor(pr["sign_bits"]), block=pr["block"], out_dtype=y_dtype,
+                scale=t(pr["s"]), sign_seed=pr["sign_seed"], block=pr["block"], out_dtype=y_dtype,
                 out=out)
     torch.cuda.synchronize()
     if full is not None:
@@ -153,7 +154,7 @@ def test_qgemm_empty_and_limits(q, orc):
     pr = _problem(orc, 8, 8, 256, 64, 8)
     x = torch.zeros((0, 256), dtype=torch.bfloat16, device=DEV)
     y = q.qgemm(x, t(pr["codes"]), t(pr["norm"].view(np.int16)), t(pr["sigma"]), t(pr["cb"]), 8,
-                scale=t(pr["s"]), sign_bits=sign_tensor(pr["sign_bits"]), block=64)
+                scale=t(pr["s"]), sign_seed=pr["sign_seed"], block=64)
     assert y.shape == (0, 8)
     x17 = torch.zeros((17, 256), dtype=torch.bfloat16, device=DEV)
     with pytest.raises(q.QamwError) as ei:
@@ -172,11 +173,11 @@ def test_qgemm_fullsize_attn4096(q, orc, synth, M):
     cb = np.ascontiguousarray(np.load("tests/golden/cb_cfg1_k2048.npz")["codebook"]).astype(np.float32)
     w = m.weights()
     s = m.channel_scale()
-    sb = synth.sign_bits(d_in)
+    sb = orc.sign_mask(q.DEFAULT_SIGN_SEED, d_in)
     sig, _ = orc.calibrate(w[:1024], s, sb, block)
     e = orc.encode(w, s, sb, block, cb, bits, sig, want_idx=False)
     pr = dict(codes=e["codes"], norm=e["norm"], d_in=d_in, sigma=sig, cb=cb, bits=bits, s=s, sign_bits=sb,
-              block=block)
+              sign_seed=q.DEFAULT_SIGN_SEED, block=block)
     x, y, ref = _run(q, orc, pr, M, seed=M)
     rel = _check_f32(orc, x, y, ref, pr)
     log("  max error %.3g of the absolute term sum" % rel)

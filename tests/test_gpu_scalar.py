@@ -16,7 +16,7 @@ import numpy as np
 import pytest
 import torch
 
-from helpers import DEV, assert_bf16_within_1ulp, check_indices, gpu_decode, log, sign_tensor, t, unpack_rows, w_tensor
+from helpers import DEV, assert_bf16_within_1ulp, check_indices, gpu_decode, log, t, unpack_rows, w_tensor
 
 pytestmark = pytest.mark.gpu
 
@@ -43,15 +43,16 @@ def _problem(seed, d_out, d_in):
     w[min(1, d_out - 1)] = 0
     w = torch.from_numpy(w).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     s = (np.abs(rng.standard_normal(d_in)) ** 0.5 + 0.1).astype(np.float32)
-    sb = rng.integers(0, 2**32, size=(d_in + 31) // 32, dtype=np.uint64).astype(np.uint32)
-    return w, s, sb
+    seed = int(rng.integers(0, 2**62))   # sign-mask seed
+    return w, s, seed
 
 
 @pytest.mark.parametrize("shape", [(40, 4096, 128, 4), (33, 768, 256, 3), (17, 512, 64, 6), (20, 1024, 32, 1)],
                          ids=lambda s: "%dx%d_b%d_%dbit" % s)
 def test_scalar_encode_matches_oracle(q, orc, shape):
     d_out, d_in, block, b = shape
-    w, s, sb = _problem(d_out + d_in + b, d_out, d_in)
+    w, s, seed = _problem(d_out + d_in + b, d_out, d_in)
+    sb = orc.sign_mask(seed, d_in)
     sig, _ = orc.calibrate(w[:1024], s, sb, block)
     lv_r, thr_r = orc.gauss_lloyd_max(b)
     tab_r = orc.scalar_table(b, lv_r)
@@ -59,7 +60,7 @@ def test_scalar_encode_matches_oracle(q, orc, shape):
     log("scalar encode %s" % (shape,))
     cb_dev = t(tab_r)
     st = torch.zeros((1,), dtype=torch.int32, device=DEV)
-    out = q.encode(w_tensor(w), cb_dev, 2 * b, q.codebook_index(cb_dev, 2 * b), scale=t(s), sign_bits=sign_tensor(sb),
+    out = q.encode(w_tensor(w), cb_dev, 2 * b, q.codebook_index(cb_dev, 2 * b), scale=t(s), sign_seed=seed,
                    block=block, status=st)
     torch.cuda.synchronize()
     codes = out["codes"].cpu().numpy()
@@ -73,7 +74,7 @@ def test_scalar_encode_matches_oracle(q, orc, shape):
     np.testing.assert_array_equal(codes[same], ref["codes"][same])
     # decode with the GPU's own table
     _, _, tab = q.scalar_codebook(b)
-    dec = gpu_decode(q, codes, out["norm"].cpu().numpy().view(np.uint16), sig, tab.cpu().numpy(), 2 * b, s, sb, d_in,
+    dec = gpu_decode(q, codes, out["norm"].cpu().numpy().view(np.uint16), sig, tab.cpu().numpy(), 2 * b, s, seed, d_in,
                      block)
     dref = orc.decode(codes, ref["norm"], d_in, sig, tab_r, 2 * b, s, sb, block)
     n = assert_bf16_within_1ulp(dec, dref["bf16"])

@@ -24,12 +24,11 @@ def test_pinned_checksums(synth):
         "cfg1_scale": _sha(m.channel_scale()),
         "cfg1_points_4096": _sha(synth.points(c1.seed, 4, 4096)),
         "cfg0_rows": _sha(synth.config(0).matrices[0].weights()),
-        "signs_13824": _sha(synth.sign_bits(13824)),
     }
     assert got == PINNED, got
 
 
-PINNED = {'cfg1_rows0_8': '918e5a424c249500', 'cfg1_scale': '75b452ba08055122', 'cfg1_points_4096': '42da9f1667686020', 'cfg0_rows': '261e4d3a9b9efbfc', 'signs_13824': '3e4e8f4f0760cc82'}
+PINNED = {'cfg1_rows0_8': '918e5a424c249500', 'cfg1_scale': '75b452ba08055122', 'cfg1_points_4096': '42da9f1667686020', 'cfg0_rows': '261e4d3a9b9efbfc'}
 
 
 def test_statistics(synth):
@@ -47,8 +46,6 @@ def test_statistics(synth):
     p = synth.points(c.seed, 4, 1 << 16).astype(np.float64)
     assert np.abs(p.mean(0)).max() < 0.02 and np.abs(p.std(0) - 1).max() < 0.02
     assert abs(np.corrcoef(p.T)[0, 1]) < 0.02
-    eps = synth.signs_from_bits(synth.sign_bits(4096), 4096)
-    assert abs(eps.mean()) < 0.05
     assert [x.n_outlier for x in synth.config(2).matrices] == [20, 55]
     assert sum(x.d_out * x.d_in for x in synth.config(4).matrices) == 12687769600
 

@@ -275,7 +275,7 @@ __global__ __launch_bounds__(MAXT) void k_decode(DecodeArgs a, int T, int R) {
     double cf[E];
 #pragma unroll
     for (int m = 0; m < E; ++m) cf[m] = 1.0;
-    if (a.scale || a.sign) {
+    {
         double* cfl = reinterpret_cast<double*>(smem + (size_t)K * sizeof(double2));
         constexpr int CB = Lo::b > E ? Lo::b : E;
         const int chunk = (int)(blockDim.x / kWave) * DW::dwords / 2 / CB * CB;
@@ -285,19 +285,16 @@ __global__ __launch_bounds__(MAXT) void k_decode(DecodeArgs a, int T, int R) {
         for (int c0 = 0; c0 < a.d_in; c0 += chunk) {
             const int n = min(chunk, a.d_in - c0);
             for (int j = 4 * (int)threadIdx.x; j < n; j += 4 * (int)blockDim.x) {
-                const int col = c0 + j;   // a multiple of 4: the four sign bits share one word
+                const int col = c0 + j;   // a multiple of 4
                 double r[4] = {1.0, 1.0, 1.0, 1.0};
                 if (a.scale) {
                     const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(srs, (uint32_t)col * 4u, 0, 0);
 #pragma unroll
                     for (int u = 0; u < 4; ++u) r[u] = recip((double)__uint_as_float(v[u]));
                 }
-                if (a.sign) {
-                    const uint32_t sw = a.sign[col >> 5] >> (col & 31);
 #pragma unroll
-                    for (int u = 0; u < 4; ++u)
-                        if ((sw >> u) & 1u) r[u] = -r[u];
-                }
+                for (int u = 0; u < 4; ++u)
+                    if (eps_negative(a.sign_seed, (uint32_t)(col + u))) r[u] = -r[u];
                 if (j + 4 <= n) {
                     *reinterpret_cast<double2*>(cfl + j) = make_double2(r[0], r[1]);
                     *reinterpret_cast<double2*>(cfl + j + 2) = make_double2(r[2], r[3]);
@@ -479,6 +476,7 @@ hipError_t decode_LBO(const DecodeArgs& a, hipStream_t st) {
     int R = kMax / T;
     if (R > 4) R = 4;
     if (R > a.d_out) R = a.d_out > 0 ? a.d_out : 1;
+    while (R > 1 && decode_smem<L>(1 << a.bits, R * T / kWave) > kLdsBytes) --R;
     const int threads = R * T;
     const size_t smem = decode_smem<L>(1 << a.bits, threads / kWave);
     if (smem > kLdsBytes) return hipErrorInvalidConfiguration;
@@ -517,6 +515,25 @@ hipError_t decode_L(const DecodeArgs& a, hipStream_t st) {
 }
 
 }  // namespace
+
+size_t decode_lds_bytes(int L, int bits, int d_in) {
+    const int E = lane_elems(L);
+    if (E <= 0) return 0;
+    const int nwaves = ((d_in / E) + kWave - 1) / kWave;
+    switch (L) {
+    case 1: return decode_smem<1>(1 << bits, nwaves);
+    case 2: return decode_smem<2>(1 << bits, nwaves);
+    case 3: return decode_smem<3>(1 << bits, nwaves);
+    case 4: return decode_smem<4>(1 << bits, nwaves);
+    case 5: return decode_smem<5>(1 << bits, nwaves);
+    case 6: return decode_smem<6>(1 << bits, nwaves);
+    case 7: return decode_smem<7>(1 << bits, nwaves);
+    case 8: return decode_smem<8>(1 << bits, nwaves);
+    case 9: return decode_smem<9>(1 << bits, nwaves);
+    case 10: return decode_smem<10>(1 << bits, nwaves);
+    default: return 0;
+    }
+}
 
 hipError_t launch_decode(const DecodeArgs& a, int L, hipStream_t st) {
     switch (L) {

@@ -55,11 +55,11 @@ __device__ __forceinline__ double sqrt_pos(double q) {
 }
 
 // s_j * eps_j of the E consecutive columns tid*E .. tid*E + E - 1 of a lane (phase A), exact in
-// fp32: the scales with 16-byte buffer loads and the E sign bits from one 32-bit word (E >= 16
-// divides 32 or is a multiple of it).  Columns at or past d_in get 1.  bad is set when a scale
-// of the lane is not > 0 (NaN included).
+// fp32: the scales with 16-byte buffer loads, the signs from the seed (once per kernel).
+// Columns at or past d_in get a scale of 1.  bad is set when a scale of the lane is not > 0
+// (NaN included).
 template <int E>
-__device__ __forceinline__ void load_cf(const float* scale, const uint32_t* sign, int tid, int d_in, float (&cf)[E],
+__device__ __forceinline__ void load_cf(const float* scale, uint64_t sign_seed, int tid, int d_in, float (&cf)[E],
                                         bool& bad) {
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     const int j0 = tid * E;
@@ -80,17 +80,9 @@ __device__ __forceinline__ void load_cf(const float* scale, const uint32_t* sign
         if (j0 + m >= d_in) cf[m] = 1.0f;
         bad |= !(cf[m] > 0.0f);
     }
-    if (sign) {
-        static_assert(E >= 16, "lane groups of at least 16 columns");
 #pragma unroll
-        for (int w = 0; w < (E + 31) / 32; ++w) {
-            const int jw = j0 + 32 * w;
-            const uint32_t bits = jw < d_in ? sign[jw >> 5] >> (jw & 31) : 0u;
-#pragma unroll
-            for (int m = 32 * w; m < E && m < 32 * (w + 1); ++m)
-                if ((bits >> (m - 32 * w)) & 1u) cf[m] = -cf[m];
-        }
-    }
+    for (int m = 0; m < E; ++m)
+        if (eps_negative(sign_seed, (uint32_t)(j0 + m))) cf[m] = -cf[m];
 }
 
 // Column of register m of this lane in the final (phase B) layout.
@@ -271,7 +263,7 @@ __global__ __launch_bounds__(MAXT) void k_calibrate(CalibArgs a, int T, int R) {
     if (active && base + grp < a.n_rows) load_raw<E, BF>(a.w, vec, (int64_t)(base + grp) * a.ld + (int64_t)tid * E, nxt);
     float cf[E];   // s_j * eps_j, exact in fp32 (scales are checked by the encoder)
     bool bad_scale = false;
-    load_cf<E>(a.scale, a.sign, tid, a.d_in, cf, bad_scale);
+    load_cf<E>(a.scale, a.sign_seed, tid, a.d_in, cf, bad_scale);
     (void)bad_scale;
     const double inv_sqrt_b = 1.0 / __builtin_sqrt((double)Lo::b);
     double acc[NP];
@@ -468,6 +460,10 @@ __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a, int T, int R) {
         front = polar_lds_bytes(a.bits - a.ba);
     } else {
         const IndexHeader ih = *reinterpret_cast<const IndexHeader*>(index);
+        if (!index_header_ok(ih, K, a.index_g)) {   // uniform over the grid: no workgroup goes on
+            if (blockIdx.x == 0 && threadIdx.x == 0) flag_status(a.status, kFlagBadIndex);
+            return;
+        }
         sl = search_lds_carve(smem, K, ih, index);
         front = search_lds_bytes(K, ih.G);
     }
@@ -504,7 +500,7 @@ __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a, int T, int R) {
 
     float cf[E];   // s_j * eps_j, exact in fp32
     bool bad_scale = false;
-    load_cf<E>(a.scale, a.sign, tid, a.d_in, cf, bad_scale);
+    load_cf<E>(a.scale, a.sign_seed, tid, a.d_in, cf, bad_scale);
     if (active && bad_scale && blockIdx.x == 0) flags |= 2;   // reported once
 #pragma unroll
     for (int m = 0; m < E; ++m) pin_reg(cf[m]);
@@ -600,7 +596,7 @@ __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a, int T, int R) {
                 nh = __half_as_ushort(hv);
                 if (tid == 0 && (nh & 0x7FFF) == 0x7C00) rf |= 4;
             }
-            __builtin_amdgcn_raw_buffer_store_b16(nh, nrs, tid == 0 ? (uint32_t)row * 2u : 0x7FFFFFF0u, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b16(nh, nrs, tid == 0 ? (uint32_t)row * 2u : kNoByte, 0, 0);
         }
         if (rv) flags |= rf;
         wave_lds_sync();
@@ -627,7 +623,7 @@ __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a, int T, int R) {
         for (int u = 0; u < NCH; ++u) {
             const int c = lane + u * kWave;
             const u32x4 q = *reinterpret_cast<const u32x4*>(wstage + 4 * min(c, nchunks - 1));
-            __builtin_amdgcn_raw_buffer_store_b128(q, crs, c < nchunks ? wave_byte0 + (uint32_t)c * 16u : 0x7FFFFFF0u, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(q, crs, c < nchunks ? wave_byte0 + (uint32_t)c * 16u : kNoByte, 0, 0);
         }
         wave_lds_sync();   // the staged words are read before the next front end reuses the buffer
     }
@@ -794,6 +790,24 @@ size_t encode_lds_bytes(int L, int bits, int d_in, int polar_bp) {
     const int nwaves = ((d_in / E) + kWave - 1) / kWave;
     const size_t front = polar_bp >= 1 ? polar_lds_bytes(polar_bp) : search_lds_bytes(1 << bits, index_grid_size(bits));
     return front + 2 * kMaxWaves * sizeof(double) + (size_t)nwaves * encode_wave_bytes(E, L > 4, bits);
+}
+
+namespace {
+// Bit j % 32 of word j / 32 is set when eps_j = -1 (the mask the kernels draw from the seed).
+__global__ __launch_bounds__(256) void k_sign_mask(uint64_t seed, int d_in, uint32_t* __restrict__ out) {
+    const int w = blockIdx.x * blockDim.x + threadIdx.x;
+    if (w * 32 >= d_in) return;
+    uint32_t v = 0;
+    for (int t = 0; t < 32 && w * 32 + t < d_in; ++t)
+        if (eps_negative(seed, (uint32_t)(w * 32 + t))) v |= 1u << t;
+    out[w] = v;
+}
+}  // namespace
+
+hipError_t launch_sign_mask(uint64_t seed, int d_in, uint32_t* bits, hipStream_t st) {
+    const int words = (d_in + 31) / 32;
+    hipLaunchKernelGGL(k_sign_mask, dim3((words + 255) / 256), dim3(256), 0, st, seed, d_in, bits);
+    return hipGetLastError();
 }
 
 int calib_groups(int n_rows) { return n_rows < kCalibMaxGroups ? n_rows : kCalibMaxGroups; }

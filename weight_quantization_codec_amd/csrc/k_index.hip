@@ -391,9 +391,16 @@ hipError_t launch_index_build(const float* cb, int bits, void* index, hipStream_
 namespace {
 
 __global__ __launch_bounds__(256) void k_nearest(const float* __restrict__ pts, int64_t n, const float* __restrict__ cb,
-                                                 int K, const char* __restrict__ index, int32_t* __restrict__ out) {
+                                                 int K, int G, const char* __restrict__ index,
+                                                 int32_t* __restrict__ out) {
     extern __shared__ __align__(16) char smem[];
-    SearchLds s = search_lds_carve(smem, K, *reinterpret_cast<const IndexHeader*>(index), index);
+    const IndexHeader ih = *reinterpret_cast<const IndexHeader*>(index);
+    if (!index_header_ok(ih, K, G)) {   // an index of another codebook size: every answer is -1
+        for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+            out[i] = -1;
+        return;
+    }
+    SearchLds s = search_lds_carve(smem, K, ih, index);
     search_lds_fill(s, index, K, threadIdx.x, blockDim.x);
     __syncthreads();
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
@@ -410,9 +417,10 @@ hipError_t launch_nearest(const float* pts, int64_t n, const float* cb, int bits
     int64_t blocks = (n + 255) / 256;
     if (blocks > 2048) blocks = 2048;
     if (blocks < 1) return hipSuccess;
-    const size_t smem = search_lds_bytes(K, index_grid_size(bits));
+    const int G = index_grid_size(bits);
+    const size_t smem = search_lds_bytes(K, G);
     allow_lds(k_nearest, smem);
-    hipLaunchKernelGGL(k_nearest, dim3((unsigned)blocks), dim3(256), smem, st, pts, n, cb, K,
+    hipLaunchKernelGGL(k_nearest, dim3((unsigned)blocks), dim3(256), smem, st, pts, n, cb, K, G,
                        reinterpret_cast<const char*>(index), out);
     return hipGetLastError();
 }

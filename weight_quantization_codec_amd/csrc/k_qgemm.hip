@@ -43,7 +43,7 @@ constexpr int kQgMaxTile = 4;           // m-tile rows x passes held in LDS
 //              component e, row m goes to ((c * 8 + s / 4) * 64 + (2 h + e) * 16 + m) * 4 + s % 4.
 __global__ __launch_bounds__(1024) void k_qgemm_rotate(const void* __restrict__ x, int x_bf16, int64_t ld_x, int M,
                                                        int d_in, int cols, int b, const float* __restrict__ s,
-                                                       const uint32_t* __restrict__ sign,
+                                                       uint64_t sign_seed,
                                                        const float* __restrict__ sigma, float* __restrict__ u,
                                                        int frag) {
     extern __shared__ double buf[];
@@ -55,7 +55,7 @@ __global__ __launch_bounds__(1024) void k_qgemm_rotate(const void* __restrict__ 
         const float xv = x_bf16 ? bf16_bits_to_float(reinterpret_cast<const uint16_t*>(x)[(size_t)m * ld_x + col])
                                 : reinterpret_cast<const float*>(x)[(size_t)m * ld_x + col];
         const double sc = s ? (double)s[col] : 1.0;
-        const bool neg = sign && ((sign[col >> 5] >> (col & 31)) & 1u);
+        const bool neg = eps_negative(sign_seed, (uint32_t)col);
         v = (neg ? -(double)xv : (double)xv) / sc;
     }
     buf[tid] = v;
@@ -452,7 +452,7 @@ hipError_t launch_qgemm(const QgemmArgs& a0, const QgemmRotateArgs& r, hipStream
     const int T = r.block > 256 ? r.block : 256;
     const int cols = mfma ? (r.d_in / 2 + 63) / 64 * 128 : r.d_in;
     hipLaunchKernelGGL(k_qgemm_rotate, dim3((cols + T - 1) / T, mfma ? 16 : a.M), dim3(T), (size_t)T * sizeof(double),
-                       st, r.x, r.x_bf16, r.ld_x, a.M, r.d_in, cols, r.block, r.scale, r.sign, r.sigma, a.u,
+                       st, r.x, r.x_bf16, r.ld_x, a.M, r.d_in, cols, r.block, r.scale, r.sign_seed, r.sigma, a.u,
                        mfma ? 1 : 0);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
 #define QAMW_QG(b) \

@@ -48,7 +48,7 @@ namespace {
 // The encoder common to QAM-W and the polar baseline: thr == nullptr selects the QAM-W search
 // (d_codebook, d_index), else the polar quantizer (ba magnitude bits, thresholds thr).
 int encode_common(const void* d_w, qamw_dtype w_dtype, int32_t d_out, int32_t d_in, int64_t ld_w,
-                  const float* d_scale, const uint32_t* d_sign_bits, int32_t block, const float* d_codebook,
+                  const float* d_scale, int32_t block, uint64_t sign_seed, const float* d_codebook,
                   int32_t bits, const void* d_index, const double* thr, int32_t ba, const float* d_sigma_in,
                   float* d_sigma_out, uint16_t* d_norm_f16, uint8_t* d_codes, int32_t* d_status, void* d_ws,
                   size_t ws_bytes, void* stream) {
@@ -80,7 +80,7 @@ int encode_common(const void* d_w, qamw_dtype w_dtype, int32_t d_out, int32_t d_
         c.d_in = d_in;
         c.ld = ld_w;
         c.scale = d_scale;
-        c.sign = d_sign_bits;
+        c.sign_seed = sign_seed;
         c.n_groups = calib_groups(c.n_rows);
         const size_t part_bytes = (size_t)(c.n_groups > 0 ? c.n_groups : 1) * (size_t)(d_in / 2) * sizeof(double);
         c.partial = reinterpret_cast<double*>(d_ws);
@@ -101,11 +101,12 @@ int encode_common(const void* d_w, qamw_dtype w_dtype, int32_t d_out, int32_t d_
     a.d_in = d_in;
     a.ld = ld_w;
     a.scale = d_scale;
-    a.sign = d_sign_bits;
+    a.sign_seed = sign_seed;
     a.sigma = sigma;
     a.cb = d_codebook;
     a.bits = bits;
     a.index = d_index;
+    a.index_g = index_grid_size(bits);
     a.thr = thr;
     a.ba = ba;
     a.norm = d_norm_f16;
@@ -188,10 +189,10 @@ int qamw_nearest(const float* d_points, int64_t n, const float* d_codebook, int3
 }
 
 int qamw_encode(const void* d_w, qamw_dtype w_dtype, int32_t d_out, int32_t d_in, int64_t ld_w, const float* d_scale,
-                const uint32_t* d_sign_bits, int32_t block, const float* d_codebook, int32_t bits, const void* d_index,
+                int32_t block, uint64_t sign_seed, const float* d_codebook, int32_t bits, const void* d_index,
                 const float* d_sigma_in, float* d_sigma_out, uint16_t* d_norm_f16, uint8_t* d_codes,
                 int32_t* d_status, void* d_ws, size_t ws_bytes, void* stream) {
-    return encode_common(d_w, w_dtype, d_out, d_in, ld_w, d_scale, d_sign_bits, block, d_codebook, bits, d_index,
+    return encode_common(d_w, w_dtype, d_out, d_in, ld_w, d_scale, block, sign_seed, d_codebook, bits, d_index,
                          nullptr, 0, d_sigma_in, d_sigma_out, d_norm_f16, d_codes, d_status, d_ws, ws_bytes, stream);
 }
 
@@ -202,7 +203,7 @@ size_t qamw_qgemm_workspace(int32_t M, int32_t d_out, int32_t d_in) {
 
 int qamw_qgemm(const void* d_x, qamw_dtype x_dtype, int32_t M, int64_t ld_x, const uint8_t* d_codes,
                const uint16_t* d_norm_f16, const float* d_sigma, const float* d_codebook, int32_t bits,
-               const float* d_scale, const uint32_t* d_sign_bits, int32_t d_out, int32_t d_in, int32_t block,
+               const float* d_scale, int32_t d_out, int32_t d_in, int32_t block, uint64_t sign_seed,
                void* d_y, qamw_dtype y_dtype, int64_t ld_y, void* d_ws, size_t ws_bytes, void* stream) {
     if (M < 0 || d_out < 0 || (x_dtype != QAMW_F32 && x_dtype != QAMW_BF16) ||
         (y_dtype != QAMW_F32 && y_dtype != QAMW_BF16))
@@ -242,7 +243,7 @@ int qamw_qgemm(const void* d_x, qamw_dtype x_dtype, int32_t M, int64_t ld_x, con
     r.d_in = d_in;
     r.block = b;
     r.scale = d_scale;
-    r.sign = d_sign_bits;
+    r.sign_seed = sign_seed;
     r.sigma = d_sigma;
     return hip_rc(launch_qgemm(a, r, (hipStream_t)stream));
 }
@@ -296,21 +297,21 @@ int qamw_polar_index(const float* d_points, int64_t n, int32_t ba, int32_t bp, c
 }
 
 int qamw_encode_polar(const void* d_w, qamw_dtype w_dtype, int32_t d_out, int32_t d_in, int64_t ld_w,
-                      const float* d_scale, const uint32_t* d_sign_bits, int32_t block, int32_t ba, int32_t bp,
+                      const float* d_scale, int32_t block, uint64_t sign_seed, int32_t ba, int32_t bp,
                       const double* d_thresholds, const float* d_sigma_in, float* d_sigma_out,
                       uint16_t* d_norm_f16, uint8_t* d_codes, int32_t* d_status, void* d_ws, size_t ws_bytes,
                       void* stream) {
     int rc = check_polar_bits(ba, bp);
     if (rc) return rc;
     if (!d_thresholds) return QAMW_ERR_ARG;
-    return encode_common(d_w, w_dtype, d_out, d_in, ld_w, d_scale, d_sign_bits, block, nullptr, ba + bp, nullptr,
+    return encode_common(d_w, w_dtype, d_out, d_in, ld_w, d_scale, block, sign_seed, nullptr, ba + bp, nullptr,
                          d_thresholds, ba, d_sigma_in, d_sigma_out, d_norm_f16, d_codes, d_status, d_ws, ws_bytes,
                          stream);
 }
 
 int qamw_decode(const uint8_t* d_codes, const uint16_t* d_norm_f16, const float* d_sigma, const float* d_codebook,
-                int32_t bits, const float* d_scale, const uint32_t* d_sign_bits, int32_t d_out, int32_t d_in,
-                int32_t block, void* d_out_w, qamw_dtype out_dtype, int64_t ld_out, void* stream) {
+                int32_t bits, const float* d_scale, int32_t d_out, int32_t d_in, int32_t block, uint64_t sign_seed,
+                void* d_out_w, qamw_dtype out_dtype, int64_t ld_out, void* stream) {
     if (d_out < 0 || (out_dtype != QAMW_F32 && out_dtype != QAMW_BF16)) return QAMW_ERR_ARG;
     if (d_out > QAMW_MAX_ROWS) return QAMW_ERR_UNSUPPORTED;
     int L = check_shape(d_in, block);
@@ -318,6 +319,7 @@ int qamw_decode(const uint8_t* d_codes, const uint16_t* d_norm_f16, const float*
     int rc = check_bits(bits);
     if (rc) return rc;
     if (ld_out < d_in || (ld_out & 1)) return QAMW_ERR_ARG;
+    if (decode_lds_bytes(L, bits, d_in) > kLdsBytes) return QAMW_ERR_UNSUPPORTED;
     if (d_out == 0) return QAMW_OK;
     if (!d_codes || !d_norm_f16 || !d_sigma || !d_codebook || !d_out_w) return QAMW_ERR_ARG;
     if (!aligned(d_codebook, 8) || !aligned(d_codes, 4) || !aligned(d_norm_f16, 2) ||
@@ -331,13 +333,20 @@ int qamw_decode(const uint8_t* d_codes, const uint16_t* d_norm_f16, const float*
     a.cb = d_codebook;
     a.bits = bits;
     a.scale = d_scale;
-    a.sign = d_sign_bits;
+    a.sign_seed = sign_seed;
     a.d_out = d_out;
     a.d_in = d_in;
     a.out = d_out_w;
     a.out_bf16 = out_dtype == QAMW_BF16;
     a.ld = ld_out;
     return hip_rc(launch_decode(a, L, (hipStream_t)stream));
+}
+
+int qamw_sign_mask(uint64_t sign_seed, int32_t d_in, uint32_t* d_bits, void* stream) {
+    if (d_in < 0) return QAMW_ERR_ARG;
+    if (d_in == 0) return QAMW_OK;
+    if (!d_bits || !aligned(d_bits, 4)) return QAMW_ERR_ARG;
+    return hip_rc(launch_sign_mask(sign_seed, d_in, d_bits, (hipStream_t)stream));
 }
 
 const char* qamw_status_string(int code) {

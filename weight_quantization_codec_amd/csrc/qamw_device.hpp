@@ -18,6 +18,11 @@ namespace qamw {
 
 constexpr int kWave = 64;
 
+// A buffer offset past the byte range of every buffer descriptor the library builds (those cover
+// fewer than 2^31 bytes), with room for small offsets to be added without wrapping: loads through
+// it return 0 and stores are dropped.
+constexpr uint32_t kNoByte = 0x80000000u;
+
 // Search-index layout (bytes from the start of the index buffer written by qamw_codebook_index).
 constexpr int kIndexFine = 2048;                          // W: fine bins per axis
 constexpr int kIndexFineMax = 2048;
@@ -53,6 +58,12 @@ __host__ __device__ constexpr int index_lds_entries(int K) {
 }
 
 __host__ __device__ constexpr size_t align16(size_t v) { return (v + 15) & ~(size_t)15; }
+
+// An index buffer fits the codebook size it is used with: built for K codewords on a G x G grid
+// (G as the host computes it for that K), so the LDS image the kernels size and fill matches.
+__host__ __device__ inline bool index_header_ok(const IndexHeader& ih, int K, int G) {
+    return ih.K == K && ih.G == G && ih.W == kIndexFine && ih.n_entries >= 0;
+}
 
 // LDS image of the codebook and its index used by the search.
 struct SearchLds {
@@ -123,6 +134,19 @@ __device__ __forceinline__ void butterfly(double (&x)[E], int rbit) {
 template <typename T>
 __device__ __forceinline__ void pin_reg(T& v) {
     asm volatile("" : "+v"(v));
+}
+
+// Sign mask of the rotation (paper section 3.3: a deterministic sign per input column, shared by
+// every row).  eps_j = -1 exactly when the top bit of the (j+1)-th output of the splitmix64
+// generator started at `seed` is set; that output is the published splitmix64 finalizer (Steele,
+// Lea and Flood, OOPSLA 2014; the constants of Vigna's reference code) applied to
+// seed + (j+1) * 0x9E3779B97F4A7C15, all arithmetic modulo 2^64.  The last xor-shift of the
+// finalizer leaves the top bit unchanged, so it is not computed.
+__host__ __device__ __forceinline__ bool eps_negative(uint64_t seed, uint32_t j) {
+    uint64_t z = seed + (uint64_t)(j + 1u) * 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return (z >> 63) != 0;
 }
 
 // Make LDS writes of this wavefront visible to its other lanes before the reads that follow.
@@ -568,6 +592,9 @@ __device__ __forceinline__ void polar_batch(const float (&px)[NB], const float (
 __device__ __forceinline__ float bf16_bits_to_float(uint16_t h) {
     return __uint_as_float((uint32_t)h << 16);
 }
+
+// QAMW_FLAG_BAD_INDEX of qamw.h: the search index was built for another codebook size.
+constexpr int32_t kFlagBadIndex = 32;
 
 __device__ __forceinline__ void flag_status(int32_t* status, int32_t f) {
     if (status && f) atomicOr(status, f);

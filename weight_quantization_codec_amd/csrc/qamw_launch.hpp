@@ -27,11 +27,12 @@ struct EncodeArgs {
     int d_out, d_in;
     int64_t ld;
     const float* scale;        // may be null (all ones)
-    const uint32_t* sign;      // may be null (all +1)
+    uint64_t sign_seed;        // sign mask eps_j (eps_negative)
     const float* sigma;        // d_in/2
     const float* cb;
     int bits;
     const void* index;
+    int index_g;               // grid size the index of a 2^bits codebook has (checked on the device)
     const double* thr;         // polar baseline: ba bits of magnitude (thresholds) and bits - ba of phase
     int ba;
     uint16_t* norm;
@@ -46,7 +47,7 @@ struct CalibArgs {
     int n_rows, d_in;
     int64_t ld;
     const float* scale;
-    const uint32_t* sign;
+    uint64_t sign_seed;
     double* partial;           // [n_groups][d_in/2]
     int32_t* nz;               // [n_groups]
     int n_groups;
@@ -60,7 +61,7 @@ struct DecodeArgs {
     const float* cb;
     int bits;
     const float* scale;
-    const uint32_t* sign;
+    uint64_t sign_seed;
     int d_out, d_in;
     void* out;
     int out_bf16;
@@ -79,6 +80,9 @@ size_t calib_workspace(int d_out, int d_in);
 hipError_t launch_calibrate(const CalibArgs& a, int L, float* sigma_out, hipStream_t st);
 hipError_t launch_encode(const EncodeArgs& a, int L, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, int L, hipStream_t st);
+// Smallest LDS the decoder needs for a row of d_in columns (one row per workgroup).
+size_t decode_lds_bytes(int L, int bits, int d_in);
+hipError_t launch_sign_mask(uint64_t seed, int d_in, uint32_t* bits, hipStream_t st);
 hipError_t launch_polar_codebook(int ba, int bp, double* levels, double* thr, float* cb, hipStream_t st);
 hipError_t launch_scalar_codebook(int b, double* levels, double* thr, float* cb, hipStream_t st);
 int act_chunks(int64_t T);
@@ -108,7 +112,7 @@ struct QgemmRotateArgs {
     int64_t ld_x;
     int d_in, block;
     const float* scale;
-    const uint32_t* sign;
+    uint64_t sign_seed;
     const float* sigma;
 };
 struct QgemmPlan {
