@@ -140,7 +140,9 @@ int qamw_nearest(const float* d_points, int64_t n, const float* d_codebook, int3
  *                  consecutive columns (E = 16 for b <= 128, 32 for b = 256 or 512, 64 for
  *                  b = 1024): d_in must be a multiple of E and d_in / E at most 1024 (E = 16)
  *                  or 512 (E = 32, 64), i.e. d_in <= 16384, 16384 and 32768; otherwise
- *                  QAMW_ERR_UNSUPPORTED.
+ *                  QAMW_ERR_UNSUPPORTED.  At b = 1024 with bits >= 11 the decoder's LDS bounds
+ *                  d_in to 28672; encode and decode reject wider rows alike
+ *                  (QAMW_ERR_UNSUPPORTED), so whatever is encoded can be decoded.
  *   sign_seed      seed of the sign mask.
  *   d_codebook, bits, d_index   K = 2^bits codebook and its index; 1 <= bits <= 12.  The index
  *                  argument is not in the problem statement of the pages: it is built once per
@@ -175,6 +177,32 @@ int qamw_decode(const uint8_t* d_codes, const uint16_t* d_norm_f16, const float*
                 const float* d_codebook, int32_t bits, const float* d_scale,
                 int32_t d_out, int32_t d_in, int32_t block, uint64_t sign_seed,
                 void* d_out_w, qamw_dtype out_dtype, int64_t ld_out, void* stream);
+
+/* One matrix of qamw_decode_many: the per-matrix arguments of qamw_decode. */
+typedef struct {
+    const uint8_t* d_codes;
+    const uint16_t* d_norm_f16;
+    const float* d_sigma;
+    const float* d_scale;     /* NULL for all ones */
+    int32_t d_out;
+    int32_t d_in;
+    uint64_t sign_seed;
+    void* d_out_w;
+    int64_t ld_out;
+} qamw_decode_job;
+
+/* Section 3.2 and section 1 for the matrices of a model (the pages quantize every linear layer with
+ * the one codebook): each job is decoded exactly as qamw_decode decodes it, with the shared
+ * d_codebook, bits, block and out_dtype.  Jobs at block 128 (block 0 with 128 the default counts)
+ * and bits 7, 8 or 11 are decoded by grouped launches of up to 48 matrices each, which start one
+ * matrix while the previous one finishes; other jobs get a launch each.  The results equal those
+ * of qamw_decode bit for bit.
+ *   jobs     host array of n_jobs entries, read during the call only; n_jobs >= 0 (0 is a no-op).
+ * Every job is checked as qamw_decode checks its arguments before anything is queued: the first
+ * failing job's error is returned and nothing is queued.  Outputs must not overlap each other or
+ * any input (the jobs run concurrently). */
+int qamw_decode_many(const qamw_decode_job* jobs, int32_t n_jobs, const float* d_codebook, int32_t bits,
+                     int32_t block, qamw_dtype out_dtype, void* stream);
 
 /* Section 3.3: the sign mask of a seed as bits, for callers and tests that need eps itself: bit
  * j % 32 of d_bits[j / 32] is set when eps_j = -1 (j < d_in); the bits of the last word past d_in

@@ -22,7 +22,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = q.header_symbols()
-    assert len(names) == 20
+    assert len(names) == 21
     out = subprocess.run(["nm", "-D", "--defined-only", q.LIB_PATH], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
     for n in names:
@@ -87,6 +87,8 @@ def _dec(lib, **kw):
     (dict(d_in=16384 + 256, ld=16384 + 256, block=64), UNSUP), (dict(d_in=16384 + 256, ld=16640, block=256), UNSUP),
     (dict(d_in=24, ld=24, block=8), UNSUP), (dict(d_in=8, ld=8, block=8), UNSUP),
     (dict(d_out=1 << 30), UNSUP), (dict(d_out=2**31 - 1), UNSUP),
+    # rows the decoder's LDS cannot hold at b = 1024 and K >= 2048: rejected by encode as well
+    (dict(d_in=32768, ld=32768, block=1024, bits=11), UNSUP), (dict(d_in=29696, ld=29696, block=1024, bits=12), UNSUP),
 ])
 def test_encode_rejects(lib, kw, code):
     assert _enc(lib, **kw) == code
@@ -97,6 +99,7 @@ def test_encode_rejects(lib, kw, code):
     (dict(bits=14), UNSUP), (dict(bits=0), ARG), (dict(codes=None), ARG), (dict(out=FAKE + 2), ARG),
     (dict(out=FAKE + 4, dt=q.F32), ARG), (dict(sigma=None), ARG), (dict(d_out=-3), ARG),
     (dict(d_in=40, ld=40, block=8), UNSUP), (dict(d_out=1 << 30), UNSUP),
+    (dict(d_in=32768, ld=32768, block=1024, bits=11), UNSUP),
 ])
 def test_decode_rejects(lib, kw, code):
     assert _dec(lib, **kw) == code
@@ -104,6 +107,35 @@ def test_decode_rejects(lib, kw, code):
 
 def test_empty_decode_is_a_noop(lib):
     assert _dec(lib, d_out=0, codes=None, norm=None, sigma=None, cb=None, out=None) == q.OK
+
+
+def _job(**kw):
+    a = dict(d_codes=FAKE, d_norm_f16=FAKE, d_sigma=FAKE, d_scale=None, d_out=16, d_in=256,
+             sign_seed=q.DEFAULT_SIGN_SEED, d_out_w=FAKE, ld_out=256)
+    a.update(kw)
+    return q.DecodeJob(**a)
+
+
+def _many(lib, jobs, bits=8, block=128, dt=q.BF16, cb=FAKE):
+    arr = (q.DecodeJob * max(1, len(jobs)))(*jobs)
+    return lib.qamw_decode_many(ctypes.cast(arr, ctypes.c_void_p), len(jobs), cb, bits, block, dt, None)
+
+
+def test_decode_many_checks_every_job_before_queueing(lib):
+    assert ctypes.sizeof(q.DecodeJob) == 64
+    assert lib.qamw_decode_many(None, 0, FAKE, 8, 128, q.BF16, None) == q.OK
+    assert lib.qamw_decode_many(None, 2, FAKE, 8, 128, q.BF16, None) == ARG
+    assert lib.qamw_decode_many(None, -1, FAKE, 8, 128, q.BF16, None) == ARG
+    # the first job would launch if it were alone: the later failing job returns its error first
+    # (a launch with these placeholder pointers would fail as a HIP error on a machine without a GPU)
+    assert _many(lib, [_job(), _job(d_in=255)]) == ARG
+    assert _many(lib, [_job(), _job(ld_out=128)]) == ARG
+    assert _many(lib, [_job(), _job(d_codes=FAKE + 2)]) == ARG
+    assert _many(lib, [_job(), _job(d_out=1 << 30)]) == UNSUP
+    assert _many(lib, [_job(), _job()], bits=13) == UNSUP
+    assert _many(lib, [_job(), _job()], dt=5) == ARG
+    assert _many(lib, [_job(), _job()], cb=None) == ARG
+    assert _many(lib, [_job(d_out=0, d_codes=None, d_norm_f16=None, d_sigma=None, d_out_w=None)]) == q.OK
 
 
 def test_train_and_index_reject(lib):
@@ -287,3 +319,14 @@ def test_binding_rejects_short_or_mistyped_buffers(lib):
     _bad(q.nearest, "index", torch.zeros((4, 2)), cb, bits, index[:10])
     _bad(q.nearest, "pairs", torch.zeros((5,)), cb, bits, index)
     _bad(q.codebook_train, "init", torch.zeros((1024, 2)), bits, 3, init=cb[:10])
+
+
+def test_encode_and_decode_accept_the_same_wide_rows(lib):
+    """Every (d_in, block, bits) the encoder accepts, the decoder accepts (checked on the host
+    rules alone, with d_out = 0 so nothing is launched)."""
+    for block in (128, 256, 512, 1024):
+        for bits in (7, 8, 11, 12):
+            for d_in in range(block, 32768 + 1, block if block >= 1024 else 4 * block):
+                e = _enc(lib, d_out=0, d_in=d_in, ld=d_in, block=block, bits=bits, w=None, codes=None, norm=None)
+                d = _dec(lib, d_out=0, d_in=d_in, ld=d_in, block=block, bits=bits)
+                assert (e == q.OK) == (d == q.OK), (d_in, block, bits, e, d)

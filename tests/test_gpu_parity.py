@@ -103,6 +103,11 @@ SHAPES = [  # d_out, d_in, block, bits
     (3, 13824, 128, 11), (4, 11008, 256, 11), (6, 5120, 128, 7), (7, 192, 4, 9), (11, 96, 8, 6),
     # the widest rows the kernels take: 1024 lanes of 16 columns, 512 of 32, 512 of 64
     (2, 16384, 128, 11), (3, 16384, 512, 12), (2, 32768, 1024, 8),
+    # b = 1024 with 11- and 12-bit indices on wide rows (the decoder's LDS limit; block 0 picks 1024
+    # for 5120 columns)
+    (8, 5120, 0, 11), (4, 16384, 1024, 12), (2, 28672, 1024, 11),
+    # the 128-column decoder: ragged 16-row tiles, one and three column blocks, every supported width
+    (17, 128, 128, 11), (33, 384, 128, 8), (100, 1280, 128, 7), (47, 2560, 128, 11),
 ]
 
 
@@ -117,15 +122,18 @@ def test_decode_crossfed(q, orc, shape):
     sb = orc.sign_mask(seed, d_in)
     w[min(2, d_out - 1)] = 0
     cb = rand_cb(bits, bits)
-    sigma, _ = orc.calibrate(w, s, sb, block)
-    enc = orc.encode(w, s, sb, block, cb, bits, sigma, want_idx=False)
-    ref = orc.decode(enc["codes"], enc["norm"], d_in, sigma, cb, bits, s, sb, block)
+    ob = block or orc.default_block(d_in)   # block 0: the library applies the section 3.3 rule
+    sigma, _ = orc.calibrate(w, s, sb, ob)
+    enc = orc.encode(w, s, sb, ob, cb, bits, sigma, want_idx=False)
+    ref = orc.decode(enc["codes"], enc["norm"], d_in, sigma, cb, bits, s, sb, ob)
     log("decode %s" % (shape,))
     got16 = gpu_decode(q, enc["codes"], enc["norm"], sigma, cb, bits, s, seed, d_in, block)
     n_diff = assert_bf16_within_1ulp(got16, ref["bf16"])
     got32 = gpu_decode(q, enc["codes"], enc["norm"], sigma, cb, bits, s, seed, d_in, block, out_dtype=torch.float32)
     assert_rel_l2(got32, ref["f32"], 1e-5)
-    assert n_diff <= max(2, got16.size // 100000)
+    # every output is within one BF16 ulp (checked above); the 128-column decoder holds eps_j / s_j
+    # in fp32, which moves about 5e-5 of the outputs across a BF16 rounding boundary
+    assert n_diff <= max(4, got16.size // 2000)
     assert not got16[min(2, d_out - 1)].any()
 
 
@@ -150,12 +158,13 @@ def _encode_case(q, orc, shape, dtype="bf16", given_sigma=False, ld=None, seed=0
     sb = orc.sign_mask(sseed, d_in)
     w[min(1, d_out - 1)] = 0
     cb = rand_cb(bits + 50, bits)
-    sig_ref, st_ref = orc.calibrate(w[:1024], s, sb, block)
+    ob = block or orc.default_block(d_in)   # block 0: the library applies the section 3.3 rule
+    sig_ref, st_ref = orc.calibrate(w[:1024], s, sb, ob)
     sigma_in = None
     if given_sigma:
         sig_ref = (np.abs(np.random.default_rng(seed).standard_normal(d_in // 2)) * 0.05 + 0.01).astype(np.float32)
         sigma_in = sig_ref
-    ref = orc.encode(w, s, sb, block, cb, bits, sig_ref, want_p=True)
+    ref = orc.encode(w, s, sb, ob, cb, bits, sig_ref, want_p=True)
     log("encode %s %s sigma=%s ld=%s" % (shape, dtype, "given" if given_sigma else "calibrated", ld))
     got = gpu_encode(q, w, s, sseed, block, cb, bits, sigma=sigma_in, ld=ld)
     np.testing.assert_array_equal(got["sigma"], sig_ref)
@@ -195,7 +204,7 @@ def test_roundtrip_gpu_encode_gpu_decode(q, orc, shape):
     whatever near-tie flips the encode had."""
     d_out, d_in, block, bits = shape
     got, ref, cb, sigma, s, sseed, sb = _encode_case(q, orc, shape, seed=3)
-    dec_ref = orc.decode(got["codes"], got["norm"], d_in, sigma, cb, bits, s, sb, block)
+    dec_ref = orc.decode(got["codes"], got["norm"], d_in, sigma, cb, bits, s, sb, block or orc.default_block(d_in))
     dec = gpu_decode(q, got["codes"], got["norm"], got["sigma"], cb, bits, s, sseed, d_in, block)
     assert_bf16_within_1ulp(dec, dec_ref["bf16"])
     dec32 = gpu_decode(q, got["codes"], got["norm"], got["sigma"], cb, bits, s, sseed, d_in, block,

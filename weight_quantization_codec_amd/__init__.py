@@ -62,6 +62,7 @@ def load(path: Optional[str] = None):
         "qamw_encode": ([vp, ctypes.c_int, i32, i32, i64, vp, i32, u64, vp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp],
                         ctypes.c_int),
         "qamw_decode": ([vp, vp, vp, vp, i32, vp, i32, i32, i32, u64, vp, ctypes.c_int, i64, vp], ctypes.c_int),
+        "qamw_decode_many": ([vp, i32, vp, i32, i32, ctypes.c_int, vp], ctypes.c_int),
         "qamw_sign_mask": ([u64, i32, vp, vp], ctypes.c_int),
         "qamw_qgemm_workspace": ([i32, i32, i32], sz),
         "qamw_qgemm": ([vp, ctypes.c_int, i32, i64, vp, vp, vp, vp, i32, vp, i32, i32, i32, u64, vp, ctypes.c_int, i64,
@@ -307,6 +308,56 @@ def _decode_inputs(codes, norm, sigma, codebook, bits, d_in, scale):
     _arg(codebook, "codebook", torch.float32, numel=2 << bits)
     _arg(scale, "scale", torch.float32, numel=d_in, optional=True)
     return d_out
+
+
+class DecodeJob(ctypes.Structure):
+    """qamw_decode_job of include/qamw.h."""
+    _fields_ = [("d_codes", ctypes.c_void_p), ("d_norm_f16", ctypes.c_void_p), ("d_sigma", ctypes.c_void_p),
+                ("d_scale", ctypes.c_void_p), ("d_out", ctypes.c_int32), ("d_in", ctypes.c_int32),
+                ("sign_seed", ctypes.c_uint64), ("d_out_w", ctypes.c_void_p), ("ld_out", ctypes.c_int64)]
+
+
+class DecodeManyPlan:
+    """A checked qamw_decode_many call, launched by calling it: the job table is built once, so
+    repeated launches (a model's weights decoded again and again) cost no per-job Python work.
+    jobs: sequence of dicts with codes, norm, sigma, d_in and optionally scale, sign_seed and out
+    (allocated when absent).  The tensors are held until the plan is dropped."""
+
+    def __init__(self, jobs, codebook: torch.Tensor, bits: int, block: int = 0, out_dtype=torch.bfloat16):
+        if out_dtype not in (torch.bfloat16, torch.float32):
+            raise ValueError("out_dtype must be bfloat16 or float32")
+        self.outs, self._keep = [], [codebook]
+        self._arr = (DecodeJob * max(1, len(jobs)))()
+        for k, j in enumerate(jobs):
+            codes, norm, sigma, d_in = j["codes"], j["norm"], j["sigma"], j["d_in"]
+            scale = j.get("scale")
+            d_out = _decode_inputs(codes, norm, sigma, codebook, bits, d_in, scale)
+            out = j.get("out")
+            if out is None:
+                out = torch.empty((d_out, d_in), dtype=out_dtype, device=codes.device)
+            if out.dtype != out_dtype:
+                raise ValueError("job %d: out must be %s" % (k, out_dtype))
+            ld_out = _matrix(out, "out", rows=d_out, cols=d_in)
+            _on_device(codes=codes, norm=norm, sigma=sigma, codebook=codebook, scale=scale, out=out)
+            self._arr[k] = DecodeJob(_ptr(codes), _ptr(norm), _ptr(sigma), _ptr(scale), d_out, d_in,
+                                     j.get("sign_seed", DEFAULT_SIGN_SEED), _ptr(out), ld_out)
+            self._keep += [codes, norm, sigma, scale]
+            self.outs.append(out)
+        self._n, self._cb, self._bits, self._block = len(jobs), _ptr(codebook), bits, block
+        self._dt = BF16 if out_dtype == torch.bfloat16 else F32
+        self._lib = load()
+
+    def __call__(self, stream=None) -> list:
+        rc = self._lib.qamw_decode_many(ctypes.addressof(self._arr), self._n, self._cb, self._bits, self._block,
+                                        self._dt, _stream(stream))
+        _check(rc, "qamw_decode_many")
+        return self.outs
+
+
+def decode_many(jobs, codebook: torch.Tensor, bits: int, block: int = 0, out_dtype=torch.bfloat16) -> list:
+    """Decode several matrices coded with one codebook (qamw_decode_many); returns the outputs in
+    job order.  See DecodeManyPlan for the job fields."""
+    return DecodeManyPlan(jobs, codebook, bits, block, out_dtype)()
 
 
 def qgemm_workspace(M: int, d_out: int, d_in: int) -> int:

@@ -1,5 +1,6 @@
 // C ABI of libqamw.so (declared in include/qamw.h).  Every argument is checked here, in host
 // code, before anything is queued; then the kernels are launched on the caller's stream.
+#include <vector>
 #include <cmath>
 
 #include "qamw.h"
@@ -60,6 +61,8 @@ int encode_common(const void* d_w, qamw_dtype w_dtype, int32_t d_out, int32_t d_
     if (rc) return rc;
     if (ld_w < d_in) return QAMW_ERR_ARG;
     if (encode_lds_bytes(L, bits, d_in, thr ? bits - ba : -1) > kLdsBytes) return QAMW_ERR_UNSUPPORTED;
+    // whatever is encoded can be decoded: the decoder's limit applies here too
+    if (decode_lds_bytes(L, bits, d_in) > kLdsBytes) return QAMW_ERR_UNSUPPORTED;
     if (!d_sigma_in && !d_sigma_out) return QAMW_ERR_ARG;
     if (d_out > 0 && (!d_w || !d_norm_f16 || !d_codes)) return QAMW_ERR_ARG;
     if (d_out > 0 && !thr && (!d_codebook || !d_index || !aligned(d_codebook, 8) || !aligned(d_index, 16)))
@@ -309,37 +312,97 @@ int qamw_encode_polar(const void* d_w, qamw_dtype w_dtype, int32_t d_out, int32_
                          stream);
 }
 
-int qamw_decode(const uint8_t* d_codes, const uint16_t* d_norm_f16, const float* d_sigma, const float* d_codebook,
-                int32_t bits, const float* d_scale, int32_t d_out, int32_t d_in, int32_t block, uint64_t sign_seed,
-                void* d_out_w, qamw_dtype out_dtype, int64_t ld_out, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The checks of qamw_decode; fills *a and *L (log2 of the block) when the call is valid.
+int decode_check(const uint8_t* d_codes, const uint16_t* d_norm_f16, const float* d_sigma, const float* d_codebook,
+                 int32_t bits, const float* d_scale, int32_t d_out, int32_t d_in, int32_t block, uint64_t sign_seed,
+                 void* d_out_w, qamw_dtype out_dtype, int64_t ld_out, qamw::DecodeArgs* a, int* L) {
+    using namespace qamw;
     if (d_out < 0 || (out_dtype != QAMW_F32 && out_dtype != QAMW_BF16)) return QAMW_ERR_ARG;
     if (d_out > QAMW_MAX_ROWS) return QAMW_ERR_UNSUPPORTED;
-    int L = check_shape(d_in, block);
-    if (L < 0) return L;
+    *L = check_shape(d_in, block);
+    if (*L < 0) return *L;
     int rc = check_bits(bits);
     if (rc) return rc;
     if (ld_out < d_in || (ld_out & 1)) return QAMW_ERR_ARG;
-    if (decode_lds_bytes(L, bits, d_in) > kLdsBytes) return QAMW_ERR_UNSUPPORTED;
-    if (d_out == 0) return QAMW_OK;
+    if (decode_lds_bytes(*L, bits, d_in) > kLdsBytes) return QAMW_ERR_UNSUPPORTED;
+    if (d_out == 0) {
+        a->d_out = 0;
+        return QAMW_OK;
+    }
     if (!d_codes || !d_norm_f16 || !d_sigma || !d_codebook || !d_out_w) return QAMW_ERR_ARG;
     if (!aligned(d_codebook, 8) || !aligned(d_codes, 4) || !aligned(d_norm_f16, 2) ||
         !aligned(d_out_w, out_dtype == QAMW_BF16 ? 4 : 8))
         return QAMW_ERR_ARG;
+    *a = DecodeArgs{};
+    a->codes = d_codes;
+    a->stride = qamw_row_stride(d_in, bits);
+    a->norm = d_norm_f16;
+    a->sigma = d_sigma;
+    a->cb = d_codebook;
+    a->bits = bits;
+    a->scale = d_scale;
+    a->sign_seed = sign_seed;
+    a->d_out = d_out;
+    a->d_in = d_in;
+    a->out = d_out_w;
+    a->out_bf16 = out_dtype == QAMW_BF16;
+    a->ld = ld_out;
+    return QAMW_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qamw_decode(const uint8_t* d_codes, const uint16_t* d_norm_f16, const float* d_sigma, const float* d_codebook,
+                int32_t bits, const float* d_scale, int32_t d_out, int32_t d_in, int32_t block, uint64_t sign_seed,
+                void* d_out_w, qamw_dtype out_dtype, int64_t ld_out, void* stream) {
     DecodeArgs a{};
-    a.codes = d_codes;
-    a.stride = qamw_row_stride(d_in, bits);
-    a.norm = d_norm_f16;
-    a.sigma = d_sigma;
-    a.cb = d_codebook;
-    a.bits = bits;
-    a.scale = d_scale;
-    a.sign_seed = sign_seed;
-    a.d_out = d_out;
-    a.d_in = d_in;
-    a.out = d_out_w;
-    a.out_bf16 = out_dtype == QAMW_BF16;
-    a.ld = ld_out;
+    int L = 0;
+    const int rc = decode_check(d_codes, d_norm_f16, d_sigma, d_codebook, bits, d_scale, d_out, d_in, block, sign_seed,
+                                d_out_w, out_dtype, ld_out, &a, &L);
+    if (rc || d_out == 0) return rc;
     return hip_rc(launch_decode(a, L, (hipStream_t)stream));
+}
+
+int qamw_decode_many(const qamw_decode_job* jobs, int32_t n_jobs, const float* d_codebook, int32_t bits,
+                     int32_t block, qamw_dtype out_dtype, void* stream) {
+    if (n_jobs < 0 || (n_jobs > 0 && !jobs)) return QAMW_ERR_ARG;
+    std::vector<DecodeArgs> args;
+    std::vector<int> ls;
+    args.reserve((size_t)n_jobs);
+    ls.reserve((size_t)n_jobs);
+    for (int i = 0; i < n_jobs; ++i) {   // every job is checked before anything is queued
+        const qamw_decode_job& j = jobs[i];
+        DecodeArgs a{};
+        int L = 0;
+        const int rc = decode_check(j.d_codes, j.d_norm_f16, j.d_sigma, d_codebook, bits, j.d_scale, j.d_out, j.d_in,
+                                    block, j.sign_seed, j.d_out_w, out_dtype, j.ld_out, &a, &L);
+        if (rc) return rc;
+        if (j.d_out == 0) continue;
+        args.push_back(a);
+        ls.push_back(L);
+    }
+    const hipStream_t st = (hipStream_t)stream;
+    size_t i = 0;
+    while (i < args.size()) {
+        if (!decode128_supported(args[i], ls[i])) {
+            const int rc = hip_rc(launch_decode(args[i], ls[i], st));
+            if (rc) return rc;
+            ++i;
+            continue;
+        }
+        size_t k = i;   // a run of jobs the grouped 128-column decoder takes
+        while (k < args.size() && decode128_supported(args[k], ls[k])) ++k;
+        const int rc = hip_rc(launch_decode128_many(args.data() + i, (int)(k - i), st));
+        if (rc) return rc;
+        i = k;
+    }
+    return QAMW_OK;
 }
 
 int qamw_sign_mask(uint64_t sign_seed, int32_t d_in, uint32_t* d_bits, void* stream) {

@@ -82,6 +82,37 @@ hipError_t launch_encode(const EncodeArgs& a, int L, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, int L, hipStream_t st);
 // Smallest LDS the decoder needs for a row of d_in columns (one row per workgroup).
 size_t decode_lds_bytes(int L, int bits, int d_in);
+
+// The decoder for 128-column blocks (k_decode128.hip): workgroups own spans of column blocks and
+// walk tiles of rows.
+// One matrix of a 128-column decode launch: its workgroups are wg0 .. wg0 + n_wg - 1 of the grid
+// (wg0 and n_wg multiples of 8).
+struct Decode128Item {
+    const uint8_t* codes;
+    const uint16_t* norm;
+    const float* sigma;
+    const float* scale;
+    void* out;
+    uint64_t sign_seed;
+    uint32_t stride;   // bytes per code row
+    int32_t d_out;
+    uint32_t ld;       // output elements per row
+    int32_t nb;        // column blocks per row
+    int32_t wg0, n_wg;
+};
+// Matrices per launch of a grouped decode: the descriptors travel as kernel arguments (4 KiB).
+constexpr int kDecodeBatch = 48;
+template <int NI>
+struct Decode128Batch {
+    const float* cb;
+    int32_t n;
+    Decode128Item it[NI];
+};
+bool decode128_supported(const DecodeArgs& a, int L);
+hipError_t launch_decode128(const DecodeArgs& a, hipStream_t st);
+// Decodes that share codebook, bits and output type, each accepted by decode128_supported, as
+// launches of up to kDecodeBatch matrices.
+hipError_t launch_decode128_many(const DecodeArgs* a, int n, hipStream_t st);
 hipError_t launch_sign_mask(uint64_t seed, int d_in, uint32_t* bits, hipStream_t st);
 hipError_t launch_polar_codebook(int ba, int bp, double* levels, double* thr, float* cb, hipStream_t st);
 hipError_t launch_scalar_codebook(int b, double* levels, double* thr, float* cb, hipStream_t st);
