@@ -11,7 +11,9 @@
  *   - `stream` is a hipStream_t passed as void*; NULL selects the default stream.  Every call
  *     only queues work on that stream and never synchronizes with the host.
  *   - The library keeps no state between calls and allocates no device memory: scratch lives
- *     in the caller's workspace (sizes from the *_workspace / qamw_index_bytes helpers).
+ *     in the caller's workspace (sizes from the *_workspace / qamw_index_bytes helpers).  The one
+ *     exception is qamw_qgemm_noalloc, whose workspace is a static array of the library on each
+ *     device (QAMW_QGEMM_NOALLOC_BYTES, held until the process ends).
  *   - Return value: QAMW_OK, or a negative QAMW_ERR_* code computed by host code before any
  *     launch (bad argument, unsupported shape, short workspace) or from a failed launch.
  *     Nothing is queued when an argument error is returned.
@@ -234,6 +236,22 @@ int qamw_qgemm(const void* d_x, qamw_dtype x_dtype, int32_t M, int64_t ld_x, con
                const uint16_t* d_norm_f16, const float* d_sigma, const float* d_codebook, int32_t bits,
                const float* d_scale, int32_t d_out, int32_t d_in, int32_t block, uint64_t sign_seed,
                void* d_y, qamw_dtype y_dtype, int64_t ld_y, void* d_ws, size_t ws_bytes, void* stream);
+
+/* For callers that cannot allocate device memory or pass a workspace -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation: qamw_qgemm without the d_ws /
+ * ws_bytes arguments, same result bit for bit.  Its workspace is an array of
+ * QAMW_QGEMM_NOALLOC_BYTES bytes that the library holds on each device from its first call there
+ * until the process ends; the call itself allocates nothing.  Shapes whose qamw_qgemm_workspace
+ * exceeds that size return QAMW_ERR_WORKSPACE (4 MiB covers M <= 16 up to 8192 x 28672 weights).
+ * `stream` must belong to the current device (NULL: its default stream); otherwise, or when the
+ * array's address cannot be obtained, QAMW_ERR_HIP.  All calls on a device share its array: calls
+ * that may run at the same time on one device (different streams, threads without ordering) race
+ * on it and their results are undefined; calls queued on one stream are safe. */
+#define QAMW_QGEMM_NOALLOC_BYTES (4u << 20)
+int qamw_qgemm_noalloc(const void* d_x, qamw_dtype x_dtype, int32_t M, int64_t ld_x, const uint8_t* d_codes,
+                       const uint16_t* d_norm_f16, const float* d_sigma, const float* d_codebook, int32_t bits,
+                       const float* d_scale, int32_t d_out, int32_t d_in, int32_t block, uint64_t sign_seed,
+                       void* d_y, qamw_dtype y_dtype, int64_t ld_y, void* stream);
 
 /* Section 3.5 (the polar baseline QAM-W is compared with): a pair is coded as a magnitude level
  * times a phase.  The magnitude quantizer is the Na = 2^ba level Lloyd-Max quantizer of the unit

@@ -22,7 +22,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = q.header_symbols()
-    assert len(names) == 21
+    assert len(names) == 22
     out = subprocess.run(["nm", "-D", "--defined-only", q.LIB_PATH], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
     for n in names:
@@ -232,6 +232,27 @@ def test_qgemm_noops_and_workspace(lib):
     assert lib.qamw_qgemm_workspace(1, 16, 255) == 0
 
 
+def test_qgemm_noalloc_checks_and_size_limit(lib):
+    """The static-workspace product checks its arguments as qamw_qgemm does and refuses shapes
+    whose workspace exceeds the library's array, before any HIP call."""
+    assert q.QGEMM_NOALLOC_BYTES == 4 << 20
+    base = dict(x=FAKE, xd=q.BF16, M=4, ldx=4096, codes=FAKE, norm=FAKE, sigma=FAKE, cb=FAKE, bits=11, scale=None,
+                d_out=4096, d_in=4096, block=128, seed=q.DEFAULT_SIGN_SEED, y=FAKE, yd=q.F32, ldy=4096)
+
+    def call(**kw):
+        a = dict(base)
+        a.update(kw)
+        return lib.qamw_qgemm_noalloc(a["x"], a["xd"], a["M"], a["ldx"], a["codes"], a["norm"], a["sigma"], a["cb"],
+                                      a["bits"], a["scale"], a["d_out"], a["d_in"], a["block"], a["seed"], a["y"],
+                                      a["yd"], a["ldy"], None)
+    assert call(M=17) == UNSUP and call(bits=13) == UNSUP and call(block=3) == ARG and call(codes=None) == ARG
+    assert call(M=0) == q.OK and call(d_out=0) == q.OK
+    big = 131072   # 16 x 131072 activations need 8 MiB of rotated fragments
+    assert lib.qamw_qgemm_workspace(16, 64, big) > q.QGEMM_NOALLOC_BYTES
+    assert call(M=16, d_in=big, ldx=big, d_out=64, ldy=64, block=1024) == WS
+    assert lib.qamw_qgemm_workspace(16, 28672, 8192) <= q.QGEMM_NOALLOC_BYTES
+
+
 def test_scalar_codebook_rejects(lib):
     assert lib.qamw_scalar_codebook(0, FAKE, FAKE, FAKE, None) == ARG
     assert lib.qamw_scalar_codebook(9, FAKE, FAKE, FAKE, None) == ARG
@@ -267,6 +288,8 @@ def test_header_default_seed_matches_binding():
     text = open(q.HEADER_PATH).read()
     m = re.search(r"#define QAMW_DEFAULT_SIGN_SEED (0x[0-9A-Fa-f]+)ull", text)
     assert m and int(m.group(1), 16) == q.DEFAULT_SIGN_SEED
+    m = re.search(r"#define QAMW_QGEMM_NOALLOC_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == q.QGEMM_NOALLOC_BYTES
 
 
 # ----------------------------------------------------------------------------- binding argument checks

@@ -29,6 +29,8 @@ FLAG_NONFINITE, FLAG_BAD_SCALE, FLAG_NORM_RANGE, FLAG_POINT_RANGE, FLAG_BAD_THRE
     1, 2, 4, 8, 16, 32)
 # seed of the rotation's sign mask when the caller gives none (QAMW_DEFAULT_SIGN_SEED of qamw.h)
 DEFAULT_SIGN_SEED = 0x51414D57
+# bytes of the static workspace of qamw_qgemm_noalloc (QAMW_QGEMM_NOALLOC_BYTES of qamw.h)
+QGEMM_NOALLOC_BYTES = 4 << 20
 
 
 class QamwError(RuntimeError):
@@ -67,6 +69,8 @@ def load(path: Optional[str] = None):
         "qamw_qgemm_workspace": ([i32, i32, i32], sz),
         "qamw_qgemm": ([vp, ctypes.c_int, i32, i64, vp, vp, vp, vp, i32, vp, i32, i32, i32, u64, vp, ctypes.c_int, i64,
                         vp, sz, vp], ctypes.c_int),
+        "qamw_qgemm_noalloc": ([vp, ctypes.c_int, i32, i64, vp, vp, vp, vp, i32, vp, i32, i32, i32, u64, vp,
+                                ctypes.c_int, i64, vp], ctypes.c_int),
         "qamw_polar_codebook": ([i32, i32, vp, vp, vp, vp], ctypes.c_int),
         "qamw_polar_index": ([vp, i64, i32, i32, vp, vp, vp, vp], ctypes.c_int),
         "qamw_scalar_codebook": ([i32, vp, vp, vp, vp], ctypes.c_int),
@@ -386,6 +390,28 @@ def qgemm(x: torch.Tensor, codes: torch.Tensor, norm: torch.Tensor, sigma: torch
                            _ptr(scale), d_out, d_in, block, sign_seed, _ptr(out), _dt(out), ld_y, _ptr(ws), ws.numel(),
                            _stream())
     _check(rc, "qamw_qgemm")
+    return out
+
+
+def qgemm_noalloc(x: torch.Tensor, codes: torch.Tensor, norm: torch.Tensor, sigma: torch.Tensor,
+                  codebook: torch.Tensor, bits: int, scale: Optional[torch.Tensor] = None,
+                  sign_seed: int = DEFAULT_SIGN_SEED, block: int = 0, out: Optional[torch.Tensor] = None,
+                  out_dtype=torch.float32) -> torch.Tensor:
+    """qgemm with the library's static workspace (qamw_qgemm_noalloc): no workspace argument, and
+    no allocation when `out` is given."""
+    if isinstance(x, torch.Tensor) and x.dim() == 1:
+        x = x.unsqueeze(0)
+    ld_x = _matrix(x, "x")
+    M, d_in = x.shape
+    d_out = _decode_inputs(codes, norm, sigma, codebook, bits, d_in, scale)
+    if out is None:
+        out = torch.empty((M, d_out), dtype=out_dtype, device=x.device)
+    ld_y = _matrix(out, "out", rows=M, cols=d_out)
+    _on_device(x=x, codes=codes, norm=norm, sigma=sigma, codebook=codebook, scale=scale, out=out)
+    rc = load().qamw_qgemm_noalloc(_ptr(x), _dt(x), M, ld_x, _ptr(codes), _ptr(norm), _ptr(sigma), _ptr(codebook),
+                                   bits, _ptr(scale), d_out, d_in, block, sign_seed, _ptr(out), _dt(out), ld_y,
+                                   _stream())
+    _check(rc, "qamw_qgemm_noalloc")
     return out
 
 

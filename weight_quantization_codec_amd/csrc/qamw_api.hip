@@ -1,5 +1,6 @@
 // C ABI of libqamw.so (declared in include/qamw.h).  Every argument is checked here, in host
 // code, before anything is queued; then the kernels are launched on the caller's stream.
+#include <mutex>
 #include <vector>
 #include <cmath>
 
@@ -204,10 +205,42 @@ size_t qamw_qgemm_workspace(int32_t M, int32_t d_out, int32_t d_in) {
     return qgemm_workspace(M, d_out, d_in);
 }
 
-int qamw_qgemm(const void* d_x, qamw_dtype x_dtype, int32_t M, int64_t ld_x, const uint8_t* d_codes,
-               const uint16_t* d_norm_f16, const float* d_sigma, const float* d_codebook, int32_t bits,
-               const float* d_scale, int32_t d_out, int32_t d_in, int32_t block, uint64_t sign_seed,
-               void* d_y, qamw_dtype y_dtype, int64_t ld_y, void* d_ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The library's own workspace for qamw_qgemm_noalloc: one array per device, held until the process
+// ends.  Host code never uses the name itself (on the host it only stands for the symbol): the
+// device address comes from hipGetSymbolAddress, once per device, with that device current.
+static __device__ __align__(256) unsigned char scratch[QAMW_QGEMM_NOALLOC_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The array's address on the device of `stream` (which must be the current device), or nullptr.
+void* scratch_address(hipStream_t stream) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    if (stream) {
+        int sdev = -1;
+        if (hipStreamGetDevice(stream, &sdev) != hipSuccess || sdev != dev) return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
+// The checks of qamw_qgemm except the workspace's; QAMW_OK with *run = false when there is nothing
+// to do.
+int qgemm_check(const void* d_x, qamw_dtype x_dtype, int32_t M, int64_t ld_x, const uint8_t* d_codes,
+                const uint16_t* d_norm_f16, const float* d_sigma, const float* d_codebook, int32_t bits, int32_t d_out,
+                int32_t d_in, int32_t block, void* d_y, qamw_dtype y_dtype, int64_t ld_y, bool* run) {
+    *run = false;
     if (M < 0 || d_out < 0 || (x_dtype != QAMW_F32 && x_dtype != QAMW_BF16) ||
         (y_dtype != QAMW_F32 && y_dtype != QAMW_BF16))
         return QAMW_ERR_ARG;
@@ -224,7 +257,15 @@ int qamw_qgemm(const void* d_x, qamw_dtype x_dtype, int32_t M, int64_t ld_x, con
     if (!aligned(d_x, x_dtype == QAMW_BF16 ? 2 : 4) || !aligned(d_y, y_dtype == QAMW_BF16 ? 2 : 4) ||
         !aligned(d_codes, 4) || !aligned(d_codebook, 8) || !aligned(d_norm_f16, 2))
         return QAMW_ERR_ARG;
-    if (!d_ws || !aligned(d_ws, 256) || ws_bytes < qamw_qgemm_workspace(M, d_out, d_in)) return QAMW_ERR_WORKSPACE;
+    *run = true;
+    return QAMW_OK;
+}
+
+// Queues the product with its workspace at d_ws (checked by the caller).
+int qgemm_run(const void* d_x, qamw_dtype x_dtype, int32_t M, int64_t ld_x, const uint8_t* d_codes,
+              const uint16_t* d_norm_f16, const float* d_sigma, const float* d_codebook, int32_t bits,
+              const float* d_scale, int32_t d_out, int32_t d_in, int32_t block, uint64_t sign_seed, void* d_y,
+              qamw_dtype y_dtype, int64_t ld_y, void* d_ws, hipStream_t stream) {
     QgemmArgs a{};
     a.codes = d_codes;
     a.stride = qamw_row_stride(d_in, bits);
@@ -244,11 +285,45 @@ int qamw_qgemm(const void* d_x, qamw_dtype x_dtype, int32_t M, int64_t ld_x, con
     r.x_bf16 = x_dtype == QAMW_BF16;
     r.ld_x = ld_x;
     r.d_in = d_in;
-    r.block = b;
+    r.block = block == 0 ? qamw_default_block(d_in) : block;
     r.scale = d_scale;
     r.sign_seed = sign_seed;
     r.sigma = d_sigma;
-    return hip_rc(launch_qgemm(a, r, (hipStream_t)stream));
+    return hip_rc(launch_qgemm(a, r, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int qamw_qgemm(const void* d_x, qamw_dtype x_dtype, int32_t M, int64_t ld_x, const uint8_t* d_codes,
+               const uint16_t* d_norm_f16, const float* d_sigma, const float* d_codebook, int32_t bits,
+               const float* d_scale, int32_t d_out, int32_t d_in, int32_t block, uint64_t sign_seed,
+               void* d_y, qamw_dtype y_dtype, int64_t ld_y, void* d_ws, size_t ws_bytes, void* stream) {
+    bool run = false;
+    const int rc = qgemm_check(d_x, x_dtype, M, ld_x, d_codes, d_norm_f16, d_sigma, d_codebook, bits, d_out, d_in,
+                               block, d_y, y_dtype, ld_y, &run);
+    if (rc || !run) return rc;
+    if (!d_ws || !aligned(d_ws, 256) || ws_bytes < qamw_qgemm_workspace(M, d_out, d_in)) return QAMW_ERR_WORKSPACE;
+    return qgemm_run(d_x, x_dtype, M, ld_x, d_codes, d_norm_f16, d_sigma, d_codebook, bits, d_scale, d_out, d_in,
+                     block, sign_seed, d_y, y_dtype, ld_y, d_ws, (hipStream_t)stream);
+}
+
+int qamw_qgemm_noalloc(const void* d_x, qamw_dtype x_dtype, int32_t M, int64_t ld_x, const uint8_t* d_codes,
+                       const uint16_t* d_norm_f16, const float* d_sigma, const float* d_codebook, int32_t bits,
+                       const float* d_scale, int32_t d_out, int32_t d_in, int32_t block, uint64_t sign_seed,
+                       void* d_y, qamw_dtype y_dtype, int64_t ld_y, void* stream) {
+    bool run = false;
+    const int rc = qgemm_check(d_x, x_dtype, M, ld_x, d_codes, d_norm_f16, d_sigma, d_codebook, bits, d_out, d_in,
+                               block, d_y, y_dtype, ld_y, &run);
+    if (rc || !run) return rc;
+    if (qamw_qgemm_workspace(M, d_out, d_in) > QAMW_QGEMM_NOALLOC_BYTES) return QAMW_ERR_WORKSPACE;
+    void* ws = scratch_address((hipStream_t)stream);
+    if (!ws) return QAMW_ERR_HIP;
+    // nothing in the workspace has to start at zero: every word the product reads was written
+    // earlier in the same call
+    return qgemm_run(d_x, x_dtype, M, ld_x, d_codes, d_norm_f16, d_sigma, d_codebook, bits, d_scale, d_out, d_in,
+                     block, sign_seed, d_y, y_dtype, ld_y, ws, (hipStream_t)stream);
 }
 
 int qamw_polar_codebook(int32_t ba, int32_t bp, double* d_levels, double* d_thresholds, float* d_codebook,
