@@ -142,7 +142,7 @@ __device__ __forceinline__ void load_raw(const void* w, bool vec, int64_t off, R
 // row's sum of squares non-finite (|a_j| < 2^256, so a_j^2 cannot overflow), so the row norm
 // alone tells whether the row has a non-finite weight.
 template <int E, bool BF>
-__device__ __forceinline__ void scale_raw(const RawW<E, BF>& r, const float (&cf)[E], double (&x)[E], double& ss) {
+__device__ __forceinline__ void scale_raw(const RawW<E, BF>& r, const double (&cf)[E], double (&x)[E], double& ss) {
 #pragma unroll
     for (int m = 0; m < E; ++m) {
         float f;
@@ -150,7 +150,7 @@ __device__ __forceinline__ void scale_raw(const RawW<E, BF>& r, const float (&cf
             f = __uint_as_float((m & 1) ? (r.u[m >> 1] & 0xFFFF0000u) : (r.u[m >> 1] << 16));
         else
             f = __uint_as_float(r.u[m]);
-        double a = (double)f * (double)cf[m];   // exact: two 24-bit significands
+        double a = (double)f * cf[m];   // exact: two 24-bit significands
         x[m] = a;
         ss += a * a;
     }
@@ -162,7 +162,7 @@ __device__ __forceinline__ void scale_raw(const RawW<E, BF>& r, const float (&cf
 // the two), so the wavefront's exchange buffer covers 32 lanes: half the LDS.
 template <int L, bool BF, bool SPLIT = false>
 __device__ __forceinline__ double front_end(const RawW<Layout<L>::E, BF>& raw, bool active, int tid,
-                                            const float (&cf)[Layout<L>::E], double (&x)[Layout<L>::E],
+                                            const double (&cf)[Layout<L>::E], double (&x)[Layout<L>::E],
                                             double* red, double* xb, int nwaves) {
     using Lo = Layout<L>;
     constexpr int E = Lo::E;
@@ -261,10 +261,14 @@ __global__ __launch_bounds__(MAXT) void k_calibrate(CalibArgs a, int T, int R) {
     const int rstride = gridDim.x * R;
     int base = blockIdx.x * R;
     if (active && base + grp < a.n_rows) load_raw<E, BF>(a.w, vec, (int64_t)(base + grp) * a.ld + (int64_t)tid * E, nxt);
-    float cf[E];   // s_j * eps_j, exact in fp32 (scales are checked by the encoder)
-    bool bad_scale = false;
-    load_cf<E>(a.scale, a.sign_seed, tid, a.d_in, cf, bad_scale);
-    (void)bad_scale;
+    double cf[E];   // s_j * eps_j (exact in fp32; scales are checked by the encoder)
+    {
+        float cf32[E];
+        bool bad_scale = false;
+        load_cf<E>(a.scale, a.sign_seed, tid, a.d_in, cf32, bad_scale);
+#pragma unroll
+        for (int m = 0; m < E; ++m) cf[m] = (double)cf32[m];
+    }
     const double inv_sqrt_b = 1.0 / __builtin_sqrt((double)Lo::b);
     double acc[NP];
 #pragma unroll
@@ -273,11 +277,10 @@ __global__ __launch_bounds__(MAXT) void k_calibrate(CalibArgs a, int T, int R) {
     for (; base < a.n_rows; base += rstride) {
         const int row = base + grp;
         const bool rv = row < a.n_rows;
-        const RawW<E, BF> cur = nxt;
+        double x[E];
+        double r2 = front_end<L, BF>(nxt, active && rv, tid, cf, x, red, xb, nwaves);
         if (active && row + rstride < a.n_rows)
             load_raw<E, BF>(a.w, vec, (int64_t)(row + rstride) * a.ld + (int64_t)tid * E, nxt);
-        double x[E];
-        double r2 = front_end<L, BF>(cur, active && rv, tid, cf, x, red, xb, nwaves);
         double r = __builtin_sqrt(r2);
         if (rv && r > 0.0 && __builtin_isfinite(r)) {
             ++nz;
@@ -430,16 +433,19 @@ __device__ __forceinline__ void load_row_raw(const void* w, int64_t ld, int d_in
 // Per pass: front end (scale, norm, transform), pairs, lockstep search in batches of four pairs
 // per lane, indices to LDS, then each wavefront packs and stores its part of the row.
 constexpr int kSearchBatch = 4;
+constexpr int kSearchCap = 3;   // lockstep steps before a longer list goes to the queue
 constexpr int kPolarBatch = 1;   // pairs per polar batch: more spill registers
 
 // LDS bytes per wavefront of the encoder.  A wavefront's lanes cover 32 E consecutive pairs of
 // the row, so it packs and stores its own part of the row: its buffer holds the exchange during
-// the front end and then the wavefront's 32 E indices (u16) and their packed words (4 E bits
-// bytes, a multiple of 16).
+// the front end and then the wavefront's 32 E indices (u16) followed by the search queue and then
+// by their packed words (4 E bits bytes, a multiple of 16).
 __host__ __device__ inline size_t encode_wave_bytes(int E, bool two_phase, int bits) {
     const size_t xch = two_phase ? (size_t)(32 * (E / 2) + 32) * sizeof(double) : 0;   // the split transpose
     const size_t pack = (size_t)64 * E + (size_t)4 * E * bits;
-    return xch > pack ? xch : pack;
+    const size_t queue = (size_t)64 * E + search_queue_bytes();   // the search queue after the indices
+    const size_t m = xch > pack ? xch : pack;
+    return m > queue ? m : queue;
 }
 
 template <int L, int MAXT, bool BF, bool VEC, bool ISG_LDS, bool POLAR>
@@ -498,10 +504,15 @@ __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a, int T, int R) {
         search_lds_fill(sl, index, K, threadIdx.x, blockDim.x);
     }
 
-    float cf[E];   // s_j * eps_j, exact in fp32
-    bool bad_scale = false;
-    load_cf<E>(a.scale, a.sign_seed, tid, a.d_in, cf, bad_scale);
-    if (active && bad_scale && blockIdx.x == 0) flags |= 2;   // reported once
+    double cf[E];   // s_j * eps_j (exact in fp32), held as doubles: converted once, not per row
+    {
+        float cf32[E];
+        bool bad_scale = false;
+        load_cf<E>(a.scale, a.sign_seed, tid, a.d_in, cf32, bad_scale);
+        if (active && bad_scale && blockIdx.x == 0) flags |= 2;   // reported once
+#pragma unroll
+        for (int m = 0; m < E; ++m) cf[m] = (double)cf32[m];
+    }
 #pragma unroll
     for (int m = 0; m < E; ++m) pin_reg(cf[m]);
     // 1 / sigma_k of the lane's pairs: in registers, or (ISG_LDS, which frees 16 VGPRs) in LDS,
@@ -532,17 +543,18 @@ __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a, int T, int R) {
     for (int pass = 0; base < a.d_out; base += rstride, ++pass) {
         const int row = base + grp;
         const bool rv = row < a.d_out;
-        const RawW<E, BF> cur = nxt;
-        load_row_raw<E, BF, VEC>(a.w, a.ld, a.d_in, a.d_out, row + rstride, tid, nxt);   // next row in flight
         double x[E];
         int32_t rf = 0;
         double* red = red_all + ((pass & 1) * R + grp) * kMaxWaves;
-        const double r2 = front_end<L, BF, true>(cur, active && rv, tid, cf, x, red, xb, nwaves);
+        const double r2 = front_end<L, BF, true>(nxt, active && rv, tid, cf, x, red, xb, nwaves);
+        // the next row, in flight during the search and the packing (its registers were free
+        // during the front end)
+        load_row_raw<E, BF, VEC>(a.w, a.ld, a.d_in, a.d_out, row + rstride, tid, nxt);
         const double r = __builtin_sqrt(r2);
         const bool nonzero = r > 0.0 && __builtin_isfinite(r);
         if (rv && !__builtin_isfinite(r)) rf |= 1;
+        float px[NP], py[NP];
         if (active) {
-            float px[NP], py[NP];
             const double hr = inv_sqrt_b / r;
 #pragma unroll
             for (int i = 0; i < NP; i += 2) {
@@ -553,41 +565,81 @@ __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a, int T, int R) {
                 px[i + 1] = (float)(x[2 * i + 2] * g1);
                 py[i + 1] = (float)(x[2 * i + 3] * g1);
             }
+        } else {
 #pragma unroll
-            for (int h = 0; h < NP / kSearchBatch; ++h) {
-                float bx[kSearchBatch], by[kSearchBatch];
-                int bi[kSearchBatch];
+            for (int i = 0; i < NP; ++i) px[i] = py[i] = 0.0f;
+        }
+        // Searches capped at kSearchCap lockstep steps; the longer lists go to the wavefront's queue
+        // (after the indices, where the packed words go later) and are finished one per lane.  Pairs
+        // past the row (inactive lanes) and zero rows get index 0, so the row's padding bits are 0.
+        const SearchQueue sq = search_queue_at(wbuf + 64 * E);
+        const uint32_t slot_l = (uint32_t)(idx_l - widx);
+        constexpr uint32_t kSlotStep = Lo::two_phase ? Lo::lanes : 1;
+        int qn = 0;   // entries in the queue (uniform over the wavefront)
+#pragma unroll
+        for (int h = 0; h < NP / kSearchBatch; ++h) {
+            float bx[kSearchBatch], by[kSearchBatch];
+            int bi[kSearchBatch];
+            SearchCont st[kSearchBatch];
+#pragma unroll
+            for (int i = 0; i < kSearchBatch; ++i) {
+                bx[i] = px[h * kSearchBatch + i];
+                by[i] = py[h * kSearchBatch + i];
+                bi[i] = 0;
+                st[i] = SearchCont{0.0f, 0u, 0u};
+            }
+            if (active && nonzero) {
+                if constexpr (POLAR) {
+#pragma unroll
+                    for (int g = 0; g < kSearchBatch; g += kPolarBatch) {
+                        float gx[kPolarBatch], gy[kPolarBatch];
+                        int gi[kPolarBatch];
+#pragma unroll
+                        for (int i = 0; i < kPolarBatch; ++i) {
+                            gx[i] = bx[g + i];
+                            gy[i] = by[g + i];
+                        }
+                        polar_batch<kPolarBatch>(gx, gy, pl, gi);
+#pragma unroll
+                        for (int i = 0; i < kPolarBatch; ++i) bi[g + i] = gi[i];
+                    }
+                } else {
+                    nearest_lds_capped<kSearchBatch, kSearchCap>(bx, by, sl, bi, st);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < kSearchBatch; ++i) idx_l[(h * kSearchBatch + i) * kSlotStep] = (uint16_t)bi[i];
+            if constexpr (!POLAR) {
 #pragma unroll
                 for (int i = 0; i < kSearchBatch; ++i) {
-                    bx[i] = px[h * kSearchBatch + i];
-                    by[i] = py[h * kSearchBatch + i];
-                }
-                if (nonzero) {
-                    if constexpr (POLAR) {
-#pragma unroll
-                        for (int g = 0; g < kSearchBatch; g += kPolarBatch) {
-                            float gx[kPolarBatch], gy[kPolarBatch];
-                            int gi[kPolarBatch];
-#pragma unroll
-                            for (int i = 0; i < kPolarBatch; ++i) {
-                                gx[i] = bx[g + i];
-                                gy[i] = by[g + i];
-                            }
-                            polar_batch<kPolarBatch>(gx, gy, pl, gi);
-#pragma unroll
-                            for (int i = 0; i < kPolarBatch; ++i) bi[g + i] = gi[i];
-                        }
-                    } else {
-                        nearest_lds_batch<kSearchBatch>(bx, by, sl, bi);
+                    const bool want = st[i].open();
+                    const uint64_t m = __builtin_amdgcn_ballot_w64(want);
+                    const int c = __builtin_popcountll(m);
+                    if (c == 0) continue;
+                    if (qn + c > kSearchQueue) {   // full: finish what it holds first
+                        wave_lds_sync();
+                        search_finish(sq, qn, sl, widx, lane);
+                        wave_lds_sync();
+                        qn = 0;
                     }
+                    if (want) {
+                        const int pos =
+                            qn + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                        sq.x[pos] = bx[i];
+                        sq.y[pos] = by[i];
+                        sq.bd[pos] = st[i].bd;
+                        sq.a[pos] = (st[i].bo_next & 0xFFFFu) | ((slot_l + (uint32_t)(h * kSearchBatch + i) * kSlotStep) << 16);
+                        sq.b[pos] = (st[i].bo_next >> 16) | (st[i].end << 16);
+                    }
+                    qn += c;
                 }
-#pragma unroll
-                for (int i = 0; i < kSearchBatch; ++i)
-                    idx_l[(h * kSearchBatch + i) * (Lo::two_phase ? Lo::lanes : 1)] = nonzero ? (uint16_t)bi[i] : (uint16_t)0;
             }
-        } else {   // pairs past the row: zero indices, so the row's padding bits are zero
-#pragma unroll
-            for (int i = 0; i < NP; ++i) idx_l[i * (Lo::two_phase ? Lo::lanes : 1)] = 0;
+        }
+        if constexpr (!POLAR) {
+            if (qn > 0) {
+                wave_lds_sync();   // the queue and the provisional indices are written
+                search_finish(sq, qn, sl, widx, lane);
+            }
         }
         {   // the norm, stored by lane 0 of the group
             uint16_t nh = 0;
@@ -600,17 +652,34 @@ __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a, int T, int R) {
         }
         if (rv) flags |= rf;
         wave_lds_sync();
-        // pack (LSB first): lane c builds words c, c + 64, ... of the wavefront's E * bits words,
-        // each from the few indices that overlap it, so all lanes share the work
-        for (int wd = lane; wd < E * bits; wd += kWave) {
-            const int b0 = 32 * wd;   // first bit of the word
-            uint32_t word = 0;
-            for (int i = b0 / bits; i * bits < b0 + 32; ++i) {   // at most 32 / bits + 2 indices
-                const uint32_t v = widx[i];
-                const int sh = i * bits - b0;                     // negative for an index begun earlier
-                word |= sh >= 0 ? (v << sh) : (v >> -sh);
+        // pack (LSB first): the wavefront's 32 E indices make E * bits words; lane l packs indices
+        // NP l .. NP l + NP - 1 (bits NP l bits onwards) through a 64-bit window, OR-ing each word
+        // it completes into LDS (the first and last ones are shared with the neighbouring lanes)
+        for (int wd = lane; wd < E * bits; wd += kWave) wstage[wd] = 0;
+        wave_lds_sync();
+        {
+            const uint32_t off = (uint32_t)(lane * NP * bits);
+            uint32_t w = off >> 5, nb = off & 31u;
+            uint64_t acc = 0;
+#pragma unroll 1
+            for (int v = 0; v < NP / 8; ++v) {   // eight indices (16 bytes) at a time
+                const u32x4 q = *reinterpret_cast<const u32x4*>(widx + NP * lane + 8 * v);
+                uint64_t lo = ((uint64_t)q[1] << 32) | q[0], hi = ((uint64_t)q[3] << 32) | q[2];
+#pragma unroll 1
+                for (int i = 0; i < 8; ++i) {
+                    acc |= (lo & 0xFFFFu) << nb;
+                    lo = (lo >> 16) | (hi << 48);
+                    hi >>= 16;
+                    nb += (uint32_t)bits;
+                    if (nb >= 32u) {
+                        __hip_atomic_fetch_or(wstage + w, (uint32_t)acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                        acc >>= 32;
+                        nb -= 32u;
+                        ++w;
+                    }
+                }
             }
-            wstage[wd] = word;
+            if (nb > 0u) __hip_atomic_fetch_or(wstage + w, (uint32_t)acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         }
         wave_lds_sync();
         // 16-byte stores of the wavefront's 4 E bits bytes: E bits / 4 chunks, lane c storing

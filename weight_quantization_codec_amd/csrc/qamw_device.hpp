@@ -338,47 +338,57 @@ __device__ __forceinline__ float2 cw_at(uint32_t addr) {
     return make_float2(v.x, v.y);
 }
 
-// NP points searched in lockstep.  Step t evaluates entry o_i + t of every point's list.  The
-// loop runs until the longest list of the wavefront is done (a uniform loop) and reads shorter
-// lists past their end, into the following cells' lists and the zero padding: that is harmless,
-// because a list holds every codeword that can be nearest or tied anywhere in its cell, so an
-// extra codeword can neither be strictly closer nor tie with a lower index than the answer
-// (lists are in increasing index order and only a strictly smaller distance replaces the best).
-// Each step issues NP independent list loads, then NP codeword loads.  Points outside the grid,
-// in exhaustive cells or non-finite take the single-point path afterwards, one point slot at a
-// time (a uniform loop, so the slow path exists once in the code).
-template <int NP>
-__device__ __forceinline__ void nearest_lds_batch(const float (&px)[NP], const float (&py)[NP], const SearchLds& s,
-                                                  int (&out)[NP]) {
-    const uint16_t* lp[NP];
+// NP points searched in lockstep, at most S steps.  Step t evaluates entry o_i + t of every point's
+// list.  The loop runs until the longest list of the wavefront is done or S steps have run (a
+// uniform loop) and reads shorter lists past their end, into the following cells' lists and the
+// zero padding: that is harmless, because a list holds every codeword that can be nearest or tied
+// anywhere in its cell, so an extra codeword can neither be strictly closer nor tie with a lower
+// index than the answer (lists are in increasing index order and only a strictly smaller distance
+// replaces the best).  A point whose list is longer than S leaves its state in `st` (best distance
+// and codeword address, next entry and end of its list) for search_finish, which evaluates the
+// rest of the list in the same order.  Points outside the grid, in exhaustive cells or non-finite
+// take the single-point path afterwards, one point slot at a time (a uniform loop, so the slow
+// path exists once in the code); their answer is final.
+struct SearchCont {
+    float bd;
+    uint32_t bo_next;   // LDS byte address of the best codeword so far | list entry to evaluate next << 16
+    uint32_t end;       // one past the list's last entry (end > next: the list is not finished)
+    __device__ bool open() const { return end > (bo_next >> 16); }
+};
+
+template <int NP, int S>
+__device__ __forceinline__ void nearest_lds_capped(const float (&px)[NP], const float (&py)[NP], const SearchLds& s,
+                                                   int (&out)[NP], SearchCont (&st)[NP]) {
     float bd[NP];
-    uint32_t bo[NP];
+    uint32_t bo[NP], o0[NP], o1[NP];
     uint32_t slow = 0;
     int steps = 0;
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
         bd[i] = __builtin_inff();
         bo[i] = s.cb_lds;
-        int o0 = 0, o1 = 0;   // empty: points outside the grid take the slow path
+        int a0 = 0, a1 = 0;   // empty: points outside the grid take the slow path
         if (fabsf(px[i]) < s.R && fabsf(py[i]) < s.R) {
             const int bx = min((int)((px[i] + s.R) * s.inv_w), s.W - 1);
             const int by = min((int)((py[i] + s.R) * s.inv_w), s.W - 1);
             const int cell = s.fine[by] * s.G + s.fine[bx];
-            o0 = s.offs[cell];
-            o1 = s.offs[cell + 1];
+            a0 = s.offs[cell];
+            a1 = s.offs[cell + 1];
         }
-        if (o1 <= o0) {   // outside the grid, non-finite, or exhaustive cell
+        if (a1 <= a0) {   // outside the grid, non-finite, or exhaustive cell
             slow |= 1u << i;
-            o0 = 0;
-            o1 = 0;
+            a0 = 0;
+            a1 = 0;
         }
-        lp[i] = s.ent + o0;
-        steps = max(steps, o1 - o0);
+        o0[i] = (uint32_t)a0;
+        o1[i] = (uint32_t)a1;
+        steps = max(steps, a1 - a0);
     }
+    if (steps > S) steps = S;
     for (int t = 0; wave_any((uint32_t)(t < steps)); ++t) {
         uint32_t ad[NP];
 #pragma unroll
-        for (int i = 0; i < NP; ++i) ad[i] = lp[i][t];
+        for (int i = 0; i < NP; ++i) ad[i] = s.ent[o0[i] + t];
         float2 c[NP];
 #pragma unroll
         for (int i = 0; i < NP; ++i) c[i] = cw_at(ad[i]);
@@ -392,7 +402,12 @@ __device__ __forceinline__ void nearest_lds_batch(const float (&px)[NP], const f
         }
     }
 #pragma unroll
-    for (int i = 0; i < NP; ++i) out[i] = (int)((bo[i] - s.cb_lds) >> 3);
+    for (int i = 0; i < NP; ++i) {
+        out[i] = (int)((bo[i] - s.cb_lds) >> 3);
+        st[i].bd = bd[i];
+        st[i].bo_next = bo[i] | ((o0[i] + S) << 16);
+        st[i].end = o1[i];   // slow points have an empty list: end 0 <= next
+    }
     if (wave_any(slow)) {
 #pragma unroll 1
         for (int i = 0; i < NP; ++i) {
@@ -410,6 +425,56 @@ __device__ __forceinline__ void nearest_lds_batch(const float (&px)[NP], const f
                 if (i == k && (slow & (1u << i))) out[k] = r;
         }
     }
+}
+
+// Queue of unfinished searches of one wavefront (kSearchQueue entries, structure of arrays in LDS):
+// the point, the best distance so far, the best codeword's LDS address with the index slot the
+// answer goes to, and the rest of the list.
+constexpr int kSearchQueue = 64;
+struct SearchQueue {
+    float* x;
+    float* y;
+    float* bd;
+    uint32_t* a;   // bo | slot << 16
+    uint32_t* b;   // next | end << 16
+};
+__host__ __device__ constexpr size_t search_queue_bytes() { return (size_t)kSearchQueue * 5 * sizeof(uint32_t); }
+__device__ __forceinline__ SearchQueue search_queue_at(char* p) {
+    SearchQueue q;
+    q.x = reinterpret_cast<float*>(p);
+    q.y = q.x + kSearchQueue;
+    q.bd = q.y + kSearchQueue;
+    q.a = reinterpret_cast<uint32_t*>(q.bd + kSearchQueue);
+    q.b = q.a + kSearchQueue;
+    return q;
+}
+
+// Finishes the n queued searches, one per lane (n <= the wavefront size), and writes each answer
+// to idx[slot].  Called by the whole wavefront; the queue's entries are visible (wave_lds_sync).
+__device__ __forceinline__ void search_finish(const SearchQueue& q, int n, const SearchLds& s, uint16_t* idx,
+                                              int lane) {
+    const bool mine = lane < n;
+    float x = 0.0f, y = 0.0f, bd = 0.0f;
+    uint32_t a = 0, b = 0;
+    if (mine) {
+        x = q.x[lane];
+        y = q.y[lane];
+        bd = q.bd[lane];
+        a = q.a[lane];
+        b = q.b[lane];
+    }
+    uint32_t bo = a & 0xFFFFu;
+    const uint32_t next = b & 0xFFFFu;
+    const int rem = mine ? (int)((b >> 16) - next) : 0;
+    for (int t = 0; wave_any((uint32_t)(t < rem)); ++t) {
+        const uint32_t ad = s.ent[next + t];   // past its end for the shorter lists: harmless
+        const float d = dist_f32(x, y, cw_at(ad));
+        if (d < bd) {
+            bd = d;
+            bo = ad;
+        }
+    }
+    if (mine) idx[a >> 16] = (uint16_t)((bo - s.cb_lds) >> 3);
 }
 
 // ----------------------------------------------------------------------------- polar baseline
