@@ -368,29 +368,46 @@ def qgemm_workspace(M: int, d_out: int, d_in: int) -> int:
     return load().qamw_qgemm_workspace(M, d_out, d_in)
 
 
+class QgemmPlan:
+    """A checked qamw_qgemm call with its inputs, output and workspace fixed, launched by calling it:
+    the argument checks run once, so a loop over the same buffers (a serving step) costs only the
+    library call per launch.  Arguments as qgemm; the tensors are held until the plan is dropped."""
+
+    def __init__(self, x: torch.Tensor, codes: torch.Tensor, norm: torch.Tensor, sigma: torch.Tensor,
+                 codebook: torch.Tensor, bits: int, scale: Optional[torch.Tensor] = None,
+                 sign_seed: int = DEFAULT_SIGN_SEED, block: int = 0, out_dtype=torch.float32,
+                 out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+        if isinstance(x, torch.Tensor) and x.dim() == 1:
+            x = x.unsqueeze(0)
+        ld_x = _matrix(x, "x")
+        M, d_in = x.shape
+        d_out = _decode_inputs(codes, norm, sigma, codebook, bits, d_in, scale)
+        if out is None:
+            out = torch.empty((M, d_out), dtype=out_dtype, device=x.device)
+        ld_y = _matrix(out, "out", rows=M, cols=d_out)
+        need = qgemm_workspace(M, d_out, d_in)
+        _arg(workspace, "workspace", torch.uint8, numel=need, optional=True)
+        _on_device(x=x, codes=codes, norm=norm, sigma=sigma, codebook=codebook, scale=scale, out=out,
+                   workspace=workspace)
+        ws = workspace if workspace is not None else _ws(need, x.device)
+        self.out = out
+        self._keep = (x, codes, norm, sigma, codebook, scale, ws)
+        self._fn = load().qamw_qgemm
+        self._args = (_ptr(x), _dt(x), M, ld_x, _ptr(codes), _ptr(norm), _ptr(sigma), _ptr(codebook), bits,
+                      _ptr(scale), d_out, d_in, block, sign_seed, _ptr(out), _dt(out), ld_y, _ptr(ws), ws.numel())
+
+    def __call__(self, stream=None) -> torch.Tensor:
+        rc = self._fn(*self._args, _stream(stream))
+        _check(rc, "qamw_qgemm")
+        return self.out
+
+
 def qgemm(x: torch.Tensor, codes: torch.Tensor, norm: torch.Tensor, sigma: torch.Tensor, codebook: torch.Tensor,
           bits: int, scale: Optional[torch.Tensor] = None, sign_seed: int = DEFAULT_SIGN_SEED, block: int = 0,
           out_dtype=torch.float32, out: Optional[torch.Tensor] = None,
           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """y = x W^T (section 1) with W the decoder's weights, W never formed.  x: M x d_in (bf16/fp32)."""
-    if isinstance(x, torch.Tensor) and x.dim() == 1:
-        x = x.unsqueeze(0)
-    ld_x = _matrix(x, "x")
-    M, d_in = x.shape
-    d_out = _decode_inputs(codes, norm, sigma, codebook, bits, d_in, scale)
-    if out is None:
-        out = torch.empty((M, d_out), dtype=out_dtype, device=x.device)
-    ld_y = _matrix(out, "out", rows=M, cols=d_out)
-    need = qgemm_workspace(M, d_out, d_in)
-    _arg(workspace, "workspace", torch.uint8, numel=need, optional=True)
-    _on_device(x=x, codes=codes, norm=norm, sigma=sigma, codebook=codebook, scale=scale, out=out,
-               workspace=workspace)
-    ws = workspace if workspace is not None else _ws(need, x.device)
-    rc = load().qamw_qgemm(_ptr(x), _dt(x), M, ld_x, _ptr(codes), _ptr(norm), _ptr(sigma), _ptr(codebook), bits,
-                           _ptr(scale), d_out, d_in, block, sign_seed, _ptr(out), _dt(out), ld_y, _ptr(ws), ws.numel(),
-                           _stream())
-    _check(rc, "qamw_qgemm")
-    return out
+    return QgemmPlan(x, codes, norm, sigma, codebook, bits, scale, sign_seed, block, out_dtype, out, workspace)()
 
 
 def qgemm_noalloc(x: torch.Tensor, codes: torch.Tensor, norm: torch.Tensor, sigma: torch.Tensor,
