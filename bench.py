@@ -338,6 +338,7 @@ def main():
             result["polar_%d_%d" % (ba, bp)] = polar_run(torch, q, sets, n_sets, scale, sign, block, ba, bp, timed,
                                                          stream)
         result["act_scale"] = act_scale_run(torch, q, sets[0], cb, bits, index, sign, block, timed)
+        result["qgemm_13b_layer"] = qgemm13b_run(torch, q, synth, cb, index, bits, block, timed, args.rot_gib)
         result["ablation"] = ablation_run(torch, q, sets[0], pts, cfg, cb, bits, scale, sign, block)
     del sets, ws
     torch.cuda.empty_cache()
@@ -608,6 +609,45 @@ def qgemm_run(torch, q, sets, n_sets, cb, bits, scale, sign, block, timed):
                           "hbm_frac": round(alg / (t_f * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                           "kernel": "vector units" if M < 6 else "matrix cores (fp32)"}
         del ws, tmp
+    return res
+
+
+def qgemm13b_run(torch, q, synth, cb, index, bits, block, timed, rot_gib):
+    """The fused product on the seven matrices of a 13B-shaped layer (q, k, v, o 5120x5120, gate and up
+    13824x5120, down 5120x13824) at M = 1, 4 and 16 activation rows, against hipBLASLt on the decoded
+    BF16 matrices; codes and weights rotate over >= rot_gib of copies."""
+    dev = cb.device
+    c3 = synth.config(3)
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    res = {}
+    for mm in c3.matrices:
+        w = mm.weights_device(dev)
+        s = torch.from_numpy(mm.channel_scale()).to(dev)
+        e = q.encode(w, cb, bits, index, scale=s, block=block)
+        d_out, d_in = w.shape
+        per = w.numel() * 2 + e["codes"].numel()
+        n = max(2, int(math.ceil(rot_gib * (1 << 30) / per)))
+        sets = [{"codes": e["codes"].clone(), "norm": e["norm"], "sigma": e["sigma"],
+                 "wd": q.decode(e["codes"], e["norm"], e["sigma"], cb, bits, d_in, scale=s, block=block)} for _ in range(n)]
+        del w
+        row = {}
+        for M in (1, 4, 16):
+            x = torch.randn((M, d_in), device=dev, generator=g).to(torch.bfloat16)
+            y = torch.empty((M, d_out), dtype=torch.float32, device=dev)
+            ws = torch.empty((q.qgemm_workspace(M, d_out, d_in),), dtype=torch.uint8, device=dev)
+            plans = [q.QgemmPlan(x, b["codes"], b["norm"], b["sigma"], cb, bits, scale=s, block=block, out=y,
+                                 workspace=ws) for b in sets]
+            t_f = timed(lambda i: plans[i % n]())
+            t_b = timed(lambda i: torch.matmul(x, sets[i % n]["wd"].t()))
+            alg = d_out * q.row_stride(d_in, bits) + d_out * 2 + M * d_in * 2 + M * d_out * 4
+            row["M%d" % M] = {"qgemm_us": round(t_f * 1e3, 2), "bf16_matmul_us": round(t_b * 1e3, 2),
+                              "speedup_vs_bf16": round(t_b / t_f, 3),
+                              "hbm_frac": round(alg / (t_f * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+            del plans, ws
+        res["%s %dx%d" % (mm.name, d_out, d_in)] = row
+        del sets, e
+        torch.cuda.empty_cache()
     return res
 
 

@@ -63,8 +63,8 @@ def test_grouped_matches_single_block128(q, orc, bits):
 
 
 def test_grouped_default_blocks_and_fp32(q, orc):
-    """block 0: 384 and 640 columns take block 128 (grouped), 512, 256 and 1024 their own larger
-    default (a launch each); fp32 output."""
+    """block 0: 384 and 640 columns take block 128 and 256 columns block 256 (grouped launches of each
+    block size), 512 and 1024 their own larger default (a launch each); fp32 output."""
     bits = 11
     rng = np.random.default_rng(7)
     cb_np = rng.standard_normal((1 << bits, 2)).astype(np.float32)

@@ -108,6 +108,8 @@ SHAPES = [  # d_out, d_in, block, bits
     (8, 5120, 0, 11), (4, 16384, 1024, 12), (2, 28672, 1024, 11),
     # the 128-column decoder: ragged 16-row tiles, one and three column blocks, every supported width
     (17, 128, 128, 11), (33, 384, 128, 8), (100, 1280, 128, 7), (47, 2560, 128, 11),
+    # ... and its 256-column form (two 128-column halves per block): spans of 2 and 4 halves
+    (33, 512, 256, 8), (70, 768, 256, 11), (17, 1024, 256, 7), (9, 11008, 256, 11),
 ]
 
 

@@ -536,7 +536,7 @@ size_t decode_lds_bytes(int L, int bits, int d_in) {
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int L, hipStream_t st) {
-    if (decode128_supported(a, L)) return launch_decode128(a, st);
+    if (decode128_supported(a, L)) return launch_decode128(a, L, st);
     switch (L) {
     case 1: return decode_L<1>(a, st);
     case 2: return decode_L<2>(a, st);

@@ -156,9 +156,10 @@ struct Smem128 {
 // A launch decodes b.n matrices; matrix m owns workgroups b.it[m].wg0 .. + n_wg - 1.  Within it a
 // workgroup w takes the NBW-block span (w / 8) % n_span and the tile groups listed below, wavefront
 // v of the workgroup taking tile 4 group + v.
-template <int BITS, bool OBF, int NBW, bool CF_LDS, bool SG_LDS, int NI>
+template <int BITS, bool OBF, int NBW, bool CF_LDS, bool SG_LDS, int NI, int L>
 __global__ __launch_bounds__(kD128Threads) __attribute__((amdgpu_waves_per_eu(D128_MIN_WAVES)))
 void k_decode128(const Decode128Batch<NI> b) {
+    static_assert(L == 7 || (L == 8 && NBW >= 2), "blocks of 256 columns are two 128-column blocks of one span");
     int m = 0;
     if constexpr (NI > 1) {
         for (int i = 1; i < b.n; ++i) m = (int)blockIdx.x >= b.it[i].wg0 ? i : m;
@@ -253,7 +254,7 @@ void k_decode128(const Decode128Batch<NI> b) {
 #pragma unroll
         for (int e = 0; e < NS; ++e)
             if ((64 * NBW) % T == 0 || e * T + t < 64 * NBW)
-                sg_l[e * T + t] = (double)sgv[e] * 0.088388347648318440550;   // sigma_k / sqrt(128)
+                sg_l[e * T + t] = (double)sgv[e] * (L == 7 ? 0.088388347648318440550 : 0.0625);   // sigma_k / sqrt(b)
     }
     __syncthreads();
     // phase-A pairs of the lane: 16 q + i of block bb
@@ -329,6 +330,18 @@ void k_decode128(const Decode128Batch<NI> b) {
         for (int j = 0; j < 32; ++j)
             if (!(j & 8)) swap_lanes32(x[j], x[j + 8]);               // register bit 3 <- element bit 6
         butterfly<32>(x, 3);                                          // stage 6
+        if constexpr (L == 8) {
+            // b = 256: the two 128-column halves of the block are blocks bb and bb ^ 1 of the span, in
+            // lanes l and l ^ 1 with the same element positions: the last stage (element bit 7) adds
+            // the partner's element (lower half) or subtracts this lane's from it (upper half)
+            const double sgn = (bb & 1) ? -1.0 : 1.0;
+#pragma unroll
+            for (int j = 0; j < 32; ++j) {
+                const int lo = __builtin_amdgcn_update_dpp(0, (int)__double2loint(x[j]), 0xB1, 0xF, 0xF, false);
+                const int hi = __builtin_amdgcn_update_dpp(0, (int)__double2hiint(x[j]), 0xB1, 0xF, 0xF, false);
+                x[j] = __builtin_fma(x[j], sgn, __hiloint2double(hi, lo));   // quad_perm [1,0,3,2]: lane ^ 1
+            }
+        }
         // eps_j / s_j, fp32 rounding, output type; staged run by run.  fma(x, c, +0) is x c rounded
         // once, except that a zero product is +0: a zero row (norm 0) decodes to +0.
         f32x4 cfv[CF_LDS ? 8 : 1];
@@ -400,9 +413,9 @@ void k_decode128(const Decode128Batch<NI> b) {
     }
 }
 
-template <int BITS, bool OBF, int NBW, int NI>
+template <int BITS, bool OBF, int NBW, int NI, int L>
 hipError_t launch128(const Decode128Batch<NI>& bt, int n_wg, hipStream_t st) {
-    auto kern = k_decode128<BITS, OBF, NBW, D128_CF_LDS, D128_SG_LDS, NI>;
+    auto kern = k_decode128<BITS, OBF, NBW, D128_CF_LDS, D128_SG_LDS, NI, L>;
     const size_t smem = ((size_t)1 << BITS) * 16 + Smem128<NBW, OBF, D128_CF_LDS, D128_SG_LDS>::bytes;
     allow_lds(kern, smem);
     hipLaunchKernelGGL(kern, dim3(n_wg), dim3(kD128Threads), smem, st, bt);
@@ -410,18 +423,22 @@ hipError_t launch128(const Decode128Batch<NI>& bt, int n_wg, hipStream_t st) {
 }
 
 template <int NI>
-hipError_t dispatch128(const Decode128Batch<NI>& bt, int bits, int nbw, bool obf, int n_wg, hipStream_t st) {
-#define QAMW_D128_CASE(B, W)                                                                  \
-    if (bits == B && nbw == W)                                                                \
-        return obf ? launch128<B, true, W, NI>(bt, n_wg, st) : launch128<B, false, W, NI>(bt, n_wg, st);
-    QAMW_D128_CASE(7, 1) QAMW_D128_CASE(7, 2) QAMW_D128_CASE(7, 4)
-    QAMW_D128_CASE(8, 1) QAMW_D128_CASE(8, 2) QAMW_D128_CASE(8, 4)
-    QAMW_D128_CASE(11, 1) QAMW_D128_CASE(11, 2) QAMW_D128_CASE(11, 4)
+hipError_t dispatch128(const Decode128Batch<NI>& bt, int bits, int nbw, int L, bool obf, int n_wg, hipStream_t st) {
+#define QAMW_D128_CASE(B, W, LL)                                                                          \
+    if (bits == B && nbw == W && L == LL)                                                                 \
+        return obf ? launch128<B, true, W, NI, LL>(bt, n_wg, st) : launch128<B, false, W, NI, LL>(bt, n_wg, st);
+    QAMW_D128_CASE(7, 1, 7) QAMW_D128_CASE(7, 2, 7) QAMW_D128_CASE(7, 4, 7)
+    QAMW_D128_CASE(8, 1, 7) QAMW_D128_CASE(8, 2, 7) QAMW_D128_CASE(8, 4, 7)
+    QAMW_D128_CASE(11, 1, 7) QAMW_D128_CASE(11, 2, 7) QAMW_D128_CASE(11, 4, 7)
+    QAMW_D128_CASE(7, 2, 8) QAMW_D128_CASE(7, 4, 8)
+    QAMW_D128_CASE(8, 2, 8) QAMW_D128_CASE(8, 4, 8)
+    QAMW_D128_CASE(11, 2, 8) QAMW_D128_CASE(11, 4, 8)
 #undef QAMW_D128_CASE
     return hipErrorInvalidValue;
 }
 
-// span width: 4 blocks (1 KB of BF16 per row per store instruction) when the row allows
+// span width in 128-column blocks: 4 (1 KB of BF16 per row per store instruction) when the row
+// allows; at least 2 for 256-column Hadamard blocks (nb is even there)
 int span_blocks(int nb) { return nb % 4 == 0 ? 4 : (nb % 2 == 0 ? 2 : 1); }
 
 // The matrix's descriptor and workgroup count (a multiple of 8: one per XCD for every tile group).
@@ -461,36 +478,36 @@ Decode128Item make_item(const DecodeArgs& d, int wg0) {
 bool decode128_supported(const DecodeArgs& d, int L) {
     // buffer offsets are 32-bit: codes and output below 2 GiB
     const size_t esz = d.out_bf16 ? 2 : 4;
-    return L == 7 && (d.bits == 7 || d.bits == 8 || d.bits == 11) && d.d_in % 128 == 0 &&
+    return (L == 7 || L == 8) && (d.bits == 7 || d.bits == 8 || d.bits == 11) && d.d_in % (1 << L) == 0 &&
            (size_t)d.d_out * d.stride < ((size_t)1 << 31) && (size_t)d.d_out * (size_t)d.ld * esz < ((size_t)1 << 31);
 }
 
-hipError_t launch_decode128(const DecodeArgs& d, hipStream_t st) {
+hipError_t launch_decode128(const DecodeArgs& d, int L, hipStream_t st) {
     Decode128Batch<1> bt{};
     bt.cb = d.cb;
     bt.n = 1;
     bt.it[0] = make_item(d, 0);
     if (bt.it[0].n_wg == 0) return hipSuccess;
-    return dispatch128(bt, d.bits, span_blocks(bt.it[0].nb), d.out_bf16 != 0, bt.it[0].n_wg, st);
+    return dispatch128(bt, d.bits, span_blocks(bt.it[0].nb), L, d.out_bf16 != 0, bt.it[0].n_wg, st);
 }
 
-hipError_t launch_decode128_many(const DecodeArgs* d, int n, hipStream_t st) {
-    // consecutive matrices of one span width share a launch, at most kDecodeBatch of them
+hipError_t launch_decode128_many(const DecodeArgs* d, const int* L, int n, hipStream_t st) {
+    // consecutive matrices of one span width and block size share a launch, at most kDecodeBatch
     Decode128Batch<kDecodeBatch> bt{};
     int i = 0;
     while (i < n) {
-        const int nbw = span_blocks(d[i].d_in / 128);
+        const int nbw = span_blocks(d[i].d_in / 128), li = L[i];
         bt.cb = d[i].cb;
         bt.n = 0;
         int wg = 0;
-        for (; i < n && bt.n < kDecodeBatch && span_blocks(d[i].d_in / 128) == nbw; ++i) {
+        for (; i < n && bt.n < kDecodeBatch && span_blocks(d[i].d_in / 128) == nbw && L[i] == li; ++i) {
             const Decode128Item it = make_item(d[i], wg);
             if (it.n_wg == 0) continue;
             bt.it[bt.n++] = it;
             wg += it.n_wg;
         }
         if (bt.n == 0) continue;
-        const hipError_t e = dispatch128(bt, d[0].bits, nbw, d[0].out_bf16 != 0, wg, st);
+        const hipError_t e = dispatch128(bt, d[0].bits, nbw, li, d[0].out_bf16 != 0, wg, st);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

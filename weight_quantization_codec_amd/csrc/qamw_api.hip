@@ -473,7 +473,7 @@ int qamw_decode_many(const qamw_decode_job* jobs, int32_t n_jobs, const float* d
         }
         size_t k = i;   // a run of jobs the grouped 128-column decoder takes
         while (k < args.size() && decode128_supported(args[k], ls[k])) ++k;
-        const int rc = hip_rc(launch_decode128_many(args.data() + i, (int)(k - i), st));
+        const int rc = hip_rc(launch_decode128_many(args.data() + i, ls.data() + i, (int)(k - i), st));
         if (rc) return rc;
         i = k;
     }

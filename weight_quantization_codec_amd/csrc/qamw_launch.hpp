@@ -109,10 +109,10 @@ struct Decode128Batch {
     Decode128Item it[NI];
 };
 bool decode128_supported(const DecodeArgs& a, int L);
-hipError_t launch_decode128(const DecodeArgs& a, hipStream_t st);
-// Decodes that share codebook, bits and output type, each accepted by decode128_supported, as
-// launches of up to kDecodeBatch matrices.
-hipError_t launch_decode128_many(const DecodeArgs* a, int n, hipStream_t st);
+hipError_t launch_decode128(const DecodeArgs& a, int L, hipStream_t st);
+// Decodes that share codebook, bits and output type, each accepted by decode128_supported (with the
+// log2 block sizes L[i]), as launches of up to kDecodeBatch matrices.
+hipError_t launch_decode128_many(const DecodeArgs* a, const int* L, int n, hipStream_t st);
 hipError_t launch_sign_mask(uint64_t seed, int d_in, uint32_t* bits, hipStream_t st);
 hipError_t launch_polar_codebook(int ba, int bp, double* levels, double* thr, float* cb, hipStream_t st);
 hipError_t launch_scalar_codebook(int b, double* levels, double* thr, float* cb, hipStream_t st);
