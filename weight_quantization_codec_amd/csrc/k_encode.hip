@@ -21,6 +21,7 @@ namespace qamw {
 namespace {
 
 constexpr int kMaxWaves = 16;
+constexpr size_t kGroupCountBytes = 64;   // the encoder's per-row-group counters (R <= 16)
 constexpr int kCalibMaxGroups = 256;
 
 // Sum over the wavefront in a fixed order, the same value returned to every lane.  DPP moves
@@ -160,10 +161,14 @@ __device__ __forceinline__ void scale_raw(const RawW<E, BF>& r, const double (&c
 // returns sum a^2 over the whole row (fixed shuffle tree, then wavefronts in order).  With SPLIT
 // the LDS transpose runs for lanes 0-31 and then for lanes 32-63 (a block's lanes never straddle
 // the two), so the wavefront's exchange buffer covers 32 lanes: half the LDS.
+// With a group counter (gcnt) the wavefronts of the row wait only for each other: each publishes
+// its partial sum and adds 1 to the group's LDS counter, which reaches nwaves * (pass + 1) once the
+// whole row's partials of this pass are in; otherwise the workgroup synchronizes.
 template <int L, bool BF, bool SPLIT = false>
 __device__ __forceinline__ double front_end(const RawW<Layout<L>::E, BF>& raw, bool active, int tid,
                                             const double (&cf)[Layout<L>::E], double (&x)[Layout<L>::E],
-                                            double* red, double* xb, int nwaves) {
+                                            double* red, double* xb, int nwaves, int* gcnt = nullptr,
+                                            int target = 0) {
     using Lo = Layout<L>;
     constexpr int E = Lo::E;
     double ss = 0.0;
@@ -174,7 +179,10 @@ __device__ __forceinline__ double front_end(const RawW<Layout<L>::E, BF>& raw, b
         for (int m = 0; m < E; ++m) x[m] = 0.0;
     }
     ss = wave_sum(ss);
-    if ((tid & (kWave - 1)) == 0) red[tid / kWave] = ss;
+    if ((tid & (kWave - 1)) == 0) {
+        red[tid / kWave] = ss;
+        if (gcnt) __hip_atomic_fetch_add(gcnt, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
     if constexpr (Lo::two_phase) {
         // The stages commute: stage 0 (element bit 0) runs last, in phase B, so the two halves
         // (bit 0 = 0 or 1) stay apart until then and each half is exchanged while the other one
@@ -233,7 +241,12 @@ __device__ __forceinline__ double front_end(const RawW<Layout<L>::E, BF>& raw, b
 #pragma unroll
         for (int r = 0; r < L; ++r) butterfly<E>(x, r);
     }
-    __syncthreads();
+    if (gcnt) {
+        while (__hip_atomic_load(gcnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < target)
+            __builtin_amdgcn_s_sleep(1);
+    } else {
+        __syncthreads();
+    }
     double r2 = 0.0;
     for (int v = 0; v < nwaves; ++v) r2 += red[v];
     return r2;
@@ -521,6 +534,9 @@ __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a, int T, int R) {
     double2 isg_reg[NP / 2];
     double2* isg_lds = reinterpret_cast<double2*>(reinterpret_cast<char*>(red_all + 2 * R * kMaxWaves) +
                                                   (size_t)(blockDim.x / kWave) * wave_bytes);
+    // per row group, the count of wavefronts that have published their pass's norm partial
+    int* gcnt = reinterpret_cast<int*>(reinterpret_cast<char*>(isg_lds) + (ISG_LDS ? (size_t)T * NP * sizeof(double) : 0)) + grp;
+    if (tid == 0) *gcnt = 0;
 #pragma unroll
     for (int i = 0; i < NP / 2; ++i) {
         const double i0 = 1.0 / (double)a.sigma[min(col_B<L>(tid, 4 * i) / 2, n_pairs - 1)];
@@ -546,7 +562,7 @@ __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a, int T, int R) {
         double x[E];
         int32_t rf = 0;
         double* red = red_all + ((pass & 1) * R + grp) * kMaxWaves;
-        const double r2 = front_end<L, BF, true>(nxt, active && rv, tid, cf, x, red, xb, nwaves);
+        const double r2 = front_end<L, BF, true>(nxt, active && rv, tid, cf, x, red, xb, nwaves, gcnt, nwaves * (pass + 1));
         // the next row, in flight during the search and the packing (its registers were free
         // during the front end)
         load_row_raw<E, BF, VEC>(a.w, a.ld, a.d_in, a.d_out, row + rstride, tid, nxt);
@@ -706,7 +722,7 @@ size_t encode_smem(size_t front, int bits, int R, int nwaves_total, bool isg_lds
     using Lo = Layout<L>;
     const size_t isg = isg_lds ? (size_t)(nwaves_total / R) * kWave * (Lo::E / 2) * sizeof(double) : 0;
     return front + (size_t)2 * R * kMaxWaves * sizeof(double) +
-           (size_t)nwaves_total * encode_wave_bytes(Lo::E, Lo::two_phase, bits) + isg;
+           (size_t)nwaves_total * encode_wave_bytes(Lo::E, Lo::two_phase, bits) + isg + kGroupCountBytes;
 }
 
 // LDS of the quantizer's tables
@@ -858,7 +874,8 @@ size_t encode_lds_bytes(int L, int bits, int d_in, int polar_bp) {
     if (E <= 0) return 0;
     const int nwaves = ((d_in / E) + kWave - 1) / kWave;
     const size_t front = polar_bp >= 1 ? polar_lds_bytes(polar_bp) : search_lds_bytes(1 << bits, index_grid_size(bits));
-    return front + 2 * kMaxWaves * sizeof(double) + (size_t)nwaves * encode_wave_bytes(E, L > 4, bits);
+    return front + 2 * kMaxWaves * sizeof(double) + (size_t)nwaves * encode_wave_bytes(E, L > 4, bits) +
+           kGroupCountBytes;
 }
 
 namespace {
