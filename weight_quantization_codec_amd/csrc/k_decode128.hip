@@ -33,20 +33,19 @@ namespace qamw {
 
 namespace {
 
-#ifndef D128_WAVES
-#define D128_WAVES 4
-#endif
-constexpr int kD128Waves = D128_WAVES;         // wavefronts per workgroup
-#ifndef D128_CF_LDS
-#define D128_CF_LDS true
-#endif
-#ifndef D128_SG_LDS
-#define D128_SG_LDS false
-#endif
-#ifndef D128_MIN_WAVES
-#define D128_MIN_WAVES 3
-#endif
-constexpr int kD128Threads = kWave * kD128Waves;
+// Two launch shapes.  4 wavefronts per workgroup with sigma_k in registers (158-164 VGPRs, three
+// wavefronts per SIMD, three workgroups per CU): the matrices of the 13B shapes and grouped
+// launches.  8 wavefronts with sigma_k in LDS (at most 128 VGPRs, four per SIMD, two workgroups
+// per CU): a lone small matrix, where more wavefronts with fewer tiles each overlap better.
+template <int W>
+struct D128Shape {
+    static constexpr int waves = W;
+    static constexpr int threads = kWave * W;
+    static constexpr bool sg_lds = W == 8;
+    static constexpr int wg_per_cu = W == 8 ? 2 : 3;
+};
+constexpr bool kD128CfLds = true;   // eps_j / s_j from LDS (frees 32 registers per lane)
+
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -138,7 +137,7 @@ __device__ __forceinline__ void unpack128(const uint32_t (&dw)[Lane128<BITS>::ND
 //   cf    eps_j / s_j (fp32) of the span's 128 NBW columns   (kept when CF_LDS, else set-up only)
 //   sg    sigma_k / sqrt(128) (double) of its 64 NBW pairs  (kept when SG_LDS, else set-up only)
 //   stage per wavefront, one tile: R rows x NBW blocks x 128 columns, each block padded by 16 bytes
-template <int NBW, bool OBF, bool CF_LDS, bool SG_LDS>
+template <int NBW, bool OBF, bool CF_LDS, bool SG_LDS, int WAVES>
 struct Smem128 {
     static constexpr int R = 16 / NBW;
     static constexpr int ESZ = OBF ? 2 : 4;
@@ -149,15 +148,15 @@ struct Smem128 {
     static constexpr int SG = 64 * NBW * 8;
     static constexpr int setup = CF + SG;
     static constexpr int keep = SG_LDS ? CF + SG : (CF_LDS ? CF : 0);   // persists past the set-up
-    static constexpr int body = keep + kD128Waves * STAGE;
+    static constexpr int body = keep + WAVES * STAGE;
     static constexpr int bytes = setup > body ? setup : body;
 };
 
 // A launch decodes b.n matrices; matrix m owns workgroups b.it[m].wg0 .. + n_wg - 1.  Within it a
 // workgroup w takes the NBW-block span (w / 8) % n_span and the tile groups listed below, wavefront
 // v of the workgroup taking tile 4 group + v.
-template <int BITS, bool OBF, int NBW, bool CF_LDS, bool SG_LDS, int NI, int L>
-__global__ __launch_bounds__(kD128Threads) __attribute__((amdgpu_waves_per_eu(D128_MIN_WAVES)))
+template <int BITS, bool OBF, int NBW, bool CF_LDS, bool SG_LDS, int NI, int L, int WAVES>
+__global__ __launch_bounds__(kWave * WAVES) __attribute__((amdgpu_waves_per_eu(WAVES == 8 ? 4 : 3)))
 void k_decode128(const Decode128Batch<NI> b) {
     static_assert(L == 7 || (L == 8 && NBW >= 2), "blocks of 256 columns are two 128-column blocks of one span");
     int m = 0;
@@ -165,7 +164,7 @@ void k_decode128(const Decode128Batch<NI> b) {
         for (int i = 1; i < b.n; ++i) m = (int)blockIdx.x >= b.it[i].wg0 ? i : m;
     }
     const Decode128Item& a = b.it[m];
-    using SM = Smem128<NBW, OBF, CF_LDS, SG_LDS>;
+    using SM = Smem128<NBW, OBF, CF_LDS, SG_LDS, WAVES>;
     constexpr int R = SM::R, ESZ = SM::ESZ;
     constexpr int K = 1 << BITS;
     extern __shared__ __align__(16) char smem[];
@@ -195,8 +194,8 @@ void k_decode128(const Decode128Batch<NI> b) {
     const uint32_t s0 = (uint32_t)(16 * (q * BITS & 1));
     const int n_tiles = (a.d_out + R - 1) / R;
     const int n_groups_launched = a.n_wg / n_span;   // a multiple of 8
-    int tile = kD128Waves * group + wave_in;
-    const uint32_t tile_step = (uint32_t)(kD128Waves * n_groups_launched);
+    int tile = WAVES * group + wave_in;
+    const uint32_t tile_step = (uint32_t)(WAVES * n_groups_launched);
     const __amdgpu_buffer_rsrc_t crs =
         __builtin_amdgcn_make_buffer_rsrc((void*)a.codes, (short)0, (int)((size_t)a.d_out * a.stride), 0x00020000);
     const __amdgpu_buffer_rsrc_t nrs =
@@ -219,7 +218,7 @@ void k_decode128(const Decode128Batch<NI> b) {
     // ---- set-up: codebook table (stage 0), eps_j / s_j of the span's columns, sigma of its pairs.
     // Fixed trip counts: every thread's loads are in flight at once.
     {
-        constexpr int T = kD128Threads;
+        constexpr int T = kWave * WAVES;
         constexpr int NE = (K + T - 1) / T, NC = (128 * NBW + T - 1) / T, NS = (64 * NBW + T - 1) / T;
         const int t = (int)threadIdx.x;
         // without a scale the descriptor has no records and its loads read 0
@@ -413,28 +412,40 @@ void k_decode128(const Decode128Batch<NI> b) {
     }
 }
 
-template <int BITS, bool OBF, int NBW, int NI, int L>
+template <int BITS, bool OBF, int NBW, int NI, int L, int W>
 hipError_t launch128(const Decode128Batch<NI>& bt, int n_wg, hipStream_t st) {
-    auto kern = k_decode128<BITS, OBF, NBW, D128_CF_LDS, D128_SG_LDS, NI, L>;
-    const size_t smem = ((size_t)1 << BITS) * 16 + Smem128<NBW, OBF, D128_CF_LDS, D128_SG_LDS>::bytes;
+    using S = D128Shape<W>;
+    auto kern = k_decode128<BITS, OBF, NBW, kD128CfLds, S::sg_lds, NI, L, W>;
+    const size_t smem = ((size_t)1 << BITS) * 16 + Smem128<NBW, OBF, kD128CfLds, S::sg_lds, W>::bytes;
     allow_lds(kern, smem);
-    hipLaunchKernelGGL(kern, dim3(n_wg), dim3(kD128Threads), smem, st, bt);
+    hipLaunchKernelGGL(kern, dim3(n_wg), dim3(S::threads), smem, st, bt);
     return hipGetLastError();
 }
 
-template <int NI>
-hipError_t dispatch128(const Decode128Batch<NI>& bt, int bits, int nbw, int L, bool obf, int n_wg, hipStream_t st) {
-#define QAMW_D128_CASE(B, W, LL)                                                                          \
-    if (bits == B && nbw == W && L == LL)                                                                 \
-        return obf ? launch128<B, true, W, NI, LL>(bt, n_wg, st) : launch128<B, false, W, NI, LL>(bt, n_wg, st);
+template <int NI, int WV, bool OBF>
+hipError_t dispatch128_o(const Decode128Batch<NI>& bt, int bits, int nbw, int L, int n_wg, hipStream_t st) {
+#define QAMW_D128_CASE(B, W, LL) \
+    if (bits == B && nbw == W && L == LL) return launch128<B, OBF, W, NI, LL, WV>(bt, n_wg, st);
     QAMW_D128_CASE(7, 1, 7) QAMW_D128_CASE(7, 2, 7) QAMW_D128_CASE(7, 4, 7)
     QAMW_D128_CASE(8, 1, 7) QAMW_D128_CASE(8, 2, 7) QAMW_D128_CASE(8, 4, 7)
     QAMW_D128_CASE(11, 1, 7) QAMW_D128_CASE(11, 2, 7) QAMW_D128_CASE(11, 4, 7)
-    QAMW_D128_CASE(7, 2, 8) QAMW_D128_CASE(7, 4, 8)
-    QAMW_D128_CASE(8, 2, 8) QAMW_D128_CASE(8, 4, 8)
-    QAMW_D128_CASE(11, 2, 8) QAMW_D128_CASE(11, 4, 8)
+    if constexpr (WV == 4 && OBF) {   // 256-column blocks: BF16 out, 4 wavefronts (the rest spill)
+        QAMW_D128_CASE(7, 2, 8) QAMW_D128_CASE(7, 4, 8)
+        QAMW_D128_CASE(8, 2, 8) QAMW_D128_CASE(8, 4, 8)
+        QAMW_D128_CASE(11, 2, 8) QAMW_D128_CASE(11, 4, 8)
+    }
 #undef QAMW_D128_CASE
     return hipErrorInvalidValue;
+}
+
+template <int NI, int WV>
+hipError_t dispatch128(const Decode128Batch<NI>& bt, int bits, int nbw, int L, bool obf, int n_wg, hipStream_t st) {
+    if constexpr (WV == 8) {   // BF16 output only (fp32 output spills at 8 wavefronts)
+        return obf ? dispatch128_o<NI, 8, true>(bt, bits, nbw, L, n_wg, st) : hipErrorInvalidValue;
+    } else {
+        return obf ? dispatch128_o<NI, 4, true>(bt, bits, nbw, L, n_wg, st)
+                   : dispatch128_o<NI, 4, false>(bt, bits, nbw, L, n_wg, st);
+    }
 }
 
 // span width in 128-column blocks: 4 (1 KB of BF16 per row per store instruction) when the row
@@ -442,7 +453,7 @@ hipError_t dispatch128(const Decode128Batch<NI>& bt, int bits, int nbw, int L, b
 int span_blocks(int nb) { return nb % 4 == 0 ? 4 : (nb % 2 == 0 ? 2 : 1); }
 
 // The matrix's descriptor and workgroup count (a multiple of 8: one per XCD for every tile group).
-Decode128Item make_item(const DecodeArgs& d, int wg0) {
+Decode128Item make_item(const DecodeArgs& d, int wg0, int waves) {
     Decode128Item it{};
     it.codes = d.codes;
     it.norm = d.norm;
@@ -458,11 +469,11 @@ Decode128Item make_item(const DecodeArgs& d, int wg0) {
     const int R = 16 / nbw;
     const int n_span = it.nb / nbw;
     const int n_tiles = (d.d_out + R - 1) / R;
-    const int n_groups = (n_tiles + kD128Waves - 1) / kD128Waves;   // a tile per wavefront
+    const int n_groups = (n_tiles + waves - 1) / waves;   // a tile per wavefront
     // about 12 (4 wavefronts per workgroup) or 16 (8) wavefronts per CU are resident: aim at that
     // many workgroups, the tiles spread evenly over them; groups per span in multiples of 8 (one
     // per XCD)
-    int per_span = 256 * (kD128Waves == 8 ? 2 : 3) / n_span;
+    int per_span = 256 * (waves == 8 ? D128Shape<8>::wg_per_cu : D128Shape<4>::wg_per_cu) / n_span;
     if (per_span < 8) per_span = 8;
     if (per_span > n_groups) per_span = n_groups;
     const int iters = (n_groups + per_span - 1) / per_span;
@@ -478,7 +489,9 @@ Decode128Item make_item(const DecodeArgs& d, int wg0) {
 bool decode128_supported(const DecodeArgs& d, int L) {
     // buffer offsets are 32-bit: codes and output below 2 GiB
     const size_t esz = d.out_bf16 ? 2 : 4;
-    return (L == 7 || L == 8) && (d.bits == 7 || d.bits == 8 || d.bits == 11) && d.d_in % (1 << L) == 0 &&
+    // b = 256 with fp32 output goes to k_decode (this kernel would spill there)
+    return (L == 7 || (L == 8 && d.out_bf16)) && (d.bits == 7 || d.bits == 8 || d.bits == 11) &&
+           d.d_in % (1 << L) == 0 &&
            (size_t)d.d_out * d.stride < ((size_t)1 << 31) && (size_t)d.d_out * (size_t)d.ld * esz < ((size_t)1 << 31);
 }
 
@@ -486,9 +499,17 @@ hipError_t launch_decode128(const DecodeArgs& d, int L, hipStream_t st) {
     Decode128Batch<1> bt{};
     bt.cb = d.cb;
     bt.n = 1;
-    bt.it[0] = make_item(d, 0);
+    // the 8-wavefront shape when it gives each workgroup at most two tile groups (a small matrix)
+    const Decode128Item i8 = make_item(d, 0, 8);
+    const int n_span = i8.nb / span_blocks(i8.nb);
+    const int R = 16 / span_blocks(i8.nb);
+    const int groups8 = ((d.d_out + R - 1) / R + 7) / 8;
+    const bool small = L == 7 && d.out_bf16 && i8.n_wg > 0 && (groups8 + i8.n_wg / n_span - 1) / (i8.n_wg / n_span) <= 2;
+    bt.it[0] = small ? i8 : make_item(d, 0, 4);
     if (bt.it[0].n_wg == 0) return hipSuccess;
-    return dispatch128(bt, d.bits, span_blocks(bt.it[0].nb), L, d.out_bf16 != 0, bt.it[0].n_wg, st);
+    const int nbw = span_blocks(bt.it[0].nb);
+    return small ? dispatch128<1, 8>(bt, d.bits, nbw, L, d.out_bf16 != 0, bt.it[0].n_wg, st)
+                 : dispatch128<1, 4>(bt, d.bits, nbw, L, d.out_bf16 != 0, bt.it[0].n_wg, st);
 }
 
 hipError_t launch_decode128_many(const DecodeArgs* d, const int* L, int n, hipStream_t st) {
@@ -501,13 +522,13 @@ hipError_t launch_decode128_many(const DecodeArgs* d, const int* L, int n, hipSt
         bt.n = 0;
         int wg = 0;
         for (; i < n && bt.n < kDecodeBatch && span_blocks(d[i].d_in / 128) == nbw && L[i] == li; ++i) {
-            const Decode128Item it = make_item(d[i], wg);
+            const Decode128Item it = make_item(d[i], wg, 4);
             if (it.n_wg == 0) continue;
             bt.it[bt.n++] = it;
             wg += it.n_wg;
         }
         if (bt.n == 0) continue;
-        const hipError_t e = dispatch128(bt, d[0].bits, nbw, li, d[0].out_bf16 != 0, wg, st);
+        const hipError_t e = dispatch128<kDecodeBatch, 4>(bt, d[0].bits, nbw, li, d[0].out_bf16 != 0, wg, st);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
