@@ -607,7 +607,7 @@ def qgemm_run(torch, q, sets, n_sets, cb, bits, scale, sign, block, timed):
                           "speedup_vs_bf16": round(t_b / t_f, 3), "speedup_vs_decode_matmul": round(t_d / t_f, 3),
                           "hbm_GBps": round(alg / (t_f * 1e-3) / 1e9, 1),
                           "hbm_frac": round(alg / (t_f * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                          "kernel": "vector units" if M < 6 else "matrix cores (fp32)"}
+                          "kernel": "matrix cores (bf16 pieces)"}
         del ws, tmp
     return res
 

@@ -217,12 +217,12 @@ int qamw_sign_mask(uint64_t sign_seed, int32_t d_in, uint32_t* d_bits, void* str
  * decoder's arguments as there), computed without forming W^: the activation is rotated instead,
  * u = sigma . blockdiag(H_b)(eps . x / s) (fp64, rounded to fp32 once), and
  *   y[m][i] = f16(norm_i) * sum_k (c[idx_ik].x u_m,2k + c[idx_ik].y u_m,2k+1)
- * summed in fp32 (up to 5 rows on the vector units: 32 pairs per lane, then a fixed-order wavefront
- * sum, rows longer than the LDS tile adding per-split partial sums in a fixed order; from 6 rows on
- * the matrix cores, v_mfma_f32_16x16x4f32 with per-wavefront partials added in a fixed order).
- * Every one of the d_in products rounds at most once on its way, so the error against the exact
- * product is at most (d_in + 64) 2^-24 times f16(norm_i) sum_k |c[idx_ik].x u_m,2k| + |c.y u_m,2k+1|
- * (measured: below 1e-7 of that sum).
+ * on the matrix cores (v_mfma_f32_16x16x32_bf16) with each fp32 operand written as a sum of bf16
+ * pieces: c = c1 + c2 (within 2^-18 |c|), u = u1 + u2 + u3 (exact) for M <= 5, u1 + u2 (within
+ * 2^-18 |u|) above; piece products are exact and the sums run in fp32, per-wavefront partials
+ * added in a fixed order, so results do not depend on timing.  The error against the exact product
+ * is at most (2^-16.9 + (6 d_in + 16) 2^-24) times f16(norm_i) sum_k |c[idx_ik].x u_m,2k| +
+ * |c.y u_m,2k+1| (measured: below 3e-6 of that sum).
  * Arguments:
  *   d_x, x_dtype, M, ld_x   M x d_in activations (QAMW_F32 or QAMW_BF16), row m at d_x + m ld_x.
  *                           1 <= M <= 16 (QAMW_ERR_UNSUPPORTED above; M = 0 is a no-op).
@@ -242,7 +242,7 @@ int qamw_qgemm(const void* d_x, qamw_dtype x_dtype, int32_t M, int64_t ld_x, con
  * ws_bytes arguments, same result bit for bit.  Its workspace is an array of
  * QAMW_QGEMM_NOALLOC_BYTES bytes that the library holds on each device from its first call there
  * until the process ends; the call itself allocates nothing.  Shapes whose qamw_qgemm_workspace
- * exceeds that size return QAMW_ERR_WORKSPACE (4 MiB covers M <= 16 up to 8192 x 28672 weights).
+ * exceeds that size return QAMW_ERR_WORKSPACE (4 MiB covers d_in <= 65536 at any M <= 16).
  * `stream` must belong to the current device (NULL: its default stream); otherwise, or when the
  * array's address cannot be obtained, QAMW_ERR_HIP.  All calls on a device share its array: calls
  * that may run at the same time on one device (different streams, threads without ordering) race

@@ -226,9 +226,11 @@ def test_qgemm_noops_and_workspace(lib):
     assert _qg(lib, M=0, x=None, y=None, ws=None) == q.OK
     assert _qg(lib, d_out=0, codes=None, norm=None, ws=None) == q.OK
     assert lib.qamw_qgemm_workspace(0, 16, 256) >= 0
-    assert lib.qamw_qgemm_workspace(1, 4096, 4096) >= 4096 * 4
-    # 13824 columns at 16 rows: the rotated activations of all 16 rows
-    assert lib.qamw_qgemm_workspace(16, 5120, 13824) >= 16 * 13824 * 4
+    # the B operands: 8 KiB per chunk of 128 pairs and operand group (one group up to 8 rows, two
+    # above)
+    assert lib.qamw_qgemm_workspace(1, 4096, 4096) == 16 * 8192
+    assert lib.qamw_qgemm_workspace(16, 5120, 13824) == 54 * 2 * 8192
+    assert lib.qamw_qgemm_workspace(8, 5120, 1000) == 4 * 8192
     assert lib.qamw_qgemm_workspace(1, 16, 255) == 0
 
 
@@ -247,10 +249,10 @@ def test_qgemm_noalloc_checks_and_size_limit(lib):
                                       a["yd"], a["ldy"], None)
     assert call(M=17) == UNSUP and call(bits=13) == UNSUP and call(block=3) == ARG and call(codes=None) == ARG
     assert call(M=0) == q.OK and call(d_out=0) == q.OK
-    big = 131072   # 16 x 131072 activations need 8 MiB of rotated fragments
+    big = 131072   # 16 x 131072 activations need 8 MiB of B operands
     assert lib.qamw_qgemm_workspace(16, 64, big) > q.QGEMM_NOALLOC_BYTES
     assert call(M=16, d_in=big, ldx=big, d_out=64, ldy=64, block=1024) == WS
-    assert lib.qamw_qgemm_workspace(16, 28672, 8192) <= q.QGEMM_NOALLOC_BYTES
+    assert lib.qamw_qgemm_workspace(16, 28672, 65536) == q.QGEMM_NOALLOC_BYTES
 
 
 def test_scalar_codebook_rejects(lib):

@@ -279,7 +279,6 @@ int qgemm_run(const void* d_x, qamw_dtype x_dtype, int32_t M, int64_t ld_x, cons
     a.y = d_y;
     a.y_bf16 = y_dtype == QAMW_BF16;
     a.ld_y = ld_y;
-    a.partial = reinterpret_cast<float*>(reinterpret_cast<char*>(d_ws) + ((size_t)M * d_in * sizeof(float) + 255) / 256 * 256);
     QgemmRotateArgs r{};
     r.x = d_x;
     r.x_bf16 = x_dtype == QAMW_BF16;

@@ -129,13 +129,11 @@ struct QgemmArgs {
     const uint16_t* norm;
     const float* cb;
     int bits;
-    float* u;            // M x d_in: the rotated, sigma-scaled activations
+    float* u;            // workspace: the rotated, sigma-scaled activations as bf16-piece B operands
     int M, n_pairs, d_out;
-    int n_pass, pps;     // passes of 2048 pairs per row; passes per split (set by the launcher)
     void* y;
     int y_bf16;
     int64_t ld_y;
-    float* partial;      // splits x M x d_out, or null when a row fits one split
 };
 struct QgemmRotateArgs {
     const void* x;
@@ -146,11 +144,6 @@ struct QgemmRotateArgs {
     uint64_t sign_seed;
     const float* sigma;
 };
-struct QgemmPlan {
-    int n_pass, mt, mtiles, pps, splits, grid_x;
-};
-size_t qgemm_lds_bytes(int bits, int mt, int pps);
-QgemmPlan qgemm_plan(int M, int d_out, int d_in);
 size_t qgemm_workspace(int M, int d_out, int d_in);
 hipError_t launch_qgemm(const QgemmArgs& a, const QgemmRotateArgs& r, hipStream_t st);
 
