@@ -146,17 +146,20 @@ __device__ __forceinline__ void qg_load(__amdgpu_buffer_rsrc_t rs, uint32_t off,
 // qx_mode.  Lane l = 16 q + j supplies A row j and B column j for the k-slots of its 4 pairs of
 // the step, and holds D[4 q + v][j] (v = 0..3).  Per step and operand group: one instruction with
 // A = c1, one with A = c2.
-// Workgroup: one tile of 16 weight rows, kQxWaves wavefronts taking the chunks w, w + kQxWaves, ...
+// Workgroup: one tile of 16 weight rows, WAVES wavefronts taking the chunks w, w + WAVES, ...
 // (lane (j, q) reads the codes of row j for pairs 32 q .. 32 q + 31 of the chunk: BITS dwords,
 // dword-aligned); each wavefront loads the next chunk's codes and B operands while it works on the
 // current one.  The partial D of the wavefronts are added in LDS in wavefront order, then the
 // pieces of each column.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-constexpr int kQxWaves = 8;
+// Wavefronts per workgroup: 4, or 8 for rows of 40 chunks and more (measured on the 4096², 5120²,
+// 13824 x 5120 and 5120 x 13824 products at M = 1, 4 and 16: 4 was up to 7% faster on the shorter
+// rows, 8 up to 4% on the longest).
+constexpr int kQxLongRow = 40;
 
-size_t qx_lds_bytes(int bits, int ng) {
-    return (size_t)(1 << bits) * sizeof(uint2) + (size_t)kQxWaves * ng * kWave * sizeof(f32x4) +
+size_t qx_lds_bytes(int bits, int ng, int waves) {
+    return (size_t)(1 << bits) * sizeof(uint2) + (size_t)waves * ng * kWave * sizeof(f32x4) +
            (size_t)ng * 256 * sizeof(float);
 }
 
@@ -204,8 +207,10 @@ __device__ __forceinline__ void qx_steps(const uint2* __restrict__ cb_l, const u
     }
 }
 
-template <int BITS, int NG>
-__global__ __launch_bounds__(kQxWaves * kWave) void k_qgemm_mx(QgemmArgs a) {
+template <int BITS, int NG, int WAVES>
+__global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(NG == 1 ? 4 : 3)))
+void k_qgemm_mx(QgemmArgs a) {
+    constexpr int kQxWaves = WAVES;
     extern __shared__ __align__(16) char smem[];
     constexpr int K = 1 << BITS;
     constexpr int kThreads = kQxWaves * kWave;
@@ -348,19 +353,19 @@ size_t qgemm_workspace(int M, int d_out, int d_in) {   // the B operands of k_qg
 }
 
 namespace {
+template <int BITS, int NG, int WAVES>
+hipError_t qgemm_mx_launch(const QgemmArgs& a, hipStream_t st) {
+    const size_t smem = qx_lds_bytes(BITS, NG, WAVES);
+    allow_lds(k_qgemm_mx<BITS, NG, WAVES>, smem);
+    hipLaunchKernelGGL((k_qgemm_mx<BITS, NG, WAVES>), dim3((a.d_out + 15) / 16), dim3(WAVES * kWave), smem, st, a);
+    return hipGetLastError();
+}
+
 template <int BITS>
 hipError_t qgemm_mx_B(const QgemmArgs& a, hipStream_t st) {
-    const int ng = qx_mode(a.M).ng;
-    const size_t smem = qx_lds_bytes(BITS, ng);
-    const int n_tiles = (a.d_out + 15) / 16;
-    if (ng == 1) {
-        allow_lds(k_qgemm_mx<BITS, 1>, smem);
-        hipLaunchKernelGGL((k_qgemm_mx<BITS, 1>), dim3(n_tiles), dim3(kQxWaves * kWave), smem, st, a);
-    } else {
-        allow_lds(k_qgemm_mx<BITS, 2>, smem);
-        hipLaunchKernelGGL((k_qgemm_mx<BITS, 2>), dim3(n_tiles), dim3(kQxWaves * kWave), smem, st, a);
-    }
-    return hipGetLastError();
+    const bool two = qx_mode(a.M).ng == 2, wide = (a.n_pairs + 127) / 128 >= kQxLongRow;
+    if (two) return wide ? qgemm_mx_launch<BITS, 2, 8>(a, st) : qgemm_mx_launch<BITS, 2, 4>(a, st);
+    return wide ? qgemm_mx_launch<BITS, 1, 8>(a, st) : qgemm_mx_launch<BITS, 1, 4>(a, st);
 }
 
 }  // namespace
