@@ -139,10 +139,11 @@ def test_qgemm_every_index_width(q, orc, bits, M):
     _check_f32(orc, x, y, ref, pr)
 
 
-@pytest.mark.parametrize("d_out,M", [(8229, 1), (8229, 3), (32851, 8)])
+@pytest.mark.parametrize("d_out,M", [(8229, 1), (8229, 3), (32851, 8), (5120, 3), (13824, 16)])
 def test_qgemm_tall_matrices(q, orc, d_out, M):
-    """Tall matrices: one workgroup per tile of 16 rows (8229 rows: 515 tiles, the last with 5 rows;
-    32851 rows: 2054 tiles, the last with 3)."""
+    """Tall matrices: whole rounds of 16-row tiles over the 256 compute units, the rows left over in
+    one round of shorter tiles (8229 rows: 512 tiles, then 37 of one row; 32851: 2048, then 83 of
+    one; 5120: 256, then 256 of four; 13824: 768, then 256 of six)."""
     log("qgemm tall %d rows M=%d" % (d_out, M))
     pr = _problem(orc, 900 + M, d_out, 256, 64, 6)
     x, y, ref = _run(q, orc, pr, M, seed=M)

@@ -157,6 +157,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // 13824 x 5120 and 5120 x 13824 products at M = 1, 4 and 16: 4 was up to 7% faster on the shorter
 // rows, 8 up to 4% on the longest).
 constexpr int kQxLongRow = 40;
+constexpr int kComputeUnits = 256;   // MI355X
 
 size_t qx_lds_bytes(int bits, int ng, int waves) {
     return (size_t)(1 << bits) * sizeof(uint2) + (size_t)waves * ng * kWave * sizeof(f32x4) +
@@ -209,7 +210,7 @@ __device__ __forceinline__ void qx_steps(const uint2* __restrict__ cb_l, const u
 
 template <int BITS, int NG, int WAVES>
 __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(NG == 1 ? 4 : 3)))
-void k_qgemm_mx(QgemmArgs a) {
+void k_qgemm_mx(QgemmArgs a, int full, int tail_h) {
     constexpr int kQxWaves = WAVES;
     extern __shared__ __align__(16) char smem[];
     constexpr int K = 1 << BITS;
@@ -222,8 +223,11 @@ void k_qgemm_mx(QgemmArgs a) {
     const int j = lane & 15, q = lane >> 4;
     const QxMode md = qx_mode(a.M);
     const int n_chunks = (a.n_pairs + 127) / 128;
-    const int tile = blockIdx.x, row0 = tile * 16;
-    const int nrows = a.d_out - row0 < 16 ? a.d_out - row0 : 16;
+    // workgroups below `full` own 16 rows, the rest `tail_h` rows each (rows past d_out: none)
+    const int tile = blockIdx.x;
+    const int row0 = tile < full ? tile * 16 : full * 16 + (tile - full) * tail_h;
+    const int h = tile < full ? 16 : tail_h;
+    const int nrows = a.d_out - row0 < h ? a.d_out - row0 : h;
 
     // Every global load goes through a buffer descriptor, unconditionally (offsets past the range
     // read zeros), so that the loop has no branches around loads and the waits count exactly.
@@ -357,7 +361,17 @@ template <int BITS, int NG, int WAVES>
 hipError_t qgemm_mx_launch(const QgemmArgs& a, hipStream_t st) {
     const size_t smem = qx_lds_bytes(BITS, NG, WAVES);
     allow_lds(k_qgemm_mx<BITS, NG, WAVES>, smem);
-    hipLaunchKernelGGL((k_qgemm_mx<BITS, NG, WAVES>), dim3((a.d_out + 15) / 16), dim3(WAVES * kWave), smem, st, a);
+    // Whole rounds of 16-row tiles over the compute units; the rows left over go to one more round
+    // of shorter tiles, so that no unit takes two full tiles while others take one.
+    const int tiles = (a.d_out + 15) / 16;
+    int full = tiles, tail_h = 16, n_wg = tiles;
+    if (tiles > kComputeUnits && tiles % kComputeUnits) {
+        full = tiles / kComputeUnits * kComputeUnits;
+        const int rest = a.d_out - full * 16;
+        tail_h = (rest + kComputeUnits - 1) / kComputeUnits;
+        n_wg = full + (rest + tail_h - 1) / tail_h;
+    }
+    hipLaunchKernelGGL((k_qgemm_mx<BITS, NG, WAVES>), dim3(n_wg), dim3(WAVES * kWave), smem, st, a, full, tail_h);
     return hipGetLastError();
 }
 
