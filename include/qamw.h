@@ -217,7 +217,8 @@ int qamw_sign_mask(uint64_t sign_seed, int32_t d_in, uint32_t* d_bits, void* str
  * decoder's arguments as there), computed without forming W^: the activation is rotated instead,
  * u = sigma . blockdiag(H_b)(eps . x / s) (fp64, rounded to fp32 once), and
  *   y[m][i] = f16(norm_i) * sum_k (c[idx_ik].x u_m,2k + c[idx_ik].y u_m,2k+1)
- * on the matrix cores (v_mfma_f32_16x16x32_bf16) with each fp32 operand written as a sum of bf16
+ * on the matrix cores (v_mfma_f32_16x16x32_bf16; from 9 rows on matrices of more than 4096 rows,
+ * v_mfma_f32_32x32x16_bf16) with each fp32 operand written as a sum of bf16
  * pieces: c = c1 + c2 (within 2^-18 |c|), u = u1 + u2 + u3 (exact) for M <= 5, u1 + u2 (within
  * 2^-18 |u|) above; piece products are exact and the sums run in fp32, per-wavefront partials
  * added in a fixed order, so results do not depend on timing.  The error against the exact product

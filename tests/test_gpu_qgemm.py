@@ -129,21 +129,24 @@ def test_qgemm_matches_oracle(q, orc, case):
     log("  max error %.3g of the absolute term sum" % rel)
 
 
-@pytest.mark.parametrize("M", [2, 12])
+@pytest.mark.parametrize("M,d_out,d_in", [(2, 12, 4416), (12, 12, 4416), (12, 4100, 320)])
 @pytest.mark.parametrize("bits", list(range(1, 13)))
-def test_qgemm_every_index_width(q, orc, bits, M):
-    """Every index width, with two and with twelve activation rows (one and two operand groups);
-    4416 columns: 2208 pairs, 17 chunks of 128 and a ragged 18th of 32."""
-    pr = _problem(orc, 500 + bits, 12, 4416, 64, bits)
+def test_qgemm_every_index_width(q, orc, bits, M, d_out, d_in):
+    """Every index width on the three kernel layouts: two activation rows (one operand group), twelve
+    on 12 weight rows (two operand groups; 4416 columns: 2208 pairs, 17 chunks of 128 and a ragged
+    18th of 32) and twelve on 4100 weight rows (32-row tiles; 320 columns: two chunks of 64 and a
+    ragged third of 32)."""
+    pr = _problem(orc, 500 + bits, d_out, d_in, 64, bits)
     x, y, ref = _run(q, orc, pr, M, seed=bits)
     _check_f32(orc, x, y, ref, pr)
 
 
-@pytest.mark.parametrize("d_out,M", [(8229, 1), (8229, 3), (32851, 8), (5120, 3), (13824, 16)])
+@pytest.mark.parametrize("d_out,M", [(8229, 1), (8229, 3), (32851, 8), (5120, 3), (8229, 9), (13824, 16), (2000, 1)])
 def test_qgemm_tall_matrices(q, orc, d_out, M):
-    """Tall matrices: whole rounds of 16-row tiles over the 256 compute units, the rows left over in
-    one round of shorter tiles (8229 rows: 512 tiles, then 37 of one row; 32851: 2048, then 83 of
-    one; 5120: 256, then 256 of four; 13824: 768, then 256 of six)."""
+    """Tall matrices: whole rounds of tiles over the 256 compute units, the rows left over in one
+    round of shorter tiles.  16-row tiles: 8229 rows are 512 tiles, then 37 of one row; 32851 are
+    2048, then 83 of one; 5120 are 256, then 256 of four; 2000 are 250 of eight.  32-row tiles
+    (M > 8): 8229 rows are 256 tiles, then 37 of one; 13824 are 256, then 256 of 22."""
     log("qgemm tall %d rows M=%d" % (d_out, M))
     pr = _problem(orc, 900 + M, d_out, 256, 64, 6)
     x, y, ref = _run(q, orc, pr, M, seed=M)

@@ -35,17 +35,30 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 // gives every piece product c_i u_p in one instruction; the sum over the pieces of a row is taken
 // at the end.
 struct QxMode {
-    int ng, np;
+    int ng, np, w32;   // operand groups, u pieces, 32-row tiles (k_qgemm_mx32)
 };
-__device__ __host__ __forceinline__ QxMode qx_mode(int M) {
-    return QxMode{M > 8 ? 2 : 1, M <= 5 ? 3 : 2};
+// Above 8 rows: 32-row tiles once the 16-row tiles would take more than one round of the 256
+// compute units (measured: on 4096 rows the 32-row tiles were 37% slower, half empty; from 5120
+// rows on they were equal or up to 20% faster), two operand groups of 16-row tiles below.
+__device__ __host__ __forceinline__ QxMode qx_mode(int M, int d_out) {
+    if (M > 8) return d_out > 16 * 256 ? QxMode{1, 2, 1} : QxMode{2, 2, 0};
+    return QxMode{1, M <= 5 ? 3 : 2, 0};
 }
+// pairs per chunk
+__device__ __host__ __forceinline__ int qx_chunk(QxMode md) { return md.w32 ? 64 : 128; }
 // Operand lane order (one chunk = 128 pairs, 8 steps of 16 pairs): lane l = 16 q + j holds, for
 // step s, the k-slots of pairs 128 c + 32 q + 4 s + (0..3), components (x, y) in the low and high
 // halves of each dword.  A: j = weight row of the tile; B: j = column.  The B operand of (chunk c,
 // step s, group g) is 64 lanes x 4 dwords at entry ((c * 8 + s) * ng + g) * 64 + lane; the dword
 // of pair k, piece p of activation row m:
+// With 32-row tiles (k_qgemm_mx32, v_mfma_f32_32x32x16_bf16) a chunk is 64 pairs: lane l = 32 q + j
+// holds the k-slots of pairs 64 c + 32 q + 4 s + (0..3), B column j = 2 m + p, at entry (c * 8 + s) *
+// 64 + lane.
 __device__ __forceinline__ size_t qx_dword(QxMode md, int m, int k, int p) {
+    if (md.w32) {
+        const int c = k >> 6, kk = k & 63, q = kk >> 5, t = kk & 31;
+        return ((size_t)(c * 8 + (t >> 2)) * kWave + q * 32 + 2 * m + p) * 4 + (t & 3);
+    }
     const int g = md.ng == 2 ? m >> 3 : 0, mm = md.ng == 2 ? m & 7 : m;
     const int c = k >> 7, kk = k & 127, q = kk >> 5, t = kk & 31;
     const size_t entry = ((size_t)(c * 8 + (t >> 2)) * md.ng + g) * kWave + q * 16 + md.np * mm + p;
@@ -58,10 +71,10 @@ __device__ __forceinline__ size_t qx_dword(QxMode md, int m, int k, int p) {
 // (whole blocks; columns past d_in are zeros, columns past `cols` are not written).  Butterflies:
 // distance 1 in registers, 2 .. 64 between lanes of a wavefront through its own LDS slice (no
 // barrier), 128 .. 512 across wavefronts (one barrier each); two LDS buffers alternate.
-__global__ __launch_bounds__(512) void k_qgemm_rotate_mx(const void* __restrict__ x, int x_bf16, int64_t ld_x, int M,
-                                                         int d_in, int cols, int b, const float* __restrict__ s,
-                                                         uint64_t sign_seed, const float* __restrict__ sigma,
-                                                         uint32_t* __restrict__ uf) {
+__global__ __launch_bounds__(512) void k_qgemm_rotate_mx(const void* __restrict__ x, int x_bf16, int64_t ld_x,
+                                                         QxMode md, int d_in, int cols, int b,
+                                                         const float* __restrict__ s, uint64_t sign_seed,
+                                                         const float* __restrict__ sigma, uint32_t* __restrict__ uf) {
     __shared__ double2 ex[2][512];
     const int m = blockIdx.y, t = threadIdx.x;
     const int k = blockIdx.x * blockDim.x + t;   // the thread's pair
@@ -96,7 +109,6 @@ __global__ __launch_bounds__(512) void k_qgemm_rotate_mx(const void* __restrict_
         v[1] = hi ? p.y - v[1] : v[1] + p.y;
     }
     if (2 * k >= cols) return;
-    const QxMode md = qx_mode(M);
     float rx = 0.0f, ry = 0.0f;
     if (2 * k < d_in) {
         const double rs = 1.0 / __builtin_sqrt((double)b);
@@ -221,7 +233,7 @@ void k_qgemm_mx(QgemmArgs a, int full, int tail_h) {
     float* dsum = reinterpret_cast<float*>(part + kQxWaves * NG * kWave);                   // NG x 16 x 16
     const int lane = threadIdx.x & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int j = lane & 15, q = lane >> 4;
-    const QxMode md = qx_mode(a.M);
+    const QxMode md = qx_mode(a.M, a.d_out);
     const int n_chunks = (a.n_pairs + 127) / 128;
     // workgroups below `full` own 16 rows, the rest `tail_h` rows each (rows past d_out: none)
     const int tile = blockIdx.x;
@@ -349,35 +361,185 @@ void k_qgemm_mx(QgemmArgs a, int full, int tail_h) {
     }
 }
 
+// 9 to 16 activation rows: v_mfma_f32_32x32x16_bf16, D[32 x 32] += A[32 x 16] B[16 x 32], a tile of
+// 32 weight rows, so that each B operand (the u pieces, 2 KB per 16 pairs at 16 rows) serves twice
+// the weight rows of the 16-row layout.  Lane l = 32 q + j supplies A row j and B column j = 2 m + p
+// for the k-slots of its 4 pairs of the step (pairs 64 c + 32 q + 4 s + (0..3) of a 64-pair chunk:
+// lane (j, q) reads row j's codes for 32 pairs, BITS dwords, dword-aligned) and holds D[8 (v / 4) +
+// 4 q + v % 4][j] (v = 0..15).  Otherwise as k_qgemm_mx with one operand group.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+size_t qx32_lds_bytes(int bits, int waves) {
+    return (size_t)(1 << bits) * sizeof(uint2) + (size_t)waves * kWave * sizeof(f32x16) + 32 * 32 * sizeof(float);
+}
+__device__ __forceinline__ f32x16 qx_mfma32(const u32x4& a, const u32x4& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+}
+
+template <int BITS, int WAVES>
+__global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(3)))
+void k_qgemm_mx32(QgemmArgs a, int full, int tail_h) {
+    extern __shared__ __align__(16) char smem[];
+    constexpr int K = 1 << BITS;
+    constexpr int kThreads = WAVES * kWave;
+    constexpr uint32_t kOut = 0xFFFFF000u;
+    uint2* cb_l = reinterpret_cast<uint2*>(smem);                                  // K x {c1, c2}
+    f32x4* part = reinterpret_cast<f32x4*>(smem + (size_t)K * sizeof(uint2));     // waves x 64 lanes x 4
+    float* dsum = reinterpret_cast<float*>(part + WAVES * kWave * 4);              // 32 x 32
+    const int lane = threadIdx.x & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int j = lane & 31, q = lane >> 5;
+    const int n_chunks = (a.n_pairs + 63) / 64;
+    const int tile = blockIdx.x;
+    const int row0 = tile < full ? tile * 32 : full * 32 + (tile - full) * tail_h;
+    const int h = tile < full ? 32 : tail_h;
+    const int nrows = a.d_out - row0 < h ? a.d_out - row0 : h;
+
+    constexpr int kCbPer = (K + kThreads - 1) / kThreads;
+    const __amdgpu_buffer_rsrc_t cbr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)a.cb, (short)0, K * (int)sizeof(float2), 0x00020000);
+    u32x2 cv[kCbPer];
+#pragma unroll
+    for (int t = 0; t < kCbPer; ++t)
+        cv[t] = __builtin_amdgcn_raw_buffer_load_b64(cbr, (uint32_t)(threadIdx.x + t * kThreads) * 8u, 0, 0);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.codes + (size_t)row0 * a.stride), (short)0, nrows * (int)a.stride, 0x00020000);
+    const uint32_t row_off = (uint32_t)j * (uint32_t)a.stride;
+    const __amdgpu_buffer_rsrc_t ur = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)a.u, (short)0, n_chunks * 8 * kWave * (int)sizeof(u32x4), 0x00020000);
+    const bool on = j < 2 * a.M;   // B columns that carry data
+    auto load_b = [&](int c, bool ok, u32x4 (&dst)[8]) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const uint32_t off = ok && on ? (uint32_t)(((c * 8 + t) * kWave + lane) * (int)sizeof(u32x4)) : kOut;
+            dst[t] = __builtin_amdgcn_raw_buffer_load_b128(ur, off, 0, 0);
+        }
+    };
+    auto load_codes = [&](int c, bool ok, uint32_t (&dst)[BITS]) {
+        qg_load<BITS>(rs, ok ? row_off + (uint32_t)((2 * c + q) * BITS) * 4u : kOut, dst);
+    };
+    uint32_t d0[BITS], d1[BITS];
+    u32x4 b0[8], b1[8];
+    int c = wave;
+    load_codes(c, c < n_chunks, d0);
+    load_b(c, c < n_chunks, b0);
+#pragma unroll
+    for (int t = 0; t < kCbPer; ++t) {
+        const int k = threadIdx.x + t * kThreads;
+        const float x = __uint_as_float(cv[t][0]), y = __uint_as_float(cv[t][1]);
+        const uint32_t x1 = f32_to_bf16_rne(x), y1 = f32_to_bf16_rne(y);
+        const uint32_t x2 = f32_to_bf16_rne(x - __uint_as_float(x1 << 16));
+        const uint32_t y2 = f32_to_bf16_rne(y - __uint_as_float(y1 << 16));
+        if (k < K) cb_l[k] = make_uint2(x1 | (y1 << 16), x2 | (y2 << 16));
+    }
+    __syncthreads();
+
+    f32x16 acc = {};   // c1 and c2 products into one accumulator (two would spill)
+    auto chunk = [&](int cc, uint32_t (&d)[BITS], u32x4 (&b)[8], uint32_t (&dn)[BITS], u32x4 (&bn)[8]) {
+        const bool more = cc + WAVES < n_chunks;
+        load_codes(cc + WAVES, more, dn);
+        load_b(cc + WAVES, more, bn);
+        __builtin_amdgcn_sched_barrier(0);
+        u32x4 a1[2], a2[2];
+        qx_gather<BITS>(cb_l, d, 0, a1[0], a2[0]);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            if (t + 1 < 8) qx_gather<BITS>(cb_l, d, t + 1, a1[(t + 1) & 1], a2[(t + 1) & 1]);
+            acc = qx_mfma32(a1[t & 1], b[t], acc);
+            acc = qx_mfma32(a2[t & 1], b[t], acc);
+        }
+    };
+    for (; c < n_chunks; c += 2 * WAVES) {
+        chunk(c, d0, b0, d1, b1);
+        if (c + WAVES >= n_chunks) break;
+        chunk(c + WAVES, d1, b1, d0, b0);
+    }
+    // wavefront partials D = (c1 + c2) u, then the sum over the wavefronts in order
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+        part[(wave * kWave + lane) * 4 + v] = f32x4{acc[4 * v], acc[4 * v + 1], acc[4 * v + 2], acc[4 * v + 3]};
+    __syncthreads();
+    if (threadIdx.x < kWave) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            f32x4 sum = part[lane * 4 + v];
+            for (int w = 1; w < WAVES; ++w) {
+                const f32x4 p2 = part[(w * kWave + lane) * 4 + v];
+                sum[0] += p2[0];
+                sum[1] += p2[1];
+                sum[2] += p2[2];
+                sum[3] += p2[3];
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dsum[(8 * v + 4 * q + r) * 32 + j] = sum[r];
+        }
+    }
+    __syncthreads();
+    for (int o = threadIdx.x; o < a.M * 32; o += kThreads) {   // y[m][row0 + i] = f16(norm) (piece 0 + piece 1)
+        const int m = o >> 5, i = o & 31;
+        if (i < nrows) {
+            const float yv = (dsum[i * 32 + 2 * m] + dsum[i * 32 + 2 * m + 1]) *
+                             __half2float(__ushort_as_half(a.norm[row0 + i]));
+            if (a.y_bf16)
+                reinterpret_cast<uint16_t*>(a.y)[(size_t)m * a.ld_y + row0 + i] = f32_to_bf16_rne(yv);
+            else
+                reinterpret_cast<float*>(a.y)[(size_t)m * a.ld_y + row0 + i] = yv;
+        }
+    }
+}
+
 }  // namespace
 
 size_t qgemm_workspace(int M, int d_out, int d_in) {   // the B operands of k_qgemm_mx
-    (void)d_out;
-    return (size_t)((d_in / 2 + 127) / 128) * 8 * qx_mode(M).ng * kWave * sizeof(u32x4);
+    const QxMode md = qx_mode(M, d_out);
+    const int ch = qx_chunk(md);
+    return (size_t)((d_in / 2 + ch - 1) / ch) * 8 * md.ng * kWave * sizeof(u32x4);
 }
 
 namespace {
+// Tiles of at most T rows over the compute units: whole rounds of T-row tiles, then one round of
+// shorter tiles for the rows left over, so that no unit takes two full tiles while others take
+// one; fewer rows than one round fills are spread over a round of shorter tiles.
+struct QxTiling {
+    int full, tail_h, n_wg;
+};
+QxTiling qx_tiling(int d_out, int T) {
+    QxTiling t{0, 1, 0};
+    const int rounds = d_out / (kComputeUnits * T);
+    t.full = rounds * kComputeUnits;
+    const int rest = d_out - t.full * T;
+    t.tail_h = (rest + kComputeUnits - 1) / kComputeUnits;
+    if (t.tail_h < 1) t.tail_h = 1;
+    t.n_wg = t.full + (rest + t.tail_h - 1) / t.tail_h;
+    return t;
+}
+
 template <int BITS, int NG, int WAVES>
 hipError_t qgemm_mx_launch(const QgemmArgs& a, hipStream_t st) {
     const size_t smem = qx_lds_bytes(BITS, NG, WAVES);
     allow_lds(k_qgemm_mx<BITS, NG, WAVES>, smem);
-    // Whole rounds of 16-row tiles over the compute units; the rows left over go to one more round
-    // of shorter tiles, so that no unit takes two full tiles while others take one.
-    const int tiles = (a.d_out + 15) / 16;
-    int full = tiles, tail_h = 16, n_wg = tiles;
-    if (tiles > kComputeUnits && tiles % kComputeUnits) {
-        full = tiles / kComputeUnits * kComputeUnits;
-        const int rest = a.d_out - full * 16;
-        tail_h = (rest + kComputeUnits - 1) / kComputeUnits;
-        n_wg = full + (rest + tail_h - 1) / tail_h;
-    }
-    hipLaunchKernelGGL((k_qgemm_mx<BITS, NG, WAVES>), dim3(n_wg), dim3(WAVES * kWave), smem, st, a, full, tail_h);
+    const QxTiling t = qx_tiling(a.d_out, 16);
+    hipLaunchKernelGGL((k_qgemm_mx<BITS, NG, WAVES>), dim3(t.n_wg), dim3(WAVES * kWave), smem, st, a, t.full,
+                       t.tail_h);
+    return hipGetLastError();
+}
+
+template <int BITS, int WAVES>
+hipError_t qgemm_mx32_launch(const QgemmArgs& a, hipStream_t st) {
+    const size_t smem = qx32_lds_bytes(BITS, WAVES);
+    allow_lds(k_qgemm_mx32<BITS, WAVES>, smem);
+    const QxTiling t = qx_tiling(a.d_out, 32);
+    hipLaunchKernelGGL((k_qgemm_mx32<BITS, WAVES>), dim3(t.n_wg), dim3(WAVES * kWave), smem, st, a, t.full, t.tail_h);
     return hipGetLastError();
 }
 
 template <int BITS>
 hipError_t qgemm_mx_B(const QgemmArgs& a, hipStream_t st) {
-    const bool two = qx_mode(a.M).ng == 2, wide = (a.n_pairs + 127) / 128 >= kQxLongRow;
+    const QxMode md = qx_mode(a.M, a.d_out);
+    if (md.w32) {
+        const bool wide32 = (a.n_pairs + 63) / 64 >= 2 * kQxLongRow;
+        return wide32 ? qgemm_mx32_launch<BITS, 8>(a, st) : qgemm_mx32_launch<BITS, 4>(a, st);
+    }
+    const bool two = md.ng == 2, wide = (a.n_pairs + 127) / 128 >= kQxLongRow;
     if (two) return wide ? qgemm_mx_launch<BITS, 2, 8>(a, st) : qgemm_mx_launch<BITS, 2, 4>(a, st);
     return wide ? qgemm_mx_launch<BITS, 1, 8>(a, st) : qgemm_mx_launch<BITS, 1, 4>(a, st);
 }
@@ -385,9 +547,11 @@ hipError_t qgemm_mx_B(const QgemmArgs& a, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_qgemm(const QgemmArgs& a, const QgemmRotateArgs& r, hipStream_t st) {
-    const int cols = (r.d_in / 2 + 127) / 128 * 256;        // whole chunks of 128 pairs
+    const QxMode md = qx_mode(a.M, a.d_out);
+    const int ch = qx_chunk(md);
+    const int cols = (r.d_in / 2 + ch - 1) / ch * ch * 2;   // whole chunks
     const int T = r.block / 2 > 256 ? r.block / 2 : 256;   // threads: pairs per workgroup
-    hipLaunchKernelGGL(k_qgemm_rotate_mx, dim3((cols / 2 + T - 1) / T, a.M), dim3(T), 0, st, r.x, r.x_bf16, r.ld_x, a.M,
+    hipLaunchKernelGGL(k_qgemm_rotate_mx, dim3((cols / 2 + T - 1) / T, a.M), dim3(T), 0, st, r.x, r.x_bf16, r.ld_x, md,
                        r.d_in, cols, r.block, r.scale, r.sign_seed, r.sigma, reinterpret_cast<uint32_t*>(a.u));
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
 #define QAMW_QX(b) \
