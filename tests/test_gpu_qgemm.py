@@ -115,6 +115,8 @@ CASES = {
     "512_b64_B3_M16": (70, 512, 64, 3, 16, "bf16"),
     "1000_b8_B9_M8_ragged_chunk": (19, 1000, 8, 9, 8, "bf16"),
     "200_b8_B11_M6_one_ragged_chunk": (35, 200, 8, 11, 6, "bf16"),
+    "2_b2_B4_M3_one_pair": (5, 2, 2, 4, 3, "fp32"),
+    "64_b64_B12_M16": (4097, 64, 64, 12, 16, "bf16"),
 }
 
 
