@@ -228,10 +228,12 @@ int qamw_sign_mask(uint64_t sign_seed, int32_t d_in, uint32_t* d_bits, void* str
  *   d_x, x_dtype, M, ld_x   M x d_in activations (QAMW_F32 or QAMW_BF16), row m at d_x + m ld_x.
  *                           1 <= M <= 16 (QAMW_ERR_UNSUPPORTED above; M = 0 is a no-op).
  *   d_codes ... block       as qamw_decode (any block size 2..1024 dividing d_in; bits <= 12;
- *                           d_out <= QAMW_MAX_ROWS).
+ *                           d_out <= QAMW_MAX_ROWS; d_in <= QAMW_QGEMM_MAX_COLS, else
+ *                           QAMW_ERR_UNSUPPORTED).
  *   d_y, y_dtype, ld_y      M x d_out outputs, y[m][i] at d_y + m ld_y (ld_y >= d_out); BF16 is the
  *                           fp32 result rounded to nearest even.
  *   d_ws, ws_bytes          at least qamw_qgemm_workspace(M, d_out, d_in) bytes, 256-byte aligned. */
+#define QAMW_QGEMM_MAX_COLS (1 << 24)
 size_t qamw_qgemm_workspace(int32_t M, int32_t d_out, int32_t d_in);
 int qamw_qgemm(const void* d_x, qamw_dtype x_dtype, int32_t M, int64_t ld_x, const uint8_t* d_codes,
                const uint16_t* d_norm_f16, const float* d_sigma, const float* d_codebook, int32_t bits,

@@ -234,6 +234,14 @@ def test_qgemm_noops_and_workspace(lib):
     assert lib.qamw_qgemm_workspace(1, 16, 255) == 0
 
 
+def test_qgemm_column_limit(lib):
+    """Rows wider than QAMW_QGEMM_MAX_COLS (2^24) are refused before any HIP call: the product's
+    buffer offsets are 32-bit."""
+    big = (1 << 24) + 64
+    assert _qg(lib, d_in=big, ld_x=big) == UNSUP
+    assert _qg(lib, d_in=(1 << 24), ld_x=(1 << 24), ws=None) == WS
+
+
 def test_qgemm_noalloc_checks_and_size_limit(lib):
     """The static-workspace product checks its arguments as qamw_qgemm does and refuses shapes
     whose workspace exceeds the library's array, before any HIP call."""

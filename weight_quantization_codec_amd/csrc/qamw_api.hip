@@ -251,6 +251,8 @@ int qgemm_check(const void* d_x, qamw_dtype x_dtype, int32_t M, int64_t ld_x, co
     int rc = check_bits(bits);
     if (rc) return rc;
     if (M > 16) return QAMW_ERR_UNSUPPORTED;
+    // the product addresses a tile's codes and the B operands through 32-bit buffer offsets
+    if (d_in > QAMW_QGEMM_MAX_COLS) return QAMW_ERR_UNSUPPORTED;
     if (ld_x < d_in || ld_y < d_out) return QAMW_ERR_ARG;
     if (M == 0 || d_out == 0) return QAMW_OK;
     if (!d_x || !d_codes || !d_norm_f16 || !d_sigma || !d_codebook || !d_y) return QAMW_ERR_ARG;
