@@ -288,7 +288,7 @@ void k_qgemm_mx(QgemmArgs a, int full, int tail_h) {
         const uint32_t x1 = f32_to_bf16_rne(x), y1 = f32_to_bf16_rne(y);
         const uint32_t x2 = f32_to_bf16_rne(x - __uint_as_float(x1 << 16));
         const uint32_t y2 = f32_to_bf16_rne(y - __uint_as_float(y1 << 16));
-        if (k < K) cb_l[k] = make_uint2(x1 | (y1 << 16), x2 | (y2 << 16));
+        if (K % kThreads == 0 || k < K) cb_l[k] = make_uint2(x1 | (y1 << 16), x2 | (y2 << 16));
     }
     __syncthreads();
 
@@ -429,7 +429,7 @@ void k_qgemm_mx32(QgemmArgs a, int full, int tail_h) {
         const uint32_t x1 = f32_to_bf16_rne(x), y1 = f32_to_bf16_rne(y);
         const uint32_t x2 = f32_to_bf16_rne(x - __uint_as_float(x1 << 16));
         const uint32_t y2 = f32_to_bf16_rne(y - __uint_as_float(y1 << 16));
-        if (k < K) cb_l[k] = make_uint2(x1 | (y1 << 16), x2 | (y2 << 16));
+        if (K % kThreads == 0 || k < K) cb_l[k] = make_uint2(x1 | (y1 << 16), x2 | (y2 << 16));
     }
     __syncthreads();
 
