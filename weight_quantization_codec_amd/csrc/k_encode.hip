@@ -55,13 +55,28 @@ __device__ __forceinline__ double sqrt_pos(double q) {
     return q > 0.0 ? q * rr : 0.0;
 }
 
+// The sign mask of columns 0 .. d_in - 1 as bits in LDS, one 64-bit word per 64 columns, drawn
+// once per workgroup: thread t takes columns t, t + blockDim.x, ..., so a wavefront's 64
+// consecutive columns come out of one ballot (a lane of the encoder would otherwise draw all E of
+// its columns, and every row group the same ones).  The caller synchronizes the workgroup before
+// the words are read.
+__device__ __forceinline__ void sign_words(uint64_t seed, int d_in, uint64_t* words) {
+    const int lane = threadIdx.x & (kWave - 1);
+    for (int c0 = (int)threadIdx.x - lane; c0 < d_in; c0 += (int)blockDim.x) {
+        const int j = c0 + lane;
+        const uint64_t m = __builtin_amdgcn_ballot_w64(j < d_in && eps_negative(seed, (uint32_t)j));
+        if (lane == 0) words[c0 / kWave] = m;
+    }
+}
+
 // s_j * eps_j of the E consecutive columns tid*E .. tid*E + E - 1 of a lane (phase A), exact in
-// fp32: the scales with 16-byte buffer loads, the signs from the seed (once per kernel).
-// Columns at or past d_in get a scale of 1.  bad is set when a scale of the lane is not > 0
-// (NaN included).
+// fp32: the scales with 16-byte buffer loads, the signs from the words of sign_words (E divides
+// 64, so a lane's columns sit in one word).  Columns at or past d_in get a scale of 1 and no sign.
+// bad is set when a scale of the lane is not > 0 (NaN included).
 template <int E>
-__device__ __forceinline__ void load_cf(const float* scale, uint64_t sign_seed, int tid, int d_in, float (&cf)[E],
+__device__ __forceinline__ void load_cf(const float* scale, const uint64_t* words, int tid, int d_in, float (&cf)[E],
                                         bool& bad) {
+    static_assert(kWave % E == 0, "a lane's columns sit in one sign word");
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     const int j0 = tid * E;
     if (scale) {
@@ -81,9 +96,10 @@ __device__ __forceinline__ void load_cf(const float* scale, uint64_t sign_seed, 
         if (j0 + m >= d_in) cf[m] = 1.0f;
         bad |= !(cf[m] > 0.0f);
     }
+    const uint64_t sw = j0 < d_in ? words[j0 / kWave] >> (j0 % kWave) : 0;
 #pragma unroll
     for (int m = 0; m < E; ++m)
-        if (eps_negative(sign_seed, (uint32_t)(j0 + m))) cf[m] = -cf[m];
+        if ((sw >> m) & 1) cf[m] = -cf[m];
 }
 
 // Column of register m of this lane in the final (phase B) layout.
@@ -276,11 +292,16 @@ __global__ __launch_bounds__(MAXT) void k_calibrate(CalibArgs a, int T, int R) {
     if (active && base + grp < a.n_rows) load_raw<E, BF>(a.w, vec, (int64_t)(base + grp) * a.ld + (int64_t)tid * E, nxt);
     double cf[E];   // s_j * eps_j (exact in fp32; scales are checked by the encoder)
     {
+        // the sign words in the exchange buffers, free until the first front end
+        uint64_t* words = reinterpret_cast<uint64_t*>(xb_all);
+        sign_words(a.sign_seed, a.d_in, words);
+        __syncthreads();
         float cf32[E];
         bool bad_scale = false;
-        load_cf<E>(a.scale, a.sign_seed, tid, a.d_in, cf32, bad_scale);
+        load_cf<E>(a.scale, words, tid, a.d_in, cf32, bad_scale);
 #pragma unroll
         for (int m = 0; m < E; ++m) cf[m] = (double)cf32[m];
+        __syncthreads();
     }
     const double inv_sqrt_b = 1.0 / __builtin_sqrt((double)Lo::b);
     double acc[NP];
@@ -519,9 +540,14 @@ __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a, int T, int R) {
 
     double cf[E];   // s_j * eps_j (exact in fp32), held as doubles: converted once, not per row
     {
+        // the sign words in the wavefronts' buffers, free until the first front end (after the
+        // barrier that ends the set-up)
+        uint64_t* words = reinterpret_cast<uint64_t*>(red_all + 2 * R * kMaxWaves);
+        sign_words(a.sign_seed, a.d_in, words);
+        __syncthreads();
         float cf32[E];
         bool bad_scale = false;
-        load_cf<E>(a.scale, a.sign_seed, tid, a.d_in, cf32, bad_scale);
+        load_cf<E>(a.scale, words, tid, a.d_in, cf32, bad_scale);
         if (active && bad_scale && blockIdx.x == 0) flags |= 2;   // reported once
 #pragma unroll
         for (int m = 0; m < E; ++m) cf[m] = (double)cf32[m];
@@ -562,7 +588,9 @@ __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a, int T, int R) {
         double x[E];
         int32_t rf = 0;
         double* red = red_all + ((pass & 1) * R + grp) * kMaxWaves;
-        const double r2 = front_end<L, BF, true>(nxt, active && rv, tid, cf, x, red, xb, nwaves, gcnt, nwaves * (pass + 1));
+        // lanes past the row (whole blocks of their own) and rows past the matrix loaded zeros,
+        // so the front end runs on every lane: nothing of theirs is stored or searched
+        const double r2 = front_end<L, BF, true>(nxt, true, tid, cf, x, red, xb, nwaves, gcnt, nwaves * (pass + 1));
         // the next row, in flight during the search and the packing (its registers were free
         // during the front end)
         load_row_raw<E, BF, VEC>(a.w, a.ld, a.d_in, a.d_out, row + rstride, tid, nxt);
