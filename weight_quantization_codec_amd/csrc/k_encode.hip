@@ -697,33 +697,39 @@ __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a, int T, int R) {
         if (rv) flags |= rf;
         wave_lds_sync();
         // pack (LSB first): the wavefront's 32 E indices make E * bits words; lane l packs indices
-        // NP l .. NP l + NP - 1 (bits NP l bits onwards) through a 64-bit window, OR-ing each word
-        // it completes into LDS (the first and last ones are shared with the neighbouring lanes)
+        // NP l .. NP l + NP - 1 (bits NP l bits onwards), eight at a time: the eight indices form a
+        // run of 8 bits <= 96 bits (bits <= 12), which, shifted to its offset within its first word,
+        // covers at most four words; each non-zero word is OR-ed into LDS (a run's first and last
+        // words are shared with its neighbours).  A zero word is skipped, so no word past the
+        // wavefront's part is touched.
         for (int wd = lane; wd < E * bits; wd += kWave) wstage[wd] = 0;
         wave_lds_sync();
-        {
-            const uint32_t off = (uint32_t)(lane * NP * bits);
-            uint32_t w = off >> 5, nb = off & 31u;
-            uint64_t acc = 0;
 #pragma unroll 1
-            for (int v = 0; v < NP / 8; ++v) {   // eight indices (16 bytes) at a time
-                const u32x4 q = *reinterpret_cast<const u32x4*>(widx + NP * lane + 8 * v);
-                uint64_t lo = ((uint64_t)q[1] << 32) | q[0], hi = ((uint64_t)q[3] << 32) | q[2];
-#pragma unroll 1
-                for (int i = 0; i < 8; ++i) {
-                    acc |= (lo & 0xFFFFu) << nb;
-                    lo = (lo >> 16) | (hi << 48);
-                    hi >>= 16;
-                    nb += (uint32_t)bits;
-                    if (nb >= 32u) {
-                        __hip_atomic_fetch_or(wstage + w, (uint32_t)acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-                        acc >>= 32;
-                        nb -= 32u;
-                        ++w;
-                    }
-                }
+        for (int v = 0; v < NP / 8; ++v) {
+            const u32x4 q = *reinterpret_cast<const u32x4*>(widx + NP * lane + 8 * v);
+            // index i of the eight starts at bit i * bits of the run (a uniform choice between the
+            // run's low 64 bits, lo, and its bits from 32 on, hi)
+            uint64_t lo = 0, hi = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint64_t id = (q[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+                const int p = i * bits;
+                if (p < 32)
+                    lo |= id << p;
+                else
+                    hi |= id << (p - 32);
             }
-            if (nb > 0u) __hip_atomic_fetch_or(wstage + w, (uint32_t)acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            const uint32_t r0 = (uint32_t)lo, r1 = (uint32_t)(lo >> 32) | (uint32_t)hi, r2 = (uint32_t)(hi >> 32);
+            const uint32_t o = (uint32_t)((lane * NP + 8 * v) * bits), nb = o & 31u;
+            uint32_t* wp = wstage + (o >> 5);
+            const uint64_t s01 = (((uint64_t)r1 << 32) | r0) << nb;
+            const uint32_t w2 = (uint32_t)(((((uint64_t)r2 << 32) | r1) << nb) >> 32);
+            const uint32_t w3 = (uint32_t)(((uint64_t)r2 << nb) >> 32);
+            if ((uint32_t)s01) __hip_atomic_fetch_or(wp, (uint32_t)s01, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            if ((uint32_t)(s01 >> 32))
+                __hip_atomic_fetch_or(wp + 1, (uint32_t)(s01 >> 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            if (w2) __hip_atomic_fetch_or(wp + 2, w2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            if (w3) __hip_atomic_fetch_or(wp + 3, w3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         }
         wave_lds_sync();
         // 16-byte stores of the wavefront's 4 E bits bytes: E bits / 4 chunks, lane c storing
