@@ -169,7 +169,7 @@ __device__ __forceinline__ void scale_raw(const RawW<E, BF>& r, const double (&c
             f = __uint_as_float(r.u[m]);
         double a = (double)f * cf[m];   // exact: two 24-bit significands
         x[m] = a;
-        ss += a * a;
+        ss = __builtin_fma(a, a, ss);   // the order of the row's sum is the kernel's own anyway
     }
 }
 
@@ -204,32 +204,37 @@ __device__ __forceinline__ double front_end(const RawW<Layout<L>::E, BF>& raw, b
         // (bit 0 = 0 or 1) stay apart until then and each half is exchanged while the other one
         // is transformed.
         if constexpr (SPLIT) {
-            static_assert(32 % Lo::lanes == 0, "a block's lanes sit in one half of the wavefront");
-            const int lane = tid & (kWave - 1);
-            const Exchange<L> ex(xb, lane & 31);
-            const bool hi = lane >= 32;
+            // Two rounds per half through a buffer of 32 lanes' size: round r carries the elements
+            // of the lanes whose top q bit is r, and every lane reads in both rounds.  The round-1
+            // writers send the values they held before round 0 (`pre`).
+            const ExchangeHalf<L> ex(xb, tid & (kWave - 1));
+            double pre[E];
 #pragma unroll
             for (int r = 1; r < Lo::e; ++r) butterfly_half<E>(x, r, 0);
-            if (!hi) ex.write(x, 0);
+            if (!ex.top) ex.write(x, 0);
 #pragma unroll
             for (int r = 1; r < Lo::e; ++r) butterfly_half<E>(x, r, 1);
+#pragma unroll
+            for (int m = 0; m < E; ++m) pre[m] = x[m];
             wave_lds_sync();
-            if (!hi) ex.read(x, 0);
+            ex.read(x, 0, 0);
             wave_lds_sync();
-            if (hi) ex.write(x, 0);
+            if (ex.top) ex.write(pre, 0);
             wave_lds_sync();
-            if (hi) ex.read(x, 0);
+            ex.read(x, 0, 1);
+#pragma unroll
+            for (int m = 0; m < E; ++m) pre[m] = x[m];
             wave_lds_sync();
-            if (!hi) ex.write(x, 1);
+            if (!ex.top) ex.write(pre, 1);
 #pragma unroll
             for (int r = 1; r < Lo::e; ++r)
                 if (L - Lo::e + r >= Lo::e) butterfly_half<E>(x, r, 0);
             wave_lds_sync();
-            if (!hi) ex.read(x, 1);
+            ex.read(x, 1, 0);
             wave_lds_sync();
-            if (hi) ex.write(x, 1);
+            if (ex.top) ex.write(pre, 1);
             wave_lds_sync();
-            if (hi) ex.read(x, 1);
+            ex.read(x, 1, 1);
             wave_lds_sync();
         } else {
             const Exchange<L> ex(xb, tid & (kWave - 1));

@@ -199,6 +199,41 @@ struct Exchange {
     }
 };
 
+// The same transpose through a buffer of half the size, in two rounds that every lane of the
+// wavefront reads in.  Reader slot i of lane q takes source lane (q + i*lanes) / H, which has its top
+// q bit clear exactly for i < H/2: round r moves the elements of the source lanes whose top q bit is r
+// (they write all H of theirs) into reader slots r*H/2 .. r*H/2 + H/2 - 1.  Only the writes depend on
+// the lane, so no register has to be merged between lanes that read and lanes that did not.
+// Round-compact index of a block's element: writer ql = q mod lanes/2, element i -> beta*HB + ql*H + i;
+// reader slot r*H/2 + j -> beta*HB + q + j*lanes; stored at c + c/H (one pad double per H).
+//   write: c/H = beta*lanes/2 + ql;  read: c/H = beta*lanes/2 + (j*lanes)/H.
+// A wavefront's buffer holds 32*(H + 1) doubles.
+template <int L>
+struct ExchangeHalf {
+    using Lo = Layout<L>;
+    static constexpr int H = Lo::half, NL = Lo::lanes, HB = NL / 2 * H;
+    static_assert(H % NL == 0 && NL % 2 == 0, "lanes of a block must be even and divide E/2");
+    double* wr;
+    double* rd;
+    bool top;   // the lane's top q bit: it writes in round 1
+    __device__ ExchangeHalf(double* xb, int lane) {
+        const unsigned beta = (unsigned)lane / NL, q = (unsigned)lane % NL, ql = q % (NL / 2);
+        top = q >= (unsigned)(NL / 2);
+        wr = xb + (beta * (HB + NL / 2) + ql * (H + 1));
+        rd = xb + (beta * (HB + NL / 2) + q);
+    }
+    // this lane's H elements of half h (x[2 i + h]), from `src` (the values before round 0's reads)
+    __device__ __forceinline__ void write(const double (&src)[Lo::E], int h) const {
+#pragma unroll
+        for (int i = 0; i < H; ++i) wr[i] = src[2 * i + h];
+    }
+    // reader slots r*H/2 .. r*H/2 + H/2 - 1 of half h
+    __device__ __forceinline__ void read(double (&x)[Lo::E], int h, int r) const {
+#pragma unroll
+        for (int j = 0; j < H / 2; ++j) x[2 * (r * (H / 2) + j) + h] = rd[j * NL + (j * NL) / H];
+    }
+};
+
 template <int L>
 __device__ __forceinline__ void exchange_AB(double (&x)[Layout<L>::E], double* xb, int lane) {
     const Exchange<L> ex(xb, lane);
