@@ -43,7 +43,10 @@ _lib = None
 
 
 def load(path: Optional[str] = None):
-    """Load libqamw.so (raises if it is missing: build it with __graft_entry__.build())."""
+    """Load libqamw.so (raises if it is missing: build it with __graft_entry__.build()).
+
+    Without a path this is the binding's library, loaded once.  With a path the file is loaded and
+    returned but not installed: the functions of this module keep calling the binding's library."""
     global _lib
     if _lib is not None and path is None:
         return _lib
