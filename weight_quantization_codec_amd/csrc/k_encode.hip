@@ -653,7 +653,9 @@ __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a, int T, int R) {
                         for (int i = 0; i < kPolarBatch; ++i) bi[g + i] = gi[i];
                     }
                 } else {
-                    nearest_lds_capped<kSearchBatch, kSearchCap>(bx, by, sl, bi, st);
+                    // the unrolled walk for aligned bf16 rows, except with E = 16 and 1/sigma in
+                    // registers: there, and for fp32 or unaligned rows, its extra registers spill
+                    nearest_lds_capped<kSearchBatch, kSearchCap, (BF && VEC && (ISG_LDS || E > 16))>(bx, by, sl, bi, st);
                 }
             }
 #pragma unroll

@@ -391,7 +391,7 @@ struct SearchCont {
     __device__ bool open() const { return end > (bo_next >> 16); }
 };
 
-template <int NP, int S>
+template <int NP, int S, bool UNROLL = true>
 __device__ __forceinline__ void nearest_lds_capped(const float (&px)[NP], const float (&py)[NP], const SearchLds& s,
                                                    int (&out)[NP], SearchCont (&st)[NP]) {
     float bd[NP];
@@ -420,7 +420,7 @@ __device__ __forceinline__ void nearest_lds_capped(const float (&px)[NP], const 
         steps = max(steps, a1 - a0);
     }
     if (steps > S) steps = S;
-    for (int t = 0; wave_any((uint32_t)(t < steps)); ++t) {
+    auto step = [&](int t) {
         uint32_t ad[NP];
 #pragma unroll
         for (int i = 0; i < NP; ++i) ad[i] = s.ent[o0[i] + t];
@@ -435,6 +435,17 @@ __device__ __forceinline__ void nearest_lds_capped(const float (&px)[NP], const 
                 bo[i] = ad[i];
             }
         }
+    };
+    if constexpr (UNROLL) {
+        // unrolled: a step's list reads are one base address per pair plus a constant offset, and
+        // no pointer increments or loop-carried copies remain (more code and live registers)
+#pragma unroll
+        for (int t = 0; t < S; ++t) {
+            if (!wave_any((uint32_t)(t < steps))) break;
+            step(t);
+        }
+    } else {
+        for (int t = 0; wave_any((uint32_t)(t < steps)); ++t) step(t);
     }
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
