@@ -180,7 +180,7 @@ __device__ __forceinline__ void scale_raw(const RawW<E, BF>& r, const double (&c
 // With a group counter (gcnt) the wavefronts of the row wait only for each other: each publishes
 // its partial sum and adds 1 to the group's LDS counter, which reaches nwaves * (pass + 1) once the
 // whole row's partials of this pass are in; otherwise the workgroup synchronizes.
-template <int L, bool BF, bool SPLIT = false>
+template <int L, bool BF, bool SPLIT = false, bool B2 = false>
 __device__ __forceinline__ double front_end(const RawW<Layout<L>::E, BF>& raw, bool active, int tid,
                                             const double (&cf)[Layout<L>::E], double (&x)[Layout<L>::E],
                                             double* red, double* xb, int nwaves, int* gcnt = nullptr,
@@ -198,6 +198,20 @@ __device__ __forceinline__ double front_end(const RawW<Layout<L>::E, BF>& raw, b
     if ((tid & (kWave - 1)) == 0) {
         red[tid / kWave] = ss;
         if (gcnt) __hip_atomic_fetch_add(gcnt, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    if constexpr (B2) {
+        // the outer stage of a 256-column block on the 128-column layout: in phase A lane q of the
+        // block holds elements 16 q + m, so element bit 7 is lane bit 3 (row_ror:8 within rows of 16
+        // lanes is lane ^ 8); the stages commute, so this one runs first.  The lower half-block adds
+        // its partner's element, the upper one subtracts its own from the partner's.
+        static_assert(L == 7, "256-column blocks run on the 128-column layout");
+        const double sgn = ((tid >> 3) & 1) ? -1.0 : 1.0;
+#pragma unroll
+        for (int m = 0; m < Layout<L>::E; ++m) {
+            const int lo = __builtin_amdgcn_update_dpp(0, (int)__double2loint(x[m]), 0x128, 0xF, 0xF, false);
+            const int hi = __builtin_amdgcn_update_dpp(0, (int)__double2hiint(x[m]), 0x128, 0xF, 0xF, false);
+            x[m] = __builtin_fma(x[m], sgn, __hiloint2double(hi, lo));
+        }
     }
     if constexpr (Lo::two_phase) {
         // The stages commute: stage 0 (element bit 0) runs last, in phase B, so the two halves
@@ -487,9 +501,21 @@ __host__ __device__ inline size_t encode_wave_bytes(int E, bool two_phase, int b
     return m > queue ? m : queue;
 }
 
+// 256-column blocks of aligned bf16 rows (the QAM-W search) run on the 128-column lane layout:
+// H_256 = [[H_128, H_128], [H_128, -H_128]] in Sylvester order, so each half-block is transformed as
+// a 128-column block and one more stage combines the halves, which lanes 8 apart hold with the same
+// element positions.  That layout has 16 elements per lane instead of 32: half the registers, so
+// twice the wavefronts per CU.
+template <int L, bool BF, bool VEC, bool POLAR>
+__host__ __device__ constexpr bool enc_b2() { return L == 8 && BF && VEC && !POLAR; }
+template <int L, bool BF, bool VEC, bool POLAR>
+__host__ __device__ constexpr int enc_layout() { return enc_b2<L, BF, VEC, POLAR>() ? 7 : L; }
+
 template <int L, int MAXT, bool BF, bool VEC, bool ISG_LDS, bool POLAR>
 __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a, int T, int R) {
-    using Lo = Layout<L>;
+    constexpr bool kB2 = enc_b2<L, BF, VEC, POLAR>();
+    constexpr int LL = enc_layout<L, BF, VEC, POLAR>();   // the lane layout's block
+    using Lo = Layout<LL>;
     constexpr int E = Lo::E, NP = E / 2;
     extern __shared__ __align__(16) char smem[];
     const int K = 1 << a.bits;
@@ -570,8 +596,8 @@ __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a, int T, int R) {
     if (tid == 0) *gcnt = 0;
 #pragma unroll
     for (int i = 0; i < NP / 2; ++i) {
-        const double i0 = 1.0 / (double)a.sigma[min(col_B<L>(tid, 4 * i) / 2, n_pairs - 1)];
-        const double i1 = 1.0 / (double)a.sigma[min(col_B<L>(tid, 4 * i + 2) / 2, n_pairs - 1)];
+        const double i0 = 1.0 / (double)a.sigma[min(col_B<LL>(tid, 4 * i) / 2, n_pairs - 1)];
+        const double i1 = 1.0 / (double)a.sigma[min(col_B<LL>(tid, 4 * i + 2) / 2, n_pairs - 1)];
         if constexpr (ISG_LDS) {
             if (grp == 0) isg_lds[i * T + tid] = make_double2(i0, i1);
         } else {
@@ -580,7 +606,7 @@ __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a, int T, int R) {
             pin_reg(isg_reg[i].y);
         }
     }
-    const double inv_sqrt_b = 1.0 / __builtin_sqrt((double)Lo::b);
+    const double inv_sqrt_b = 1.0 / __builtin_sqrt((double)(1 << L));
     const int bits = a.bits;
     const __amdgpu_buffer_rsrc_t nrs =
         __builtin_amdgcn_make_buffer_rsrc((void*)a.norm, (short)0, a.d_out * 2, 0x00020000);
@@ -595,7 +621,7 @@ __global__ __launch_bounds__(MAXT) void k_encode(EncodeArgs a, int T, int R) {
         double* red = red_all + ((pass & 1) * R + grp) * kMaxWaves;
         // lanes past the row (whole blocks of their own) and rows past the matrix loaded zeros,
         // so the front end runs on every lane: nothing of theirs is stored or searched
-        const double r2 = front_end<L, BF, true>(nxt, true, tid, cf, x, red, xb, nwaves, gcnt, nwaves * (pass + 1));
+        const double r2 = front_end<LL, BF, true, kB2>(nxt, true, tid, cf, x, red, xb, nwaves, gcnt, nwaves * (pass + 1));
         // the next row, in flight during the search and the packing (its registers were free
         // during the front end)
         load_row_raw<E, BF, VEC>(a.w, a.ld, a.d_in, a.d_out, row + rstride, tid, nxt);
@@ -809,31 +835,32 @@ hipError_t encode_launch(const EncodeArgs& a, int R, int threads, size_t smem, i
 
 template <int L, bool BF, bool VEC, bool POLAR>
 hipError_t encode_LBVP(const EncodeArgs& a, hipStream_t st) {
-    using Lo = Layout<L>;
+    constexpr int LL = enc_layout<L, BF, VEC, POLAR>();   // the kernel's lane layout
+    using Lo = Layout<LL>;
     const int T = ((a.d_in / Lo::E) + kWave - 1) / kWave * kWave;
-    if (T > 1024 || (T > 512 && L > 7)) return hipErrorInvalidConfiguration;
+    if (T > 1024 || (T > 512 && LL > 7)) return hipErrorInvalidConfiguration;
     const size_t front = encode_front_bytes(a);
-    if constexpr (L <= 7) {
+    if constexpr (LL <= 7) {
         // up to 1024 threads with 1 / sigma in LDS (128 VGPRs, four wavefronts per SIMD)
         int R = 1024 / T;
         if (R > 4) R = 4;
         if (R > a.d_out) R = a.d_out > 0 ? a.d_out : 1;
-        while (R > 1 && encode_smem<L>(front, a.bits, R, R * T / kWave, true) > kLdsBytes) --R;
+        while (R > 1 && encode_smem<LL>(front, a.bits, R, R * T / kWave, true) > kLdsBytes) --R;
         const int threads = R * T;
-        const size_t smem = encode_smem<L>(front, a.bits, R, threads / kWave, true);
+        const size_t smem = encode_smem<LL>(front, a.bits, R, threads / kWave, true);
         if (smem <= kLdsBytes) return encode_launch<L, 1024, BF, VEC, true, POLAR>(a, R, threads, smem, T, st);
     }
     // 1 / sigma in registers
-    constexpr int kMax = L <= 7 ? 768 : 512;
+    constexpr int kMax = LL <= 7 ? 768 : 512;
     int R = T >= kMax ? 1 : kMax / T;
     if (R > 4) R = 4;
     if (R > a.d_out) R = a.d_out > 0 ? a.d_out : 1;
-    while (R > 1 && encode_smem<L>(front, a.bits, R, R * T / kWave, false) > kLdsBytes) --R;
+    while (R > 1 && encode_smem<LL>(front, a.bits, R, R * T / kWave, false) > kLdsBytes) --R;
     const int threads = R * T;
-    const size_t smem = encode_smem<L>(front, a.bits, R, threads / kWave, false);
+    const size_t smem = encode_smem<LL>(front, a.bits, R, threads / kWave, false);
     if (smem > kLdsBytes) return hipErrorInvalidConfiguration;
     if (threads <= 512) return encode_launch<L, 512, BF, VEC, false, POLAR>(a, R, threads, smem, T, st);
-    if constexpr (L <= 7) {
+    if constexpr (LL <= 7) {
         if (threads <= 768) return encode_launch<L, 768, BF, VEC, false, POLAR>(a, R, threads, smem, T, st);
         return encode_launch<L, 1024, BF, VEC, false, POLAR>(a, R, threads, smem, T, st);
     }
