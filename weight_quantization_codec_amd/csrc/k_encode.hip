@@ -292,9 +292,15 @@ __device__ __forceinline__ double front_end(const RawW<Layout<L>::E, BF>& raw, b
 // gridDim.x), ...  Every group runs every pass (rows past the end are zero), so the barriers in
 // the front end are reached by the whole workgroup.  At the end the groups' |z_k| sums are added
 // in group order and written as the workgroup's partial sums.
+// The calibration's lane layout: 256-column blocks of bf16 rows on the 128-column one, as in the
+// encoder (one DPP stage for the outer butterfly; see enc_b2 below).
+template <int L, bool BF>
+__host__ __device__ constexpr int cal_layout() { return (L == 8 && BF) ? 7 : L; }
+
 template <int L, int MAXT, bool BF>
 __global__ __launch_bounds__(MAXT) void k_calibrate(CalibArgs a, int T, int R) {
-    using Lo = Layout<L>;
+    constexpr int LL = cal_layout<L, BF>();
+    using Lo = Layout<LL>;
     constexpr int E = Lo::E, NP = E / 2;
     extern __shared__ __align__(16) char smem[];
     const int grp = __builtin_amdgcn_readfirstlane(threadIdx.x / T);
@@ -322,7 +328,7 @@ __global__ __launch_bounds__(MAXT) void k_calibrate(CalibArgs a, int T, int R) {
         for (int m = 0; m < E; ++m) cf[m] = (double)cf32[m];
         __syncthreads();
     }
-    const double inv_sqrt_b = 1.0 / __builtin_sqrt((double)Lo::b);
+    const double inv_sqrt_b = 1.0 / __builtin_sqrt((double)(1 << L));
     double acc[NP];
 #pragma unroll
     for (int i = 0; i < NP; ++i) acc[i] = 0.0;
@@ -331,7 +337,7 @@ __global__ __launch_bounds__(MAXT) void k_calibrate(CalibArgs a, int T, int R) {
         const int row = base + grp;
         const bool rv = row < a.n_rows;
         double x[E];
-        double r2 = front_end<L, BF>(nxt, active && rv, tid, cf, x, red, xb, nwaves);
+        double r2 = front_end<LL, BF, false, (LL != L)>(nxt, active && rv, tid, cf, x, red, xb, nwaves);
         if (active && row + rstride < a.n_rows)
             load_raw<E, BF>(a.w, vec, (int64_t)(row + rstride) * a.ld + (int64_t)tid * E, nxt);
         double r = __builtin_sqrt(r2);
@@ -352,7 +358,7 @@ __global__ __launch_bounds__(MAXT) void k_calibrate(CalibArgs a, int T, int R) {
         if (grp == g && active) {
 #pragma unroll
             for (int i = 0; i < NP; ++i) {
-                const int k = col_B<L>(tid, 2 * i) / 2;
+                const int k = col_B<LL>(tid, 2 * i) / 2;
                 comb[k] = (g == 0) ? acc[i] : comb[k] + acc[i];
             }
         }
@@ -366,7 +372,7 @@ __global__ __launch_bounds__(MAXT) void k_calibrate(CalibArgs a, int T, int R) {
         double* part = a.partial + (size_t)blockIdx.x * (a.d_in / 2);
 #pragma unroll
         for (int i = 0; i < NP; ++i) {
-            const int k = col_B<L>(tid, 2 * i) / 2;
+            const int k = col_B<LL>(tid, 2 * i) / 2;
             part[k] = comb[k];
         }
     }
@@ -880,8 +886,9 @@ hipError_t encode_LB(const EncodeArgs& a, hipStream_t st) {
 
 template <int L, bool BF>
 hipError_t calibrate_LB(const CalibArgs& a, float* sigma, hipStream_t st) {
-    using Lo = Layout<L>;
-    constexpr int kMax = L <= 7 ? 1024 : 512;
+    constexpr int LL = cal_layout<L, BF>();   // the kernel's lane layout
+    using Lo = Layout<LL>;
+    constexpr int kMax = LL <= 7 ? 1024 : 512;
     const int T = ((a.d_in / Lo::E) + kWave - 1) / kWave * kWave;
     if (T > kMax) return hipErrorInvalidConfiguration;
     int R = kMax / T;
@@ -892,11 +899,11 @@ hipError_t calibrate_LB(const CalibArgs& a, float* sigma, hipStream_t st) {
         groups = (a.n_rows + R - 1) / R;
         if (groups > a.n_groups) groups = a.n_groups;   // the workspace holds n_groups partial rows
         const int threads = R * T;
-        const size_t smem = calib_smem<L>(R, threads / kWave);
+        const size_t smem = calib_smem<LL>(R, threads / kWave);
         if (threads <= 512) {
             allow_lds(k_calibrate<L, 512, BF>, smem);
             hipLaunchKernelGGL((k_calibrate<L, 512, BF>), dim3(groups), dim3(threads), smem, st, a, T, R);
-        } else if constexpr (L <= 7) {
+        } else if constexpr (LL <= 7) {
             allow_lds(k_calibrate<L, 1024, BF>, smem);
             hipLaunchKernelGGL((k_calibrate<L, 1024, BF>), dim3(groups), dim3(threads), smem, st, a, T, R);
         } else {
